@@ -1,0 +1,240 @@
+"""The multi-tenant LoRA linear layer on an FP8 or 4-bit base, step by step.
+
+TEST INFRASTRUCTURE ONLY (see the package docstring).
+
+For each token t with tenant index a_t the layer computes
+
+    y_t = dequant(W_q . quant(x_t)) + s * B[a_t] (A[a_t] x_t)
+
+("EpiLoRA: Fusing Many LoRA Adapters into Low-Precision GEMMs for Serving
+and RL", Background: an adapter adds the low-rank update BA to the frozen
+weight, A projecting the input down to rank r and B back up; Design,
+"Multi-adapter kernels": the activations are quantized per token, the
+down-projection h = x A^T is taken from the bf16 activations, and the GEMM's
+epilogue applies the scales and adds h B^T for each adapter group).  a_t = -1
+means no adapter.  With a prefill mask the adapter applies only to flagged
+tokens ("PreFT: Prefill-only finetuning for efficient inference", abstract:
+the adapter is applied to prefill tokens only).
+
+Array conventions (all numpy):
+  x        uint16 [M][K]      bf16 bit patterns of the activations
+  xq, sx   uint8 [M][K], float32 [M]
+  w        uint16 [N][K]      bf16 weights before quantisation
+  wq, sw   uint8 [N][K], float32 [N]                    (FP8 base)
+  wc, bs, gs  uint8 [N][K/2], uint8 [N][K/16], float32  (4-bit base)
+  A        uint16 [L][r][K]   bf16
+  B        uint16 [L][N][r]   bf16
+  ranks    int32 [L] or None
+  idx      int32 [M]          tenant per token, -1 = none
+  mask     uint8 [M] or None  nonzero = the adapter applies
+Results are float64 unless stated.
+"""
+
+import numpy as np
+
+from .formats import (
+    FOLD_SHIFT,
+    bf16_to_f32,
+    e2m1_decode_table,
+    e2m1_encode,
+    e4m3_decode,
+    e4m3_encode,
+    fold_table,
+)
+
+E4M3_MAX = np.float32(448.0)
+
+# ---------------------------------------------------------------------------
+# Quantisation (integer results decided in fp32)
+# ---------------------------------------------------------------------------
+
+
+def quant_rows_e4m3(v):
+    """Per-row dynamic E4M3 quantisation of a float32 matrix.
+
+    amax = max |v| over the row; scale = fp32(amax / 448) (an IEEE, correctly
+    rounded division), 1.0 for an all-zero row; code = E4M3(fp32(v / scale)),
+    one correctly rounded division per element, the result rounded to
+    nearest-even and saturated at 448 (v / scale may exceed 448 by an ulp
+    when the scale was rounded down)."""
+    v = np.asarray(v, dtype=np.float32)
+    amax = np.max(np.abs(v), axis=1).astype(np.float32)
+    scale = (amax / E4M3_MAX).astype(np.float32)
+    scale[amax == 0] = np.float32(1.0)
+    q = (v / scale[:, None]).astype(np.float32)
+    return e4m3_encode(q), scale
+
+
+def quant_act(x):
+    """Per-token dynamic FP8 quantisation of the activations (Design,
+    "Multi-adapter kernels": K1 quantizes the layer's activations once, with
+    a per-token scale).  x: uint16 [M][K] bf16 -> (xq uint8 [M][K],
+    sx float32 [M])."""
+    return quant_rows_e4m3(bf16_to_f32(x))
+
+
+def quant_weight_fp8(w):
+    """Per-output-channel FP8 weight quantisation done when the model loads
+    (Evaluation, Setup: FP8 bases quantized at load).  Same rule as the
+    activations, one scale per row n of W[N][K]."""
+    return quant_rows_e4m3(bf16_to_f32(w))
+
+
+def quant_weight_fp4(w):
+    """4-bit weight encoder in the NVFP4 layout: E2M1 codes, one E4M3 scale
+    per 16 consecutive elements along K, one fp32 global scale.
+
+    gs = fp32(amax(W) / 2688) (1.0 if W is all zero);
+    bs = E4M3(fp32(amax_block / fp32(6 * gs)));
+    codes = E2M1(fp32(w / fp32(e4m3(bs) * gs))), or code 0 where that block
+    scale is zero.  Element 2i goes in the low nibble of byte i.
+    Returns (wc uint8 [N][K/2], bs uint8 [N][K/16], gs float32)."""
+    wf = bf16_to_f32(w)
+    n, k = wf.shape
+    if k % 16:
+        raise ValueError("K must be a multiple of 16")
+    amax = np.float32(np.max(np.abs(wf)))
+    gs = np.float32(amax / np.float32(6.0 * 448.0)) if amax > 0 else np.float32(1.0)
+    blocks = wf.reshape(n, k // 16, 16)
+    amax_b = np.max(np.abs(blocks), axis=2).astype(np.float32)
+    denom = np.float32(np.float32(6.0) * gs)
+    bs = e4m3_encode((amax_b / denom).astype(np.float32))
+    step = (e4m3_decode(bs).astype(np.float32) * gs).astype(np.float32)
+    safe = np.where(step == 0, np.float32(1.0), step).astype(np.float32)
+    codes = e2m1_encode((blocks / safe[:, :, None]).astype(np.float32))
+    codes = np.where((step == 0)[:, :, None], np.uint8(0), codes).astype(np.uint8)
+    codes = codes.reshape(n, k)
+    wc = (codes[:, 0::2] | (codes[:, 1::2] << np.uint8(4))).astype(np.uint8)
+    return wc, bs, gs
+
+
+def unpack_fp4(wc):
+    """uint8 [N][K/2] -> uint8 [N][K] E2M1 codes (low nibble first)."""
+    wc = np.asarray(wc, dtype=np.uint8)
+    n, kh = wc.shape
+    out = np.empty((n, 2 * kh), dtype=np.uint8)
+    out[:, 0::2] = wc & 0xF
+    out[:, 1::2] = wc >> 4
+    return out
+
+
+def fold_decode_fp4(wc, bs):
+    """The FP8 byte each 4-bit weight becomes inside the GEMM:
+    T[code][block scale] (the fold table).  uint8 [N][K]."""
+    codes = unpack_fp4(wc)
+    n, k = codes.shape
+    b = np.repeat(np.asarray(bs, dtype=np.uint8), 16, axis=1)
+    return fold_table()[codes, b]
+
+
+def exact_decode_fp4(wc, bs, gs):
+    """The NVFP4 value e2m1(code) * e4m3(bs) * gs, float64 [N][K]
+    (a diagnostic; the GEMM uses the fold)."""
+    codes = unpack_fp4(wc)
+    b = np.repeat(np.asarray(bs, dtype=np.uint8), 16, axis=1)
+    return e2m1_decode_table()[codes] * e4m3_decode(b) * float(gs)
+
+
+# ---------------------------------------------------------------------------
+# Base GEMM (sums in fp64)
+# ---------------------------------------------------------------------------
+
+
+def _pick(a, sel):
+    return a if sel is None else a[np.asarray(sel)]
+
+
+def base_fp8(xq, sx, wq, sw, rows=None, cols=None):
+    """acc[t][n] = sum_k e4m3(xq[t][k]) * e4m3(wq[n][k]);
+    base = (acc * sx[t]) * sw[n].  rows/cols select a subset of tokens and
+    output channels (sampled checks at full size)."""
+    X = e4m3_decode(_pick(xq, rows))
+    W = e4m3_decode(_pick(wq, cols))
+    acc = X @ W.T
+    s_t = _pick(np.asarray(sx, np.float32), rows).astype(np.float64)
+    s_n = _pick(np.asarray(sw, np.float32), cols).astype(np.float64)
+    return (acc * s_t[:, None]) * s_n[None, :]
+
+
+def base_fp4(xq, sx, wc, bs, gs, rows=None, cols=None):
+    """4-bit base through the fold: each weight is the FP8 byte
+    T[code][block scale]; base = (acc * sx[t]) * (gs * 2**3)."""
+    X = e4m3_decode(_pick(xq, rows))
+    W8 = e4m3_decode(fold_decode_fp4(_pick(wc, cols), _pick(bs, cols)))
+    acc = X @ W8.T
+    s_t = _pick(np.asarray(sx, np.float32), rows).astype(np.float64)
+    return (acc * s_t[:, None]) * (float(np.float32(gs)) * 2.0 ** FOLD_SHIFT)
+
+
+# ---------------------------------------------------------------------------
+# Adapters
+# ---------------------------------------------------------------------------
+
+
+def active_rows(idx, L, r, ranks=None, mask=None):
+    """(active bool [M], adapter int [M], rank int [M]).
+
+    A token is adapted when its index lies in [0, L), its mask byte (if a
+    mask is given) is nonzero, and its adapter's rank (ranks[a], or r when
+    no ranks are given) is positive.  An index outside [-1, L) counts as -1."""
+    idx = np.asarray(idx, dtype=np.int64)
+    valid = (idx >= 0) & (idx < L)
+    a = np.where(valid, idx, 0)
+    if ranks is None:
+        rk = np.full(idx.shape, r, dtype=np.int64)
+    else:
+        rk = np.minimum(np.asarray(ranks, dtype=np.int64)[a], r)
+    act = valid & (rk > 0)
+    if mask is not None:
+        act &= np.asarray(mask, dtype=np.uint8) != 0
+    return act, a, np.where(act, rk, 0)
+
+
+def shrink(x, A, idx, ranks=None, mask=None):
+    """z[t][j] = sum_k A[a_t][j][k] * x[t][k] over the bf16 values, for
+    active tokens and j < rank(a_t); zero elsewhere.  float64 [M][r]."""
+    L, r, _ = A.shape
+    act, a, rk = active_rows(idx, L, r, ranks, mask)
+    xf = bf16_to_f32(x).astype(np.float64)
+    z = np.zeros((xf.shape[0], r), dtype=np.float64)
+    for t in np.nonzero(act)[0]:
+        Af = bf16_to_f32(A[a[t], : rk[t]]).astype(np.float64)
+        z[t, : rk[t]] = Af @ xf[t]
+    return z
+
+
+def expand(z, B, idx, scale, ranks=None, mask=None, cols=None):
+    """lora[t][n] = s * sum_j B[a_t][n][j] * z[t][j] for active tokens,
+    zero for the others (which receive no add at all).  float64 [M][N]."""
+    L, _, r = B.shape
+    act, a, rk = active_rows(idx, L, r, ranks, mask)
+    Bsel = B if cols is None else B[:, np.asarray(cols)]
+    out = np.zeros((z.shape[0], Bsel.shape[1]), dtype=np.float64)
+    for t in np.nonzero(act)[0]:
+        Bf = bf16_to_f32(Bsel[a[t], :, : rk[t]]).astype(np.float64)
+        out[t] = float(np.float32(scale)) * (Bf @ z[t, : rk[t]])
+    return out, act
+
+
+def linear_lora(x, A, B, idx, scale, *, wq=None, sw=None, wc=None, bs=None,
+                gs=None, ranks=None, mask=None, rows=None, cols=None):
+    """The whole layer: per-token quantisation, base GEMM, shrink and the
+    epilogue.  Exactly one weight format is given (wq+sw, or wc+bs+gs).
+
+    Returns a dict with xq, sx (bit-exact targets), z (float64), base,
+    y (float64: base plus the adapter term on active rows, base alone on
+    the others) and the active-row flags.  rows/cols restrict base, z and y
+    to a sample of tokens and output channels."""
+    xq, sx = quant_act(x)
+    if wq is not None:
+        base = base_fp8(xq, sx, wq, sw, rows=rows, cols=cols)
+    else:
+        base = base_fp4(xq, sx, wc, bs, gs, rows=rows, cols=cols)
+    xs = _pick(x, rows)
+    idx_s = _pick(np.asarray(idx), rows)
+    mask_s = None if mask is None else _pick(np.asarray(mask), rows)
+    z = shrink(xs, A, idx_s, ranks, mask_s)
+    lora, act = expand(z, B, idx_s, scale, ranks, mask_s, cols=cols)
+    y = base.copy()
+    y[act] = base[act] + lora[act]
+    return dict(xq=xq, sx=sx, z=z, base=base, y=y, active=act)
