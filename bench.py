@@ -1,0 +1,316 @@
+"""Benchmark of the multi-tenant LoRA low-precision linear layer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+
+A step is one pass of the whole hot path over one batch: the Llama-8B-shaped
+decoder layer's four projections (qkv, o, gate_up, down) at M = 1 token with
+one rank-64 tenant, each through the fused decode path (per-token FP8
+quantization, shrink, FP8 GEMM with the adapter epilogue, in one launch per
+projection).  Inputs are resident in HBM; the steps are replayed from a HIP
+graph, and 4 copies of the weights and adapters are cycled so that no step
+finds its 218 MB of weights in the 256 MB Infinity Cache (the method's
+kernel timings flush the L2 between runs).  `value` is microseconds per
+layer (lower is better).
+
+Also reported: the same layer without an adapter (base-only FP8 GEMM, same
+kernel), the unfused paths, per-projection times, the 2048-token prefill
+GEMMs (gate_up and down, FP8 and 4-bit weights, 16 and 32 tenant segments)
+in TFLOP/s, the roofline of the dominant kernel, and the CPU oracle timed
+on a bounded sample of the same layer.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import fp4_gemm_amd as ep  # noqa: E402
+from workloads import config  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+ROTATE = 4
+DEV = "cuda"
+
+METRIC = "µs/layer + %HBM peak at M=1 r=64; FP8 TFLOP/s at M=2048, 32 tenants"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def dev(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(a).to(DEV)
+
+
+class Proj:
+    """One projection on the device: ROTATE copies of weights and adapters."""
+
+    def __init__(self, g, wfmt="fp8", copies=ROTATE):
+        lay = g.layer
+        self.g, self.M, self.K, self.N, self.r = g, g.M, g.K, g.N, lay.r
+        self.wfmt = wfmt
+        self.x = dev(g.x())
+        w = dev(g.w())
+        if wfmt == "fp8":
+            wq = torch.empty(self.N, self.K, dtype=torch.uint8, device=DEV)
+            sw = torch.empty(self.N, dtype=torch.float32, device=DEV)
+            ep.epilora_quant_weight_fp8(w, wq, sw)
+            self.w = [(wq, dict(sw=sw))] + [(wq.clone(), dict(sw=sw.clone())) for _ in range(copies - 1)]
+        else:
+            wc = torch.empty(self.N, self.K // 2, dtype=torch.uint8, device=DEV)
+            bs = torch.empty(self.N, self.K // 16, dtype=torch.uint8, device=DEV)
+            gs = torch.empty(1, dtype=torch.float32, device=DEV)
+            ws = ep.new_workspace(ep.OP_QUANT_W4, 1, self.N, self.K, 16)
+            ep.epilora_quant_weight_fp4(w, wc, bs, gs, ws)
+            self.w = [(wc, dict(bs=bs, gs=gs))] + [(wc.clone(), dict(bs=bs.clone(), gs=gs.clone()))
+                                                   for _ in range(copies - 1)]
+        del w
+        A, B = dev(g.A()), dev(g.B())
+        self.A = [A] + [A.clone() for _ in range(copies - 1)]
+        self.B = [B] + [B.clone() for _ in range(copies - 1)]
+        self.idx = dev(lay.idx.astype(np.int32))
+        self.mask = None if lay.mask is None else dev(lay.mask.astype(np.uint8))
+        self.ranks = None if lay.ranks is None else dev(lay.ranks.astype(np.int32))
+        self.scale = lay.scale
+        self.y = torch.empty(self.M, self.N, dtype=torch.bfloat16, device=DEV)
+        self.xq = torch.empty(self.M, self.K, dtype=torch.uint8, device=DEV)
+        self.sx = torch.empty(self.M, dtype=torch.float32, device=DEV)
+        self.z = torch.empty(self.M, self.r, dtype=torch.float32, device=DEV)
+        self.ws_dec = ep.new_workspace(ep.OP_DECODE, self.M, self.N, self.K, self.r)
+        self.ws_shr = ep.new_workspace(ep.OP_SHRINK, self.M, self.N, self.K, self.r)
+        self.copies = copies
+
+    def adapters(self, c):
+        return dict(B=self.B[c], idx=self.idx, ranks=self.ranks, mask=self.mask, scale=self.scale)
+
+    # paths ------------------------------------------------------------------
+    def fused(self, c):
+        w, kw = self.w[c]
+        ep.epilora_decode_lora(self.x, w, self.y, A=self.A[c], ws=self.ws_dec, xq_out=self.xq, sx_out=self.sx,
+                               **self.adapters(c), **kw)
+
+    def fused_base(self, c):
+        w, kw = self.w[c]
+        ep.epilora_decode_lora(self.x, w, self.y, ws=self.ws_dec, xq_out=self.xq, sx_out=self.sx, **kw)
+
+    def quant(self, c):
+        ep.epilora_quant_act(self.x, self.xq, self.sx)
+
+    def shrink(self, c):
+        ep.epilora_lora_shrink(self.x, self.A[c], self.idx, self.z, self.ws_shr, ranks=self.ranks, mask=self.mask)
+
+    def gemm_lora(self, c):
+        w, kw = self.w[c]
+        ep.epilora_gemm_lora(self.xq, self.sx, w, self.y, z=self.z, ws=self.ws_shr, **self.adapters(c), **kw)
+
+    def gemm_base(self, c):
+        w, kw = self.w[c]
+        ep.epilora_gemm_lora(self.xq, self.sx, w, self.y, **kw)
+
+    def expand(self, c):
+        ep.epilora_lora_expand_add(self.z, self.B[c], self.idx, self.scale, self.y, self.ws_shr,
+                                   ranks=self.ranks, mask=self.mask)
+
+    # algorithmic counts -------------------------------------------------------
+    def adapter_ranks(self):
+        lay = self.g.layer
+        act = [int(a) for a, m in zip(lay.idx, lay.mask if lay.mask is not None else [1] * self.M)
+               if 0 <= a < lay.L and m]
+        distinct = sorted(set(act))
+        rk = lambda a: lay.r if lay.ranks is None else int(lay.ranks[a])
+        return act, distinct, rk
+
+    def bytes(self):
+        act, distinct, rk = self.adapter_ranks()
+        if self.wfmt == "fp8":
+            wb = self.K * self.N + 4 * self.N
+        else:
+            wb = self.K * self.N // 2 + self.K * self.N // 16 + 4
+        ab = sum(2 * rk(a) * (self.K + self.N) for a in distinct)
+        return wb + ab + 2 * self.M * self.K + 2 * self.M * self.N
+
+    def flops(self):
+        act, _, rk = self.adapter_ranks()
+        return 2 * self.M * self.N * self.K + sum(2 * rk(a) * (self.K + self.N) for a in act)
+
+
+def graph_of(fns, copies):
+    """Capture `copies` rounds of fns (round c uses weight copy c) in one graph."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for c in range(copies):  # warm (first-launch costs out of the capture)
+            for f in fns:
+                f(c)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for c in range(copies):
+            for f in fns:
+                f(c)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(g, rounds, warmup):
+    """Milliseconds per replay of g: events on the replay stream."""
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(rounds):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / rounds
+
+
+def per_step_us(projs, fn_names, steps, warmup):
+    fns = [getattr(p, n) for p in projs for n in fn_names]
+    g = graph_of(fns, ROTATE)
+    rounds = max(1, steps // ROTATE)
+    ms = time_graph(g, rounds, max(1, warmup // ROTATE))
+    return 1000.0 * ms / ROTATE, rounds * ROTATE
+
+
+def cpu_baseline(layer, frac=8, min_seconds=10.0, max_reps=50):
+    """The oracle on a bounded sample of the decode layer: every frac-th
+    output channel of each projection (its weights quantized by the oracle
+    outside the timed region), repeated until about min_seconds of CPU work
+    have been timed; the mean time of one pass, scaled by frac, is reported
+    in microseconds per layer."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    cases = []
+    for g in layer.gemms:
+        cols = np.arange(0, g.N, frac)
+        wq, sw = oracle.quant_weight_fp8(g.w()[cols])
+        cases.append((g.x(), g.A(), g.B()[:, cols], wq, sw))
+    timed, reps = 0.0, 0
+    while reps < max_reps and (timed < min_seconds or reps < 2):
+        t0 = time.perf_counter()
+        for x, A, B, wq, sw in cases:
+            oracle.linear_lora(x, A, B, layer.idx, layer.scale, wq=wq, sw=sw, ranks=layer.ranks, mask=layer.mask)
+        timed += time.perf_counter() - t0
+        reps += 1
+    us = timed / reps * frac * 1e6
+    return {"value": round(us, 1), "unit": "us/layer", "cores": int(threads), "kind": "oracle",
+            "sample": f"Llama-8B decode layer (M=1, r=64): every {frac}th output channel of each of the 4 "
+                      f"projections (fp64 oracle incl. the FP8 decode of those weights), {reps} passes, "
+                      f"{timed:.1f} s timed, scaled x{frac}; host has {os.cpu_count()} cpus"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this layer shards by tensor parallelism, which is "
+              "not part of this build; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    ep.lib()
+
+    # ---- headline: the Llama-8B decode layer, M = 1, one rank-64 tenant ----
+    layer = config(2)
+    log("setting up the decode layer ...")
+    projs = [Proj(g) for g in layer.gemms]
+    torch.cuda.synchronize()
+    fused_us, timed_steps = per_step_us(projs, ["fused"], args.steps, args.warmup)
+    base_us, _ = per_step_us(projs, ["fused_base"], args.steps, args.warmup)
+    serial_us, _ = per_step_us(projs, ["quant", "shrink", "gemm_lora"], args.steps, args.warmup)
+    separate_us, _ = per_step_us(projs, ["quant", "gemm_base", "shrink", "expand"], args.steps, args.warmup)
+    per_proj = {}
+    for p in projs:
+        f_us, _ = per_step_us([p], ["fused"], args.steps, args.warmup)
+        b_us, _ = per_step_us([p], ["fused_base"], args.steps, args.warmup)
+        per_proj[p.g.name] = {"fused_us": round(f_us, 2), "base_us": round(b_us, 2),
+                              "bytes": p.bytes(), "GBps": round(p.bytes() / f_us / 1e3, 1)}
+    layer_bytes = sum(p.bytes() for p in projs)
+    dom = max(projs, key=lambda p: p.bytes())  # gate_up: the dominant kernel
+    dom_us = per_proj[dom.g.name]["fused_us"]
+    dom_gbs = dom.bytes() / dom_us / 1e3
+    log(f"decode layer: fused {fused_us:.1f} us, base {base_us:.1f} us")
+
+    # ---- prefill: M = 2048, tenant segments ----
+    prefill = {}
+    if not args.no_prefill:
+        for wfmt, segs in (("fp8", 32), ("fp8", 16), ("fp4", 16)):
+            lay5 = config(5, segments=segs, wfmt=wfmt)
+            for g in lay5.gemms:
+                log(f"prefill {wfmt} {segs} segments {g.name} ...")
+                p = Proj(g, wfmt, copies=3)
+                p.quant(0)
+                p.shrink(0)
+                gemm_ms = time_graph(graph_of([p.gemm_lora], 3), 10, 2) / 3
+                path_ms = time_graph(graph_of([p.quant, p.shrink, p.gemm_lora], 3), 5, 1) / 3
+                prefill[f"{g.name}_{wfmt}_{segs}seg"] = {
+                    "gemm_us": round(gemm_ms * 1e3, 1), "path_us": round(path_ms * 1e3, 1),
+                    "gemm_tflops": round(p.flops() / gemm_ms / 1e9, 1),
+                    "path_tflops": round(p.flops() / path_ms / 1e9, 1),
+                    "gemm_frac_fp8_peak": round(p.flops() / gemm_ms / 1e9 / FP8_PEAK_TFLOPS, 4)}
+                del p
+                torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu:
+        log("timing the CPU oracle on a sample ...")
+        cpu = cpu_baseline(layer)
+
+    out = {
+        "metric": METRIC,
+        "value": round(fused_us, 2),
+        "unit": "us/layer",
+        "n_gpus": 1,
+        "steps": timed_steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(fused_us / 1000.0, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3 (fp32 accumulate)",
+        "data": "synthetic (seeded; Llama-8B layer shapes, random adapters)",
+        "config": {"workload": "Llama-8B-shaped decode layer (qkv 4096->6144, o 4096->4096, "
+                               "gate_up 4096->28672, down 14336->4096), M=1 token, one rank-64 tenant, "
+                               "FP8 e4m3 per-channel weights, fused decode path, HIP graph replay, "
+                               f"{ROTATE} rotated weight copies",
+                   "M": 1, "rank": 64, "tenants": 1},
+        "hbm_frac": round(layer_bytes / fused_us / 1e3 / HBM_PEAK_GBS, 4),
+        "layer_bytes": layer_bytes,
+        "base_only_us": round(base_us, 2),
+        "fused_over_base": round(fused_us / base_us, 3),
+        "serialized_us": round(serial_us, 2),
+        "separate_kernels_us": round(separate_us, 2),
+        "per_projection": per_proj,
+        "roofline": {"kernel": f"decode_kernel ({dom.g.name}, fused)", "bound": "hbm",
+                     "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "prefill": prefill,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

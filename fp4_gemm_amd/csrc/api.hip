@@ -1,0 +1,236 @@
+// The C ABI (include/epilora.h): host-side validation, workspace sizing and
+// dispatch to the kernels.  No entry point allocates memory or synchronizes
+// the stream, except the diagnostic epilora_device_error.
+#include "../../include/epilora.h"
+#include "kernels.h"
+#include "layout.h"
+
+using namespace epilora;
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int hip_status(hipError_t e) { return e == hipSuccess ? EPILORA_OK : EPILORA_ERR_HIP; }
+
+hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+// Checks shared by the quantizers: sizes, pointers, alignment.
+int check_rows(const void* src, int64_t rows, int64_t K, int64_t ld_src, const void* dst, int64_t ld_dst,
+               const void* scale) {
+  if (rows < 0 || K < 0) return EPILORA_ERR_INVALID_ARG;
+  if (rows == 0) return EPILORA_OK;
+  if (src == nullptr || dst == nullptr || scale == nullptr) return EPILORA_ERR_INVALID_ARG;
+  if (ld_src < K || ld_dst < K) return EPILORA_ERR_INVALID_ARG;
+  if (K % 16 != 0 || ld_src % 16 != 0 || ld_dst % 16 != 0) return EPILORA_ERR_UNSUPPORTED;
+  if (!aligned(src, 16) || !aligned(dst, 16) || !aligned(scale, 4)) return EPILORA_ERR_UNSUPPORTED;
+  return EPILORA_OK;
+}
+
+// Adapter arguments: slot geometry and pointers (A only where needed).
+int check_adapters(int32_t L, int32_t r, const void* A, bool need_A, const void* B, bool need_B,
+                   const int32_t* ranks, const int32_t* idx) {
+  if (L < 0 || r <= 0 || idx == nullptr) return EPILORA_ERR_INVALID_ARG;
+  if (r > EPILORA_MAX_RANK || r % 16 != 0) return EPILORA_ERR_UNSUPPORTED;
+  if (L > 0 && ((need_A && A == nullptr) || (need_B && B == nullptr))) return EPILORA_ERR_INVALID_ARG;
+  if ((A && !aligned(A, 16)) || (B && !aligned(B, 16)) || !aligned(idx, 4) || (ranks && !aligned(ranks, 4)))
+    return EPILORA_ERR_UNSUPPORTED;
+  return EPILORA_OK;
+}
+
+int check_ws(const void* ws, size_t have, size_t need) {
+  if (ws == nullptr || have < need) return EPILORA_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return EPILORA_ERR_UNSUPPORTED;
+  return EPILORA_OK;
+}
+
+int check_weights(const epilora_layer_args* a) {
+  if (a->w == nullptr) return EPILORA_ERR_INVALID_ARG;
+  if (a->wfmt == EPILORA_W_FP8) {
+    if (a->sw == nullptr) return EPILORA_ERR_INVALID_ARG;
+    if (!aligned(a->w, 16) || !aligned(a->sw, 4)) return EPILORA_ERR_UNSUPPORTED;
+  } else if (a->wfmt == EPILORA_W_FP4) {
+    if (a->bs == nullptr || a->gs == nullptr) return EPILORA_ERR_INVALID_ARG;
+    if (!aligned(a->w, 16) || !aligned(a->bs, 2) || !aligned(a->gs, 4)) return EPILORA_ERR_UNSUPPORTED;
+  } else {
+    return EPILORA_ERR_INVALID_ARG;
+  }
+  if (a->K % 32 != 0) return EPILORA_ERR_UNSUPPORTED;
+  return EPILORA_OK;
+}
+
+WeightArgs weights_of(const epilora_layer_args* a) {
+  WeightArgs w;
+  w.fmt = a->wfmt; w.w = a->w; w.sw = a->sw; w.bs = a->bs; w.gs = a->gs;
+  return w;
+}
+
+AdapterArgs adapters_of(const epilora_layer_args* a, bool on) {
+  AdapterArgs d;
+  d.A = a->A; d.B = a->B; d.ranks = a->ranks; d.mask = a->mask;
+  d.idx = on ? a->idx : nullptr;
+  d.L = a->L; d.r = a->r; d.scale = a->scale;
+  if (!on) { d.r = 16; d.L = 0; }
+  return d;
+}
+
+}  // namespace
+
+extern "C" {
+
+int epilora_version(void) { return EPILORA_VERSION; }
+
+const char* epilora_strerror(int status) {
+  switch (status) {
+    case EPILORA_OK: return "ok";
+    case EPILORA_ERR_INVALID_ARG: return "invalid argument";
+    case EPILORA_ERR_UNSUPPORTED: return "unsupported shape, alignment or batch size";
+    case EPILORA_ERR_WORKSPACE: return "workspace missing or too small";
+    case EPILORA_ERR_HIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+size_t epilora_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int32_t r) {
+  (void)N;
+  if (M < 0 || K < 0 || r < 0) return 0;
+  switch (op) {
+    case EPILORA_OP_SHRINK: return shrink_ws(kCtrlBytes, M, K, r).total;
+    case EPILORA_OP_GEMM:
+    case EPILORA_OP_EXPAND:
+    case EPILORA_OP_QUANT_W4: return kCtrlBytes;
+    case EPILORA_OP_DECODE: return decode_ws(M, K, r).total;
+    default: return 0;
+  }
+}
+
+int epilora_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (ws == nullptr || ws_bytes < kCtrlBytes) return EPILORA_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return EPILORA_ERR_UNSUPPORTED;
+  return hip_status(launch_fill_u32(ws, 0u, (int64_t)(ws_bytes / 4), as_stream(stream)));
+}
+
+int epilora_device_error(void* ws, int32_t clear, int32_t* out_code, void* stream) {
+  if (ws == nullptr || out_code == nullptr) return EPILORA_ERR_INVALID_ARG;
+  hipStream_t s = as_stream(stream);
+  int32_t word = 0;
+  if (hipMemcpyAsync(&word, ws, sizeof(word), hipMemcpyDeviceToHost, s) != hipSuccess) return EPILORA_ERR_HIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return EPILORA_ERR_HIP;
+  *out_code = word;
+  if (clear) return hip_status(launch_fill_u32(ws, 0u, 1, s));
+  return EPILORA_OK;
+}
+
+int epilora_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* xq, int64_t ldq, float* sx,
+                      void* stream) {
+  const int st = check_rows(x, M, K, ldx, xq, ldq, sx);
+  if (st != EPILORA_OK || M == 0) return st;
+  return hip_status(launch_quant_rows(x, M, K, ldx, xq, ldq, sx, as_stream(stream)));
+}
+
+int epilora_quant_weight_fp8(const uint16_t* w, int64_t N, int64_t K, uint8_t* wq, float* sw, void* stream) {
+  const int st = check_rows(w, N, K, K, wq, K, sw);
+  if (st != EPILORA_OK || N == 0) return st;
+  return hip_status(launch_quant_rows(w, N, K, K, wq, K, sw, as_stream(stream)));
+}
+
+int epilora_quant_weight_fp4(const uint16_t* w, int64_t N, int64_t K, uint8_t* wc, uint8_t* bs, float* gs,
+                             void* ws, size_t ws_bytes, void* stream) {
+  if (N < 0 || K < 0) return EPILORA_ERR_INVALID_ARG;
+  if (N == 0 || K == 0) return EPILORA_OK;
+  if (w == nullptr || wc == nullptr || bs == nullptr || gs == nullptr) return EPILORA_ERR_INVALID_ARG;
+  if (K % 32 != 0) return EPILORA_ERR_UNSUPPORTED;
+  if (!aligned(w, 16) || !aligned(wc, 8) || !aligned(gs, 4)) return EPILORA_ERR_UNSUPPORTED;
+  const int st = check_ws(ws, ws_bytes, kCtrlBytes);
+  if (st != EPILORA_OK) return st;
+  return hip_status(launch_quant_weight_fp4(w, N, K, wc, bs, gs, ws, as_stream(stream)));
+}
+
+int epilora_lora_shrink(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* A, int32_t L,
+                        int32_t r, const int32_t* ranks, const int32_t* idx, const uint8_t* mask, float* z,
+                        void* ws, size_t ws_bytes, void* stream) {
+  if (M < 0 || K < 0) return EPILORA_ERR_INVALID_ARG;
+  if (M == 0) return EPILORA_OK;
+  if (x == nullptr || z == nullptr) return EPILORA_ERR_INVALID_ARG;
+  int st = check_adapters(L, r, A, true, nullptr, false, ranks, idx);
+  if (st != EPILORA_OK) return st;
+  if (ldx < K) return EPILORA_ERR_INVALID_ARG;
+  if (K % 16 != 0 || ldx % 16 != 0 || !aligned(x, 16) || !aligned(z, 16)) return EPILORA_ERR_UNSUPPORTED;
+  st = check_ws(ws, ws_bytes, shrink_ws(kCtrlBytes, M, K, r).total);
+  if (st != EPILORA_OK) return st;
+  AdapterArgs ad;
+  ad.A = A; ad.B = nullptr; ad.ranks = ranks; ad.idx = idx; ad.mask = mask;
+  ad.L = L; ad.r = r; ad.scale = 1.0f;
+  return hip_status(launch_shrink(x, M, K, ldx, ad, z, ws, as_stream(stream)));
+}
+
+int epilora_gemm_lora(const epilora_layer_args* a, void* stream) {
+  if (a == nullptr) return EPILORA_ERR_INVALID_ARG;
+  if (a->M < 0 || a->N < 0 || a->K < 0) return EPILORA_ERR_INVALID_ARG;
+  if (a->M == 0 || a->N == 0) return EPILORA_OK;
+  if (a->xq == nullptr || a->sx == nullptr || a->y == nullptr) return EPILORA_ERR_INVALID_ARG;
+  int st = check_weights(a);
+  if (st != EPILORA_OK) return st;
+  if (a->ldq < a->K || a->ldy < a->N) return EPILORA_ERR_INVALID_ARG;
+  if (a->ldq % 16 != 0 || !aligned(a->xq, 16) || !aligned(a->sx, 4) || !aligned(a->y, 2))
+    return EPILORA_ERR_UNSUPPORTED;
+  const bool lora = a->z != nullptr;
+  if (lora) {
+    st = check_adapters(a->L, a->r, a->A, false, a->B, true, a->ranks, a->idx);
+    if (st != EPILORA_OK) return st;
+    if (!aligned(a->z, 16)) return EPILORA_ERR_UNSUPPORTED;
+    st = check_ws(a->ws, a->ws_bytes, kCtrlBytes);
+    if (st != EPILORA_OK) return st;
+  }
+  return hip_status(launch_gemm_lora(a->xq, a->sx, a->ldq, a->M, a->N, a->K, weights_of(a), adapters_of(a, lora),
+                                     a->z, a->y, a->ldy, a->ws, as_stream(stream)));
+}
+
+int epilora_lora_expand_add(const float* z, int64_t M, int64_t N, const uint16_t* B, int32_t L, int32_t r,
+                            const int32_t* ranks, const int32_t* idx, const uint8_t* mask, float scale, uint16_t* y,
+                            int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
+  if (M < 0 || N < 0) return EPILORA_ERR_INVALID_ARG;
+  if (M == 0 || N == 0) return EPILORA_OK;
+  if (z == nullptr || y == nullptr) return EPILORA_ERR_INVALID_ARG;
+  int st = check_adapters(L, r, nullptr, false, B, true, ranks, idx);
+  if (st != EPILORA_OK) return st;
+  if (ldy < N) return EPILORA_ERR_INVALID_ARG;
+  if (!aligned(z, 16) || !aligned(y, 2)) return EPILORA_ERR_UNSUPPORTED;
+  st = check_ws(ws, ws_bytes, kCtrlBytes);
+  if (st != EPILORA_OK) return st;
+  AdapterArgs ad;
+  ad.A = nullptr; ad.B = B; ad.ranks = ranks; ad.idx = idx; ad.mask = mask;
+  ad.L = L; ad.r = r; ad.scale = scale;
+  return hip_status(launch_expand_add(z, M, N, ad, y, ldy, ws, as_stream(stream)));
+}
+
+int epilora_decode_lora(const epilora_layer_args* a, void* stream) {
+  if (a == nullptr) return EPILORA_ERR_INVALID_ARG;
+  if (a->M < 0 || a->N < 0 || a->K < 0) return EPILORA_ERR_INVALID_ARG;
+  if (a->M == 0 || a->N == 0) return EPILORA_OK;
+  if (a->M > EPILORA_DECODE_MAX_M) return EPILORA_ERR_UNSUPPORTED;
+  if (a->x == nullptr || a->y == nullptr) return EPILORA_ERR_INVALID_ARG;
+  int st = check_weights(a);
+  if (st != EPILORA_OK) return st;
+  if (a->ldx < a->K || a->ldy < a->N) return EPILORA_ERR_INVALID_ARG;
+  if (a->ldx % 16 != 0 || !aligned(a->x, 16) || !aligned(a->y, 2)) return EPILORA_ERR_UNSUPPORTED;
+  if (a->xq_out != nullptr) {
+    if (a->ldq_out < a->K) return EPILORA_ERR_INVALID_ARG;
+    if (a->ldq_out % 16 != 0 || !aligned(a->xq_out, 16)) return EPILORA_ERR_UNSUPPORTED;
+  }
+  if (a->sx_out != nullptr && !aligned(a->sx_out, 4)) return EPILORA_ERR_UNSUPPORTED;
+  const bool lora = a->idx != nullptr;
+  int32_t r = 16;
+  if (lora) {
+    st = check_adapters(a->L, a->r, a->A, true, a->B, true, a->ranks, a->idx);
+    if (st != EPILORA_OK) return st;
+    r = a->r;
+  }
+  st = check_ws(a->ws, a->ws_bytes, decode_ws(a->M, a->K, r).total);
+  if (st != EPILORA_OK) return st;
+  AdapterArgs ad = adapters_of(a, lora);
+  return hip_status(launch_decode_lora(a->x, a->ldx, a->M, a->N, a->K, weights_of(a), ad, a->y, a->ldy, a->xq_out,
+                                       a->sx_out, a->ldq_out, a->ws, as_stream(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,173 @@
+// Device-side helpers shared by the gfx950 kernels: number formats, wave
+// reductions, matrix-core wrappers and agent-scope flags.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace epilora {
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// bf16
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16, round to nearest even (finite inputs; NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (u >> 16) | 0x40u;
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------------------
+// FP8 E4M3FN (OCP): bias 7, 3 mantissa bits, max 448, S.1111.111 = NaN
+// ---------------------------------------------------------------------------
+
+// fp32 -> E4M3 code: nearest, ties to even, |q| >= 448 saturates to 448, the
+// sign is kept (-0 -> 0x80).  Pure integer/exact arithmetic.
+__device__ __forceinline__ uint32_t e4m3_encode(float q) {
+  const uint32_t u = __float_as_uint(q);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7FFFFFFFu;
+  uint32_t code;
+  if (a >= 0x43E00000u) {          // |q| >= 448 (or NaN): saturate
+    code = 0x7Eu;
+  } else if (a < 0x3C800000u) {    // |q| < 2^-6: subnormal grid, step 2^-9
+    // the scaling by 2^9 is exact; rint rounds to nearest even
+    code = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  } else {                         // normal: keep 3 of the 23 mantissa bits
+    const uint32_t mant = a & 0x7FFFFFu;
+    code = (((a >> 23) - 120u) << 3) | (mant >> 20);
+    const uint32_t rem = mant & 0xFFFFFu;
+    code += (rem > 0x80000u) || (rem == 0x80000u && (code & 1u));
+  }
+  return code | sign;
+}
+
+// E4M3 code -> fp32 (exact).
+__device__ __forceinline__ float e4m3_decode(uint32_t c) {
+  const uint32_t s = (c & 0x80u) << 24;
+  const uint32_t e = (c >> 3) & 0xFu;
+  const uint32_t m = c & 0x7u;
+  if (e == 0xFu && m == 0x7u) return __uint_as_float(0x7FC00000u);
+  if (e == 0) return __uint_as_float(s | __float_as_uint((float)m * 0.001953125f));
+  return __uint_as_float(s | ((e + 120u) << 23) | (m << 20));
+}
+
+// E2M1 magnitude code (0..7) -> fp32.
+__device__ __forceinline__ float e2m1_magnitude(uint32_t c) {
+  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  if (e == 0) return m ? 0.5f : 0.0f;
+  return __uint_as_float(((e + 126u) << 23) | (m << 22));
+}
+
+// fp32 -> E2M1 code: nearest, ties to the even code, saturated at 6.
+__device__ __forceinline__ uint32_t e2m1_encode(float v) {
+  const float a = fabsf(v);
+  uint32_t c;
+  if (a <= 0.25f) c = 0;
+  else if (a < 0.75f) c = 1;
+  else if (a <= 1.25f) c = 2;
+  else if (a < 1.75f) c = 3;
+  else if (a <= 2.5f) c = 4;
+  else if (a < 3.5f) c = 5;
+  else if (a <= 5.0f) c = 6;
+  else c = 7;
+  return c | ((__float_as_uint(v) >> 28) & 0x8u);
+}
+
+// One entry of the fold table: the FP8 byte that a 4-bit magnitude code c
+// (0..7) becomes under block scale b: E4M3(e2m1(c) * e4m3(b) / 8).  The
+// product is exact in fp32; only the encode rounds.  NaN scales give 0x7F.
+__device__ __forceinline__ uint32_t fold_entry(uint32_t c, uint32_t b) {
+  if ((b & 0x7Fu) == 0x7Fu) return 0x7Fu;
+  return e4m3_encode(e2m1_magnitude(c) * e4m3_decode(b) * 0.125f);
+}
+
+// Decode 8 packed E2M1 codes (one dword, element 0 in the low nibble) into 8
+// FP8 bytes, in element order, given the 8-entry magnitude table of their
+// block (tlo: codes 0..3, thi: codes 4..7).  The sign nibble bit flips the
+// sign bit of the looked-up byte.
+__device__ __forceinline__ void fold8(uint32_t d, uint32_t tlo, uint32_t thi,
+                                      uint32_t& out0, uint32_t& out1) {
+  const uint32_t sel_even = d & 0x07070707u;
+  const uint32_t sel_odd = (d >> 4) & 0x07070707u;
+  const uint32_t even = __builtin_amdgcn_perm(thi, tlo, sel_even) ^ ((d & 0x08080808u) << 4);
+  const uint32_t odd = __builtin_amdgcn_perm(thi, tlo, sel_odd) ^ (d & 0x80808080u);
+  out0 = __builtin_amdgcn_perm(odd, even, 0x05010400u);  // e0 e1 e2 e3
+  out1 = __builtin_amdgcn_perm(odd, even, 0x07030602u);  // e4 e5 e6 e7
+}
+
+// ---------------------------------------------------------------------------
+// Reductions
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t o = (uint32_t)__shfl_xor((int)v, off, kWave);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Matrix cores
+// ---------------------------------------------------------------------------
+
+// C[16][16] += A[16][128] * B[128][16], both operands E4M3 (32 bytes per
+// lane).  Zero scale operands select the unscaled instruction.
+__device__ __forceinline__ f32x4 mfma_fp8_16x16x128(const i32x8& a, const i32x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// C[16][16] += A[16][32] * B[32][16], bf16 operands (8 per lane).
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x32(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ i32x8 as_i32x8(const uint4& lo, const uint4& hi) {
+  i32x8 r;
+  r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+  r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Agent-scope counters and flags (visible across the chip's XCDs)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ int atomic_add_acq_rel(int* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void atomic_add_release(int* p, int v) {
+  __hip_atomic_fetch_add(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int load_acquire(int* p) {
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_relaxed(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void atomic_or_relaxed(int* p, int v) {
+  __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace epilora

@@ -1,0 +1,53 @@
+// Host-side launchers of the gfx950 kernels (internal to the library; the
+// public ABI is include/epilora.h).  Every launcher assumes its arguments
+// were validated by the API layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace epilora {
+
+// Adapter metadata as the kernels see it.
+struct AdapterArgs {
+  const uint16_t* A;     // [L][r][K]
+  const uint16_t* B;     // [L][N][r]
+  const int32_t* ranks;  // [L] or null
+  const int32_t* idx;    // [M] or null (no adapters)
+  const uint8_t* mask;   // [M] or null
+  int32_t L, r;
+  float scale;
+};
+
+// Base-weight operand.
+struct WeightArgs {
+  int32_t fmt;           // 0 = FP8 per channel, 1 = 4-bit (fold to FP8)
+  const uint8_t* w;
+  const float* sw;
+  const uint8_t* bs;
+  const float* gs;
+};
+
+hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* xq,
+                             int64_t ldq, float* scale, hipStream_t stream);
+hipError_t launch_quant_weight_fp4(const uint16_t* w, int64_t N, int64_t K, uint8_t* wc, uint8_t* bs,
+                                   float* gs, void* ws, hipStream_t stream);
+hipError_t launch_fill_u32(void* p, uint32_t v, int64_t n, hipStream_t stream);
+
+hipError_t launch_shrink(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const AdapterArgs& ad,
+                         float* z, void* ws, hipStream_t stream);
+hipError_t launch_expand_add(const float* z, int64_t M, int64_t N, const AdapterArgs& ad, uint16_t* y,
+                             int64_t ldy, void* ws, hipStream_t stream);
+
+// The GEMM with the multi-adapter epilogue.  z == null: base only.
+hipError_t launch_gemm_lora(const uint8_t* xq, const float* sx, int64_t ldq, int64_t M, int64_t N,
+                            int64_t K, const WeightArgs& wt, const AdapterArgs& ad, const float* z,
+                            uint16_t* y, int64_t ldy, void* ws, hipStream_t stream);
+
+// The fused decode path.
+hipError_t launch_decode_lora(const uint16_t* x, int64_t ldx, int64_t M, int64_t N, int64_t K,
+                              const WeightArgs& wt, const AdapterArgs& ad, uint16_t* y, int64_t ldy,
+                              uint8_t* xq_out, float* sx_out, int64_t ldq_out, void* ws,
+                              hipStream_t stream);
+
+}  // namespace epilora

@@ -1,0 +1,73 @@
+// Workspace layout and launch-shape rules shared by the host API and the
+// kernels.  Host and device code both include this file.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace epilora {
+
+// Control block at the start of every workspace (int32 words).
+constexpr size_t kCtrlBytes = 256;
+constexpr int kCtrlError = 0;      // device error word (sticky bits)
+constexpr int kCtrlAmax = 1;       // 4-bit weight quantizer: global amax bits
+constexpr int kCtrlQuantDone = 8;  // fused path: rows quantized
+constexpr int kCtrlZDone = 9;      // fused path: shrink tiles combined
+constexpr int kCtrlGemmDone = 10;  // fused path: GEMM workgroups finished
+
+constexpr size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+constexpr int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---- shrink -----------------------------------------------------------------
+// One workgroup = 4 waves over 16 tokens and a K range made of 128-wide
+// steps; the K range is split over `splits` workgroups whose partial sums are
+// combined in a fixed order by the last one to finish.
+constexpr int kShrinkTokens = 16;
+constexpr int kShrinkStep = 128;
+
+inline int shrink_splits(int64_t M, int64_t K) {
+  const int64_t steps = cdiv(K, kShrinkStep);
+  const int64_t tiles = cdiv(M, kShrinkTokens);
+  int64_t s = cdiv(steps, 4);              // at most one step per wave
+  const int64_t want = cdiv(1024, tiles);  // enough workgroups to fill the chip
+  if (s > want) s = want;
+  if (s < 1) s = 1;
+  return (int)s;
+}
+
+struct ShrinkWs {
+  size_t counters;  // int32 [tiles]
+  size_t partials;  // float [splits][M][r]
+  size_t total;
+};
+
+inline ShrinkWs shrink_ws(size_t base, int64_t M, int64_t K, int32_t r) {
+  ShrinkWs w;
+  const int64_t tiles = cdiv(M, kShrinkTokens);
+  const int s = shrink_splits(M, K);
+  w.counters = base;
+  w.partials = align256(w.counters + 4 * (size_t)tiles);
+  w.total = align256(w.partials + (s > 1 ? (size_t)s * M * r * 4 : 0));
+  return w;
+}
+
+// ---- fused decode path ------------------------------------------------------
+struct DecodeWs {
+  size_t xq;     // uint8 [M][K] (when the caller keeps no copy)
+  size_t sx;     // float [M]
+  size_t z;      // float [M][r]
+  ShrinkWs shrink;
+  size_t total;
+};
+
+inline DecodeWs decode_ws(int64_t M, int64_t K, int32_t r) {
+  DecodeWs w;
+  w.xq = kCtrlBytes;
+  w.sx = align256(w.xq + (size_t)M * K);
+  w.z = align256(w.sx + 4 * (size_t)M);
+  w.shrink = shrink_ws(align256(w.z + 4 * (size_t)M * r), M, K, r);
+  w.total = w.shrink.total;
+  return w;
+}
+
+}  // namespace epilora

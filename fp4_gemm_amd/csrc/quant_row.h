@@ -1,0 +1,96 @@
+// Per-row dynamic E4M3 quantization as a workgroup-level device function,
+// used by the quantization kernel and by the fused decode path.
+#pragma once
+
+#include "device.h"
+
+namespace epilora {
+
+// ---------------------------------------------------------------------------
+// Per-row dynamic E4M3.  One 256-thread workgroup per row.  Each thread holds
+// up to kRegVecs 16-byte vectors (8 bf16 each) of the row in registers, so a
+// row of up to 32768 elements is read from HBM once; longer rows are read a
+// second time for the encode pass.
+// amax: the largest |x| is the largest 15-bit bf16 magnitude, an integer max.
+// scale: amax / 448, an IEEE division (built with correctly rounded fp32
+// division); 1.0 for an all-zero row.  code: E4M3(x / scale), one IEEE
+// division per element.
+// ---------------------------------------------------------------------------
+constexpr int kQuantThreads = 256;
+constexpr int kRegVecs = 16;
+
+__device__ __forceinline__ uint32_t absmax8(const uint4& v) {
+  uint32_t m = 0;
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = w[i] & 0x7FFFu, hi = (w[i] >> 16) & 0x7FFFu;
+    m = m > lo ? m : lo;
+    m = m > hi ? m : hi;
+  }
+  return m;
+}
+
+__device__ __forceinline__ uint2 encode8(const uint4& v, float s) {
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t out[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t c0 = e4m3_encode(bf16_lo(w[2 * h]) / s);
+    const uint32_t c1 = e4m3_encode(bf16_hi(w[2 * h]) / s);
+    const uint32_t c2 = e4m3_encode(bf16_lo(w[2 * h + 1]) / s);
+    const uint32_t c3 = e4m3_encode(bf16_hi(w[2 * h + 1]) / s);
+    out[h] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+  }
+  return make_uint2(out[0], out[1]);
+}
+
+// Block-wide max of a uint32 over 256 threads.
+__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
+  v = wave_max_u32(v);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) red[wave] = v;
+  __syncthreads();
+  uint32_t m = red[0];
+#pragma unroll
+  for (int i = 1; i < kQuantThreads / kWave; ++i) m = m > red[i] ? m : red[i];
+  return m;
+}
+
+__device__ __forceinline__ float row_scale(uint32_t amax_bits) {
+  const float amax = bf16_to_f32((uint16_t)amax_bits);
+  return amax == 0.0f ? 1.0f : amax / 448.0f;
+}
+
+// Quantize one row of bf16 values into E4M3 codes and its scale, with the
+// 256 threads of the calling workgroup.  `red` is 4 words of LDS.
+__device__ __forceinline__ void quant_row(const uint16_t* __restrict__ xrow, int64_t K, uint8_t* __restrict__ qrow,
+                                          float* __restrict__ scale_out, uint32_t* red) {
+  const uint4* src = reinterpret_cast<const uint4*>(xrow);
+  uint2* dst = reinterpret_cast<uint2*>(qrow);
+  const int nv = (int)(K / 8);
+  const int tid = threadIdx.x;
+
+  uint4 v[kRegVecs];
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < kRegVecs; ++i) {
+    const int j = tid + i * kQuantThreads;
+    if (j < nv) {
+      v[i] = src[j];
+      amax = max(amax, absmax8(v[i]));
+    }
+  }
+  for (int j = tid + kRegVecs * kQuantThreads; j < nv; j += kQuantThreads) amax = max(amax, absmax8(src[j]));
+  amax = block_max_u32(amax, red);
+  const float s = row_scale(amax);
+  if (tid == 0) *scale_out = s;
+#pragma unroll
+  for (int i = 0; i < kRegVecs; ++i) {
+    const int j = tid + i * kQuantThreads;
+    if (j < nv) dst[j] = encode8(v[i], s);
+  }
+  for (int j = tid + kRegVecs * kQuantThreads; j < nv; j += kQuantThreads) dst[j] = encode8(src[j], s);
+}
+
+}  // namespace epilora

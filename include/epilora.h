@@ -1,0 +1,249 @@
+/*
+ * epilora.h -- C ABI of a multi-tenant LoRA linear layer on a low-precision
+ * (FP8 or 4-bit) base, for AMD Instinct MI355X (gfx950).
+ *
+ * For every token t with tenant index a_t the layer computes
+ *
+ *     Y[t] = bf16( dequant(W_q . quant(x_t)) + s * B[a_t] (A[a_t] x_t) )
+ *
+ * where a_t = -1 means "no adapter" and an optional per-token mask limits the
+ * adapter to flagged (prefill) tokens.  The method is described in
+ * "EpiLoRA: Fusing Many LoRA Adapters into Low-Precision GEMMs for Serving and
+ * RL" (Background; Design, section "Multi-adapter kernels": K1 quantizes the
+ * activations once and forms the down-projection from the bf16 activations,
+ * K2 runs the low-precision GEMM and adds each adapter group's up-projection
+ * in its epilogue; the decode path overlaps the down-projection with the
+ * GEMM's main loop) and, for the mask, "PreFT: Prefill-only finetuning for
+ * efficient inference" (abstract; Figure 6: a per-forward position mask
+ * written outside the compiled region, adapter parameters at stable
+ * addresses).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every buffer pointer is a DEVICE pointer owned by the caller.  The
+ *   library never allocates, frees, retains or copies them, never
+ *   synchronizes the stream, and keeps no global state: calls are reentrant
+ *   and may be captured in a HIP graph.  (The pages' fused call is a custom
+ *   operator captured in the engine's CUDA graphs and reads the engine's own
+ *   adapter buffers and batching metadata in place: "The vLLM plugin".)
+ * - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ * - bf16 values are passed as their uint16_t bit patterns; FP8 is OCP E4M3FN
+ *   (bias 7, max 448, no infinity); 4-bit weights are E2M1 codes.
+ * - Matrices are row-major with the given leading dimension (in elements).
+ *   The leading dimensions of inputs (ldx, ldq) must be multiples of 16 and
+ *   input matrix pointers 16-byte aligned; outputs (y, ldy >= N) take any
+ *   2-byte-aligned layout.  M = 0 or N = 0 is a valid call that does nothing.
+ * - Host-side validation happens before any HIP call; a failing call
+ *   launches nothing.  Content that lives on the device (indices, ranks) is
+ *   checked in the kernels: an index outside [-1, L) is treated as -1 and
+ *   raises EPILORA_DEV_BAD_INDEX in the workspace's device error word.
+ * - Inputs must be finite.
+ *
+ * Status codes: EPILORA_OK, EPILORA_ERR_INVALID_ARG (a null pointer, a
+ * negative size, a bad enum), EPILORA_ERR_UNSUPPORTED (a valid request this
+ * library does not serve, e.g. an alignment or a batch too large for the
+ * fused decode path: the caller's cue to fall back, as the pages' plugin
+ * falls back to the engine's own path), EPILORA_ERR_WORKSPACE (workspace
+ * missing or too small), EPILORA_ERR_HIP (a HIP launch failed).
+ */
+#ifndef EPILORA_H
+#define EPILORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define EPILORA_VERSION 10000 /* 1.0.0 */
+
+enum epilora_status {
+  EPILORA_OK = 0,
+  EPILORA_ERR_INVALID_ARG = 1,
+  EPILORA_ERR_UNSUPPORTED = 2,
+  EPILORA_ERR_WORKSPACE = 3,
+  EPILORA_ERR_HIP = 4
+};
+
+/* Bits of the device error word kept in a workspace (sticky until cleared). */
+enum epilora_device_error_bits {
+  EPILORA_DEV_BAD_INDEX = 1,   /* an index outside [-1, L) was treated as -1 */
+  EPILORA_DEV_WAIT_TIMEOUT = 2 /* the fused path's bounded wait expired; the
+                                  outputs of that call are not valid */
+};
+
+/* Weight formats. */
+enum epilora_wfmt {
+  EPILORA_W_FP8 = 0, /* w: E4M3 [N][K]; sw: fp32 [N] (per output channel) */
+  EPILORA_W_FP4 = 1  /* w: packed E2M1 [N][K/2], element 2i in the low
+                        nibble of byte i; bs: E4M3 [N][K/16], one scale per
+                        16 consecutive elements along K; gs: one fp32 */
+};
+
+/* Operations, for epilora_workspace_bytes. */
+enum epilora_op {
+  EPILORA_OP_SHRINK = 1,
+  EPILORA_OP_GEMM = 2,
+  EPILORA_OP_EXPAND = 3,
+  EPILORA_OP_DECODE = 4,
+  EPILORA_OP_QUANT_W4 = 5
+};
+
+/* Largest batch the fused decode path serves (the pages use the decode path
+ * for batches of up to 32 tokens; this library's kernel takes up to 64). */
+#define EPILORA_DECODE_MAX_M 64
+/* Largest adapter rank (slot width r). */
+#define EPILORA_MAX_RANK 128
+
+/* Arguments of epilora_gemm_lora and epilora_decode_lora. */
+typedef struct epilora_layer_args {
+  int64_t M, N, K;          /* tokens, output features, input features */
+  /* Activations. */
+  const uint16_t* x;        /* bf16 [M][ldx]; read by epilora_decode_lora */
+  int64_t ldx;
+  const uint8_t* xq;        /* E4M3 [M][ldq]; read by epilora_gemm_lora */
+  const float* sx;          /* fp32 [M] per-token scales (gemm_lora) */
+  int64_t ldq;
+  /* Base weights. */
+  int32_t wfmt;             /* enum epilora_wfmt */
+  const uint8_t* w;
+  const float* sw;          /* EPILORA_W_FP8 */
+  const uint8_t* bs;        /* EPILORA_W_FP4 */
+  const float* gs;          /* EPILORA_W_FP4: device pointer to one float */
+  /* Adapters, in the caller's stacked slots. */
+  int32_t L, r;             /* slots, slot width (rank padded), r <= 128 */
+  const uint16_t* A;        /* bf16 [L][r][K]; read by epilora_decode_lora */
+  const uint16_t* B;        /* bf16 [L][N][r] */
+  const int32_t* ranks;     /* [L] true ranks (<= r) or NULL (all r);
+                               columns j >= rank are ignored, rank 0 means
+                               the adapter is off */
+  const int32_t* idx;       /* [M] tenant per token, -1 = none */
+  const uint8_t* mask;      /* [M], nonzero = adapter applies; NULL = all */
+  const float* z;           /* fp32 [M][r] down-projection from
+                               epilora_lora_shrink (gemm_lora only);
+                               NULL = base GEMM only */
+  float scale;              /* LoRA scaling s */
+  /* Output. */
+  uint16_t* y;              /* bf16 [M][ldy] */
+  int64_t ldy;
+  /* epilora_decode_lora: where the quantized activations go (E4M3
+     [M][ldq_out] and fp32 [M]); NULL = kept in the workspace only. */
+  uint8_t* xq_out;
+  float* sx_out;
+  int64_t ldq_out;
+  /* Scratch. */
+  void* ws;
+  size_t ws_bytes;
+} epilora_layer_args;
+
+/* Library version (EPILORA_VERSION of the build). */
+int epilora_version(void);
+
+/* Static text for a status code. */
+const char* epilora_strerror(int status);
+
+/* Bytes of workspace `op` needs for a call of the given sizes (r = slot
+ * width); each call checks its own need against ws_bytes.  One workspace may
+ * serve every call on one stream in turn (the pages' plugin shares its
+ * scratch buffers across layers: "The vLLM plugin", Memory); calls that
+ * overlap in time must not share one. */
+size_t epilora_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K,
+                               int32_t r);
+
+/* Zero a workspace (a fill kernel, safe inside graph capture).  Required once
+ * after allocation; every call leaves its counters at zero again. */
+int epilora_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Read the device error word of a workspace into *out_code: enqueues a copy
+ * on `stream` and waits for it (a synchronizing diagnostic, not for use
+ * inside graph capture).  Then clears the word when `clear` is nonzero. */
+int epilora_device_error(void* ws, int32_t clear, int32_t* out_code,
+                         void* stream);
+
+/* Per-token dynamic FP8 quantization ("Multi-adapter kernels", K1).
+ * For each row t: amax = max_k |x[t][k]|; sx[t] = fp32(amax / 448) (IEEE
+ * division; 1.0 for an all-zero row); xq[t][k] = E4M3(fp32(x[t][k] / sx[t]))
+ * rounded to nearest even and saturated at +-448.  Bit-exact.
+ * x: bf16 [M][ldx]; xq: [M][ldq]; sx: [M].  K % 16 == 0. */
+int epilora_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                      uint8_t* xq, int64_t ldq, float* sx, void* stream);
+
+/* Load-time FP8 weight quantization, one scale per output channel (the
+ * pages' FP8 bases are quantized when the model loads: Evaluation, Setup).
+ * Same rule as epilora_quant_act applied to the rows of W.
+ * w: bf16 [N][K]; wq: [N][K]; sw: [N].  K % 16 == 0. */
+int epilora_quant_weight_fp8(const uint16_t* w, int64_t N, int64_t K,
+                             uint8_t* wq, float* sw, void* stream);
+
+/* Load-time 4-bit weight quantization in the NVFP4 layout.
+ * gs = fp32(amax(W) / 2688) (1.0 if W is zero);
+ * bs[n][b] = E4M3(fp32(amax(block) / fp32(6 * gs)));
+ * code = E2M1(fp32(w / fp32(e4m3(bs) * gs))) (nearest even, saturated at 6;
+ * 0 where that product is 0).  w: bf16 [N][K]; wc: [N][K/2]; bs: [N][K/16];
+ * gs: one float.  K % 32 == 0.  Needs a workspace of EPILORA_OP_QUANT_W4. */
+int epilora_quant_weight_fp4(const uint16_t* w, int64_t N, int64_t K,
+                             uint8_t* wc, uint8_t* bs, float* gs, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* The shrink ("Multi-adapter kernels", K1: h = x A^T from the bf16
+ * activations, the sum over K split across workgroups).
+ * z[t][j] = sum_k A[idx[t]][j][k] * x[t][k] (fp32 accumulation) for active
+ * tokens and j < rank; 0 elsewhere.  A token is active when idx[t] is in
+ * [0, L), its mask byte (if any) is nonzero and its rank is positive.
+ * Split-K partial sums are combined in a fixed order, so results are
+ * deterministic ("The decode path").  x: bf16 [M][ldx]; A: bf16 [L][r][K];
+ * z: fp32 [M][r].  K % 16 == 0, r % 16 == 0, r <= 128.
+ * Needs a workspace of EPILORA_OP_SHRINK. */
+int epilora_lora_shrink(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
+                        const uint16_t* A, int32_t L, int32_t r,
+                        const int32_t* ranks, const int32_t* idx,
+                        const uint8_t* mask, float* z, void* ws,
+                        size_t ws_bytes, void* stream);
+
+/* The low-precision GEMM with the multi-adapter epilogue
+ * ("Multi-adapter kernels", K2; "Kernel details", one output tile of K2).
+ * base[t][n] = (acc[t][n] * sx[t]) * sw[n] for FP8 weights, where
+ * acc = sum_k e4m3(xq[t][k]) * e4m3(w[n][k]) in fp32; for 4-bit weights each
+ * weight is first decoded to the FP8 byte E4M3(e2m1(code) * e4m3(bs) / 8)
+ * and base = (acc * sx[t]) * (gs * 8).  Active rows (as in
+ * epilora_lora_shrink) get y = base + s * sum_j B[idx[t]][n][j] * z[t][j];
+ * the other rows get y = base with no add at all, so they are bitwise equal
+ * to the base-only GEMM.  Y = bf16(y), round to nearest even.
+ * Tokens may come in any order; runs of equal indices (tokens sorted by
+ * adapter) make the epilogue cheaper.  K % 32 == 0.  With z == NULL the call
+ * is the base GEMM only and needs no workspace. */
+int epilora_gemm_lora(const epilora_layer_args* args, void* stream);
+
+/* The separate up-projection used by the pages' baseline path (Background,
+ * "The cost of the separate adapter path": the expand reads, adds to and
+ * writes the output again).  y[t][n] = bf16(y[t][n] + s * sum_j
+ * B[idx[t]][n][j] * z[t][j]) for active rows; other rows untouched.
+ * Needs a workspace of EPILORA_OP_EXPAND (device error word). */
+int epilora_lora_expand_add(const float* z, int64_t M, int64_t N,
+                            const uint16_t* B, int32_t L, int32_t r,
+                            const int32_t* ranks, const int32_t* idx,
+                            const uint8_t* mask, float scale, uint16_t* y,
+                            int64_t ldy, void* ws, size_t ws_bytes,
+                            void* stream);
+
+/* The fused small-batch (decode) path ("Multi-adapter kernels", The decode
+ * path): quantization, shrink and the GEMM with its epilogue in ONE launch.
+ * The lowest workgroups quantize x and compute z and publish each with a
+ * device flag (release/acquire, agent scope); the GEMM workgroups stream
+ * their weights meanwhile and wait for z only before the epilogue.  HIP has
+ * no programmatic dependent launch; this persistent split replaces it.
+ * After a call that raised EPILORA_DEV_WAIT_TIMEOUT, re-initialise the
+ * workspace (epilora_workspace_init) before using it again.
+ * Same result as epilora_quant_act + epilora_lora_shrink +
+ * epilora_gemm_lora.  Reads x (not xq/sx/z).  M <= EPILORA_DECODE_MAX_M,
+ * else EPILORA_ERR_UNSUPPORTED.  Every wait is bounded; on expiry the
+ * kernel sets EPILORA_DEV_WAIT_TIMEOUT and returns without the epilogue.
+ * Needs a workspace of EPILORA_OP_DECODE. */
+int epilora_decode_lora(const epilora_layer_args* args, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EPILORA_H */

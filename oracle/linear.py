@@ -80,7 +80,7 @@ def quant_weight_fp8(w):
     return quant_rows_e4m3(bf16_to_f32(w))
 
 
-def quant_weight_fp4(w):
+def quant_weight_fp4(w, rows=None):
     """4-bit weight encoder in the NVFP4 layout: E2M1 codes, one E4M3 scale
     per 16 consecutive elements along K, one fp32 global scale.
 
@@ -88,12 +88,16 @@ def quant_weight_fp4(w):
     bs = E4M3(fp32(amax_block / fp32(6 * gs)));
     codes = E2M1(fp32(w / fp32(e4m3(bs) * gs))), or code 0 where that block
     scale is zero.  Element 2i goes in the low nibble of byte i.
-    Returns (wc uint8 [N][K/2], bs uint8 [N][K/16], gs float32)."""
+    Returns (wc uint8 [N][K/2], bs uint8 [N][K/16], gs float32).  With
+    `rows`, gs still comes from the whole matrix but only those rows are
+    encoded (each row's codes depend on its own values and gs only)."""
     wf = bf16_to_f32(w)
-    n, k = wf.shape
-    if k % 16:
+    if wf.shape[1] % 16:
         raise ValueError("K must be a multiple of 16")
     amax = np.float32(np.max(np.abs(wf)))
+    if rows is not None:
+        wf = wf[np.asarray(rows)]
+    n, k = wf.shape
     gs = np.float32(amax / np.float32(6.0 * 448.0)) if amax > 0 else np.float32(1.0)
     blocks = wf.reshape(n, k // 16, 16)
     amax_b = np.max(np.abs(blocks), axis=2).astype(np.float32)
@@ -223,14 +227,15 @@ def linear_lora(x, A, B, idx, scale, *, wq=None, sw=None, wc=None, bs=None,
 
     Returns a dict with xq, sx (bit-exact targets), z (float64), base,
     y (float64: base plus the adapter term on active rows, base alone on
-    the others) and the active-row flags.  rows/cols restrict base, z and y
-    to a sample of tokens and output channels."""
-    xq, sx = quant_act(x)
-    if wq is not None:
-        base = base_fp8(xq, sx, wq, sw, rows=rows, cols=cols)
-    else:
-        base = base_fp4(xq, sx, wc, bs, gs, rows=rows, cols=cols)
+    the others) and the active-row flags.  `rows` restricts every result
+    to a sample of tokens; to sample output channels either pass `cols`, or
+    pass the weights and B of the sampled channels only."""
     xs = _pick(x, rows)
+    xq, sx = quant_act(xs)  # per-token quantisation is row-local
+    if wq is not None:
+        base = base_fp8(xq, sx, wq, sw, cols=cols)
+    else:
+        base = base_fp4(xq, sx, wc, bs, gs, cols=cols)
     idx_s = _pick(np.asarray(idx), rows)
     mask_s = None if mask is None else _pick(np.asarray(mask), rows)
     z = shrink(xs, A, idx_s, ranks, mask_s)

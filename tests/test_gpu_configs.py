@@ -1,0 +1,118 @@
+"""GPU parity at the five workloads' full sizes, in the launch configuration
+the benchmark times: the fused decode path for the decode batches (M <= 64)
+and quant + shrink + tiled GEMM for the 2048-token prefill GEMMs.  The oracle
+computes a seeded sample of tokens and output channels; quantized
+activations and weight codes of the sample are bit-exact."""
+
+import numpy as np
+import pytest
+import torch
+
+import fp4_gemm_amd as ep
+from workloads import config
+
+from gpu_harness import DeviceGemm, compare, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ep.lib()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def sample(n, k, seed):
+    rng = np.random.default_rng(seed)
+    return np.sort(rng.choice(n, size=min(n, k), replace=False))
+
+
+def check(d, out, rows=None, ncols=256, seed=0, what=""):
+    cols = sample(d.N, ncols, seed)
+    ref = d.oracle(rows=rows, cols=cols)
+    xq = to_np(out["xq"]) if rows is None else to_np(out["xq"])[rows]
+    sx = to_np(out["sx"]) if rows is None else to_np(out["sx"])[rows]
+    assert np.array_equal(xq, ref["xq"]), f"{what}: activation codes"
+    assert np.array_equal(sx, ref["sx"]), f"{what}: activation scales"
+    if d.wfmt == "fp8":
+        assert np.array_equal(to_np(d.wq)[cols], ref["w"]["wq"]), f"{what}: weight codes"
+    else:
+        assert np.array_equal(to_np(d.wq)[cols], ref["w"]["wc"]), f"{what}: 4-bit codes"
+        assert np.array_equal(to_np(d.bs)[cols], ref["w"]["bs"]), f"{what}: block scales"
+    y = to_np(out["y"])
+    y = y[:, cols] if rows is None else y[np.ix_(rows, cols)]
+    mx, mean = compare(y, ref["y"], what)
+    say(f"  {what}: max|dY|/rms {mx:.2e}  mean rel {mean:.2e}")
+    return ref
+
+
+def test_config1_toy():
+    lay = config(1)
+    d = DeviceGemm(lay.gemms[0])
+    ref = d.oracle()
+    for out in (d.decode(), d.separate()):
+        compare(to_np(out["y"]), ref["y"], "toy")
+        assert np.array_equal(to_np(out["xq"]), ref["xq"])
+
+
+@pytest.mark.parametrize("name", ["qkv", "o", "gate_up", "down"])
+def test_config2_llama8b_decode(name):
+    say(f"config 2 {name}")
+    d = DeviceGemm(config(2).gemm(name))
+    fused = d.decode()
+    check(d, fused, seed=21, what=f"cfg2 {name} fused")
+    sep = d.separate()
+    assert torch.equal(sep["y"], fused["y"])
+    assert ep.epilora_device_error(fused["ws"]) == 0
+
+
+@pytest.mark.parametrize("name", ["qkv", "o", "gate_up", "down"])
+def test_config3_multitenant_decode(name):
+    say(f"config 3 {name}")
+    lay = config(3)
+    d = DeviceGemm(lay.gemm(name))
+    fused = d.decode()
+    ref = check(d, fused, seed=31, what=f"cfg3 {name} fused")
+    assert ref["active"].sum() == 28
+    # rows without an adapter equal the base GEMM bit for bit
+    xq, sx = d.quant()
+    base = to_np(d.gemm(xq, sx))
+    y = to_np(fused["y"])
+    assert np.array_equal(y[lay.idx < 0], base[lay.idx < 0])
+
+
+@pytest.mark.parametrize("name", ["qkv", "o", "gate_up", "down"])
+def test_config4_72b_preft(name):
+    for M in (64, 8, 1):
+        say(f"config 4 {name} M={M}")
+        lay = config(4, M=M)
+        d = DeviceGemm(lay.gemm(name))
+        fused = d.decode()
+        ref = check(d, fused, seed=40 + M, what=f"cfg4 {name} M={M}")
+        # PreFT: masked-off rows equal the base GEMM exactly
+        y = torch.empty_like(fused["y"])
+        ws = ep.new_workspace(ep.OP_DECODE, d.M, d.N, d.K, 16)
+        ep.epilora_decode_lora(d.x, d.wq, y, ws=ws, **d.wkw)
+        off = lay.mask == 0
+        assert np.array_equal(to_np(fused["y"])[off], to_np(y)[off])
+        assert ref["active"].sum() == int(np.ceil(0.75 * M))
+        del d
+
+
+@pytest.mark.parametrize("wfmt,segments,name", [
+    ("fp8", 16, "gate_up"), ("fp8", 16, "down"), ("fp4", 16, "gate_up"), ("fp4", 16, "down"),
+    ("fp8", 32, "gate_up"),
+])
+def test_config5_prefill(wfmt, segments, name):
+    say(f"config 5 {wfmt} {segments} segments {name}")
+    lay = config(5, segments=segments, wfmt=wfmt)
+    d = DeviceGemm(lay.gemm(name), wfmt)
+    out = d.separate()
+    rows = sample(d.M, 128, 50 + segments)
+    check(d, out, rows=rows, seed=51, what=f"cfg5 {wfmt} {name}")
+    assert ep.epilora_device_error(out["ws"]) == 0

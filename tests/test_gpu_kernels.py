@@ -1,0 +1,272 @@
+"""GPU parity of every entry point against the CPU oracle at small sizes that
+still span several tiles, ragged M / N / K tails and the degenerate cases
+(no adapter, rank 0, masked tokens, out-of-range indices, all-zero rows)."""
+
+import numpy as np
+import pytest
+import torch
+
+import fp4_gemm_amd as ep
+import oracle
+from workloads import bf16_bits, custom_layer
+
+from gpu_harness import DEV, DeviceGemm, bf16_np_to_f64, compare, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ep.lib()
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+# --- quantization -------------------------------------------------------------------
+
+def _special_rows(K, rng):
+    rows = []
+    rows.append(np.zeros(K, np.float32))                                  # all zero -> sx = 1
+    mids = (oracle.e4m3_decode(np.arange(0x7E)) + oracle.e4m3_decode(np.arange(1, 0x7F))) / 2
+    up = bf16_bits(mids.astype(np.float32))
+    near = np.concatenate([mids, (up.astype(np.uint32) << 16).view(np.float32),
+                           ((up + 1).astype(np.uint32) << 16).view(np.float32),
+                           ((up - 1).astype(np.uint32) << 16).view(np.float32)]).astype(np.float32)
+    r = np.resize(near * rng.choice([-1.0, 1.0], size=near.size), K).astype(np.float32)
+    r[0] = 448.0                                                           # sx = 1 exactly: ties land on midpoints
+    rows.append(r)
+    rows.append((rng.standard_normal(K) * 1e-36).astype(np.float32))     # tiny values
+    rows.append((rng.standard_normal(K) * 3e37).astype(np.float32))      # huge values
+    rows.append(np.resize(np.array([1.0, -0.0, 0.0, 2.0 ** -20], np.float32), K))
+    return np.stack(rows)
+
+
+@pytest.mark.parametrize("M,K", [(1, 16), (5, 256), (37, 4096), (3, 14336), (2, 40960)])
+def test_quant_act_bit_exact(M, K):
+    say(f"quant_act M={M} K={K}")
+    rng = np.random.default_rng(1000 + K)
+    x = bf16_bits(rng.standard_normal((M, K)).astype(np.float32) * np.float32(rng.uniform(0.01, 100)))
+    x = np.concatenate([x, bf16_bits(_special_rows(K, rng))])
+    xq_ref, sx_ref = oracle.quant_act(x)
+    xd = to_dev(x)
+    xq = torch.empty(x.shape, dtype=torch.uint8, device=DEV)
+    sx = torch.empty(x.shape[0], dtype=torch.float32, device=DEV)
+    ep.epilora_quant_act(xd, xq, sx)
+    assert np.array_equal(to_np(sx).view(np.uint32), sx_ref.view(np.uint32))
+    got = to_np(xq)
+    bad = np.argwhere(got != xq_ref)
+    assert bad.size == 0, f"{len(bad)} codes differ, first {bad[:5].tolist()}"
+
+
+def test_quant_act_strided_rows():
+    rng = np.random.default_rng(5)
+    x = bf16_bits(rng.standard_normal((6, 512)).astype(np.float32))
+    xq_ref, sx_ref = oracle.quant_act(x[:, :256])
+    xd = to_dev(x)[:, :256]
+    out = torch.full((6, 384), 0xAB, dtype=torch.uint8, device=DEV)
+    sx = torch.empty(6, dtype=torch.float32, device=DEV)
+    ep.epilora_quant_act(xd, out[:, :256], sx)
+    got = to_np(out)
+    assert np.array_equal(got[:, :256], xq_ref) and np.all(got[:, 256:] == 0xAB)
+    assert np.array_equal(to_np(sx), sx_ref)
+
+
+@pytest.mark.parametrize("N,K", [(3, 32), (300, 512), (64, 4096)])
+def test_weight_quantizers_bit_exact(N, K):
+    say(f"weight quant N={N} K={K}")
+    rng = np.random.default_rng(2000 + N)
+    w = bf16_bits(rng.standard_normal((N, K)).astype(np.float32) * np.float32(0.02))
+    w[0, :16] = 0                     # a zero block
+    w[-1] = 0                         # a zero row
+    wd = to_dev(w)
+    wq = torch.empty(N, K, dtype=torch.uint8, device=DEV)
+    sw = torch.empty(N, dtype=torch.float32, device=DEV)
+    ep.epilora_quant_weight_fp8(wd, wq, sw)
+    wq_ref, sw_ref = oracle.quant_weight_fp8(w)
+    assert np.array_equal(to_np(wq), wq_ref) and np.array_equal(to_np(sw), sw_ref)
+    wc = torch.empty(N, K // 2, dtype=torch.uint8, device=DEV)
+    bs = torch.empty(N, K // 16, dtype=torch.uint8, device=DEV)
+    gs = torch.empty(1, dtype=torch.float32, device=DEV)
+    ws = ep.new_workspace(ep.OP_QUANT_W4, 1, N, K, 16)
+    ep.epilora_quant_weight_fp4(wd, wc, bs, gs, ws)
+    wc_ref, bs_ref, gs_ref = oracle.quant_weight_fp4(w)
+    assert to_np(gs)[0] == gs_ref
+    assert np.array_equal(to_np(bs), bs_ref)
+    assert np.array_equal(to_np(wc), wc_ref)
+
+
+# --- shrink -----------------------------------------------------------------------------
+
+SHRINK_CASES = [
+    # M, K, L, r, idx kind, mask, ranks
+    (1, 4096, 1, 64, "zero", False, False),
+    (7, 256, 4, 16, "mixed", True, False),
+    (33, 4224, 6, 32, "mixed", False, True),
+    (100, 512, 3, 128, "sorted", True, True),
+    (16, 14336, 64, 64, "distinct", False, False),
+]
+
+
+def _idx(kind, M, L, rng):
+    if kind == "zero":
+        return np.zeros(M, np.int32)
+    if kind == "sorted":
+        return np.sort(rng.integers(-1, L, M)).astype(np.int32)
+    if kind == "distinct":
+        return rng.permutation(L)[:M].astype(np.int32)
+    return rng.integers(-1, L, M).astype(np.int32)
+
+
+@pytest.mark.parametrize("M,K,L,r,kind,use_mask,use_ranks", SHRINK_CASES)
+def test_shrink_vs_oracle(M, K, L, r, kind, use_mask, use_ranks):
+    say(f"shrink M={M} K={K} L={L} r={r} {kind}")
+    rng = np.random.default_rng(3000 + M + K)
+    idx = _idx(kind, M, L, rng)
+    mask = rng.integers(0, 2, M).astype(np.uint8) if use_mask else None
+    ranks = rng.choice([0, 8, r // 2, r, 21 if r > 21 else r], size=L).astype(np.int32) if use_ranks else None
+    lay = custom_layer("s", 300 + M, M, K, 64, L, r, idx, mask=mask, ranks=ranks)
+    d = DeviceGemm(lay.gemms[0])
+    z, ws = d.shrink()
+    z_ref = oracle.shrink(d.x_np, d.A_np, idx, ranks, mask)
+    zg = to_np(z).astype(np.float64)
+    scale = max(np.sqrt(np.mean(z_ref ** 2)), 1e-30)
+    assert np.abs(zg - z_ref).max() <= 1e-4 * scale
+    act, _, _ = oracle.active_rows(idx, L, r, ranks, mask)
+    assert not zg[~act].any()
+    # deterministic: the same call again gives the same bits
+    z2, _ = d.shrink(ws)
+    assert torch.equal(z, z2)
+
+
+# --- the GEMM with its epilogue -----------------------------------------------------------
+
+GEMM_CASES = [
+    # M, K, N, L, r, kind, mask, ranks, wfmt
+    (1, 256, 512, 1, 16, "zero", False, False, "fp8"),
+    (5, 160, 200, 4, 16, "mixed", True, False, "fp8"),
+    (16, 4096, 1024, 8, 64, "mixed", False, False, "fp8"),
+    (17, 512, 300, 4, 32, "mixed", True, True, "fp8"),
+    (33, 384, 128, 40, 64, "distinct", False, False, "fp8"),
+    (64, 1024, 272, 5, 128, "mixed", True, True, "fp8"),
+    (65, 256, 512, 4, 16, "sorted", False, False, "fp8"),
+    (130, 4096, 384, 6, 64, "sorted", True, True, "fp8"),
+    (257, 288, 200, 9, 32, "mixed", False, False, "fp8"),
+    (1, 256, 512, 1, 16, "zero", False, False, "fp4"),
+    (20, 4096, 512, 4, 64, "mixed", True, False, "fp4"),
+    (150, 1024, 300, 6, 32, "sorted", False, True, "fp4"),
+]
+
+
+@pytest.mark.parametrize("M,K,N,L,r,kind,use_mask,use_ranks,wfmt", GEMM_CASES)
+def test_gemm_lora_vs_oracle(M, K, N, L, r, kind, use_mask, use_ranks, wfmt):
+    say(f"gemm_lora M={M} K={K} N={N} L={L} r={r} {kind} {wfmt}")
+    rng = np.random.default_rng(4000 + M + K + N)
+    idx = _idx(kind, M, L, rng)
+    mask = rng.integers(0, 2, M).astype(np.uint8) if use_mask else None
+    ranks = rng.choice([0, 16, r // 2, r], size=L).astype(np.int32) if use_ranks else None
+    lay = custom_layer("g", 500 + M + N, M, K, N, L, r, idx, mask=mask, ranks=ranks, wfmt=wfmt)
+    d = DeviceGemm(lay.gemms[0], wfmt)
+    out = d.separate()
+    ref = d.oracle()
+    assert np.array_equal(to_np(out["xq"]), ref["xq"])
+    assert np.array_equal(to_np(out["sx"]), ref["sx"])
+    if wfmt == "fp8":
+        assert np.array_equal(to_np(d.wq), ref["w"]["wq"])
+    else:
+        assert np.array_equal(to_np(d.wq), ref["w"]["wc"]) and np.array_equal(to_np(d.bs), ref["w"]["bs"])
+    compare(to_np(out["y"]), ref["y"], f"M={M} N={N} {wfmt}")
+    # rows without an adapter equal the base-only GEMM bit for bit
+    base = d.gemm(out["xq"], out["sx"])
+    inactive = ~ref["active"]
+    yb, yl = to_np(base), to_np(out["y"])
+    assert np.array_equal(yl[inactive], yb[inactive])
+    compare(yb, ref["base"], "base only")
+    # and the call is deterministic
+    again = d.gemm(out["xq"], out["sx"], out["z"], out["ws"])
+    assert torch.equal(again, out["y"])
+    assert ep.epilora_device_error(out["ws"]) == 0
+
+
+def test_bad_index_sets_device_error():
+    lay = custom_layer("bad", 900, 6, 256, 256, 4, 16, [0, 7, -1, -3, 3, 1])
+    d = DeviceGemm(lay.gemms[0])
+    out = d.separate()
+    assert ep.epilora_device_error(out["ws"]) & ep.DEV_BAD_INDEX
+    ref = d.oracle()
+    compare(to_np(out["y"]), ref["y"], "bad index")
+    base = to_np(d.gemm(out["xq"], out["sx"]))
+    assert np.array_equal(to_np(out["y"])[[1, 2, 3]], base[[1, 2, 3]])
+    assert ep.epilora_device_error(out["ws"]) == 0  # cleared by the previous read
+
+
+def test_expand_add_baseline():
+    """The unfused baseline: base GEMM, then the separate expand-add."""
+    rng = np.random.default_rng(7)
+    idx = rng.integers(-1, 5, 40).astype(np.int32)
+    lay = custom_layer("e", 901, 40, 512, 384, 5, 32, idx)
+    d = DeviceGemm(lay.gemms[0])
+    xq, sx = d.quant()
+    z, ws = d.shrink()
+    y = d.gemm(xq, sx)
+    ep.epilora_lora_expand_add(z, d.B, d.idx, d.scale, y, ws)
+    ref = d.oracle()
+    # This path rounds to bf16 twice: the base GEMM's output, then the sum.
+    # Half a bf16 ulp is at most 2^-8 of the value, so
+    # |dY| <= 2^-8 (|base| + |y|) plus the fp32 arithmetic.  Rows without an
+    # adapter are rounded once.
+    yg = bf16_np_to_f64(to_np(y))
+    rms = np.sqrt(np.mean(ref["y"] ** 2))
+    bound = 2.0 ** -8 * (np.abs(ref["base"]) + np.abs(ref["y"])) * 1.001 + 1e-4 * rms
+    assert np.all(np.abs(yg - ref["y"]) <= bound)
+    assert np.abs(yg - ref["y"]).sum() <= 5e-3 * np.abs(ref["y"]).sum()
+    compare(to_np(y)[~ref["active"]], ref["y"][~ref["active"]], "expand baseline, inactive rows")
+
+
+# --- the fused decode path ------------------------------------------------------------------
+
+DECODE_CASES = [
+    (1, 4096, 1024, 1, 64, "zero", False, False, "fp8"),
+    (4, 256, 512, 4, 16, "mixed", True, True, "fp8"),
+    (16, 512, 200, 8, 32, "mixed", False, False, "fp8"),
+    (32, 4096, 512, 64, 64, "distinct", False, False, "fp8"),
+    (64, 1024, 256, 9, 16, "mixed", True, False, "fp8"),
+    (1, 4096, 512, 1, 64, "zero", False, False, "fp4"),
+    (24, 512, 300, 6, 32, "mixed", True, True, "fp4"),
+]
+
+
+@pytest.mark.parametrize("M,K,N,L,r,kind,use_mask,use_ranks,wfmt", DECODE_CASES)
+def test_decode_matches_separate_and_oracle(M, K, N, L, r, kind, use_mask, use_ranks, wfmt):
+    say(f"decode M={M} K={K} N={N} L={L} r={r} {kind} {wfmt}")
+    rng = np.random.default_rng(6000 + M + K + N)
+    idx = _idx(kind, M, L, rng)
+    mask = rng.integers(0, 2, M).astype(np.uint8) if use_mask else None
+    ranks = rng.choice([0, 16, r], size=L).astype(np.int32) if use_ranks else None
+    lay = custom_layer("d", 700 + M + N, M, K, N, L, r, idx, mask=mask, ranks=ranks, wfmt=wfmt)
+    d = DeviceGemm(lay.gemms[0], wfmt)
+    fused = d.decode()
+    sep = d.separate()
+    # the same kernels in one launch: bit-identical to the separate calls
+    assert torch.equal(fused["xq"], sep["xq"]) and torch.equal(fused["sx"], sep["sx"])
+    assert torch.equal(fused["y"], sep["y"])
+    ref = d.oracle()
+    compare(to_np(fused["y"]), ref["y"], "decode")
+    assert ep.epilora_device_error(fused["ws"]) == 0
+    # the workspace is clean again: a second call on it gives the same bits
+    again = d.decode(ws=fused["ws"], keep_xq=False)
+    assert torch.equal(again["y"], fused["y"])
+    assert ep.epilora_device_error(fused["ws"]) == 0
+
+
+def test_decode_base_only():
+    lay = custom_layer("db", 950, 3, 512, 256, 1, 16, [-1, -1, -1])
+    d = DeviceGemm(lay.gemms[0])
+    y = torch.empty(3, 256, dtype=torch.bfloat16, device=DEV)
+    ws = ep.new_workspace(ep.OP_DECODE, 3, 256, 512, 16)
+    ep.epilora_decode_lora(d.x, d.wq, y, sw=d.sw, ws=ws)
+    xq, sx = d.quant()
+    assert torch.equal(y, d.gemm(xq, sx))
