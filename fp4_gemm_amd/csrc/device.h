@@ -151,6 +151,64 @@ __device__ __forceinline__ i32x8 as_i32x8(const uint4& lo, const uint4& hi) {
 }
 
 // ---------------------------------------------------------------------------
+// Buffer loads and stores.  A raw buffer resource returns 0 for any access
+// at or past its byte size, which serves as the bounds check.  Cache policy
+// kCoherent (sc1) makes an access device-coherent: a store writes through to
+// the point of coherence shared by all XCDs and a load reads from it, so
+// data handed between workgroups of one grid needs no L2-wide writeback or
+// invalidate.
+// ---------------------------------------------------------------------------
+constexpr int kCached = 0;
+constexpr int kCoherent = 16;
+constexpr uint32_t kOutOfRange = 0x80000000u;  // an offset past any buffer this library builds
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+template <int POLICY>
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POLICY);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+template <int POLICY>
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, POLICY);
+}
+template <int POLICY>
+__device__ __forceinline__ uint32_t buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, POLICY);
+}
+template <int POLICY>
+__device__ __forceinline__ void buf_store16(__amdgpu_buffer_rsrc_t r, uint32_t off, const uint4& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(u32x4{v.x, v.y, v.z, v.w}, r, off, 0, POLICY);
+}
+template <int POLICY>
+__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t off, const uint2& v) {
+  __builtin_amdgcn_raw_buffer_store_b64(u32x2{v.x, v.y}, r, off, 0, POLICY);
+}
+template <int POLICY>
+__device__ __forceinline__ void buf_store4(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, POLICY);
+}
+
+// Native-vector forms for hot loops (the union-based HIP vector types do not
+// always stay in registers).
+template <int POLICY>
+__device__ __forceinline__ u32x4 bufv_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, POLICY);
+}
+__device__ __forceinline__ i32x8 cat8(const u32x4& lo, const u32x4& hi) {
+  return __builtin_bit_cast(i32x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Wait until every memory access this wave issued has completed.
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+// ---------------------------------------------------------------------------
 // Agent-scope counters and flags (visible across the chip's XCDs)
 // ---------------------------------------------------------------------------
 
@@ -168,6 +226,13 @@ __device__ __forceinline__ void store_relaxed(int* p, int v) {
 }
 __device__ __forceinline__ void atomic_or_relaxed(int* p, int v) {
   __hip_atomic_fetch_or(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int atomic_add_relaxed(int* p, int v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// A device-coherent read of a flag word, without acquire side effects.
+__device__ __forceinline__ int load_relaxed(int* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace epilora

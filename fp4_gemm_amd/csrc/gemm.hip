@@ -1,29 +1,19 @@
 // The low-precision GEMM with the multi-adapter epilogue: a skinny
 // weight-streaming kernel for decode batches (M <= 64) and an LDS-tiled
 // matrix-core kernel for larger batches (prefill).
-#include "gemm_common.h"
+#include "skinny.h"
 
 namespace epilora {
 
 // ---------------------------------------------------------------------------
-// Skinny kernel: see skinny_mainloop / skinny_epilogue.
+// Skinny kernel (M <= 64): persistent workgroups over 16-row tiles; see
+// skinny.h.
 // ---------------------------------------------------------------------------
-template <int MB, int FMT, int U>
-__global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmParams p) {
-  __shared__ __align__(16) float part[4 * MB * 16 * 16];
-  __shared__ uint2 tbl[FMT == EPILORA_W_FP4 ? 256 : 1];
-  __shared__ TokenSlot tok[MB * 16];
-  const int64_t n0 = (int64_t)blockIdx.x * 16;
-  if (FMT == EPILORA_W_FP4) build_fold_table(tbl);
-  for (int t = threadIdx.x; t < MB * 16; t += blockDim.x) {
-    int rk = 0;
-    const int a = p.z != nullptr ? resolve_token(t, p.M, p.ad, p.ctrl + kCtrlError, blockIdx.x == 0, rk) : -1;
-    tok[t] = TokenSlot{a, rk};
-  }
-  __syncthreads();
-  f32x4 acc[MB];
-  skinny_mainloop<MB, FMT, U>(p, n0, acc, tbl);
-  skinny_epilogue<MB, FMT>(p, n0, acc, part, tok, p.z);
+template <int MB, int FMT, int NW, bool XLDS>
+__global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(SkinnyJob J) {
+  extern __shared__ __align__(16) char lds[];
+  Skinny<MB, FMT, NW, XLDS, false> s(J, lds, blockIdx.x);
+  s.run();
 }
 
 // ---------------------------------------------------------------------------
@@ -266,17 +256,35 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(GemmParams p) {
 
 // ---------------------------------------------------------------------------
 
-template <int MB, int FMT, int U>
+template <int MB, int FMT, int NW, bool XLDS>
+static void launch_skinny_x(SkinnyJob& J, hipStream_t stream) {
+  const GemmParams& p = J.g;
+  const size_t lds = skinny_lds(p.M, p.K, MB, NW, p.ad.r, false, XLDS);
+  J.gwgs = skinny_groups(p.N, resident_groups(gemm_skinny_kernel<MB, FMT, NW, XLDS>, NW * 64, lds));
+  hipLaunchKernelGGL((gemm_skinny_kernel<MB, FMT, NW, XLDS>), dim3(J.gwgs), dim3(NW * 64), lds, stream, J);
+}
+
+template <int MB, int FMT, int NW>
+static void launch_skinny_nw(const GemmParams& p, hipStream_t stream) {
+  SkinnyJob J{};
+  J.g = p;
+  J.tiles = (int)cdiv(p.N, 16);
+  if (skinny_x_in_lds(p.M, p.K, MB, NW, p.ad.r, false)) launch_skinny_x<MB, FMT, NW, true>(J, stream);
+  else launch_skinny_x<MB, FMT, NW, false>(J, stream);
+}
+
+template <int MB, int FMT>
 static void launch_skinny(const GemmParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((gemm_skinny_kernel<MB, FMT, U>), dim3((unsigned)cdiv(p.N, 16)), dim3(256), 0, stream, p);
+  if (skinny_waves(p.N, MB) == 8) launch_skinny_nw<MB, FMT, 8>(p, stream);
+  else launch_skinny_nw<MB, FMT, 4>(p, stream);
 }
 
 template <int FMT>
 static void dispatch_gemm(const GemmParams& p, hipStream_t stream) {
-  if (p.M <= 16) launch_skinny<1, FMT, 8>(p, stream);
-  else if (p.M <= 32) launch_skinny<2, FMT, 4>(p, stream);
-  else if (p.M <= 48) launch_skinny<3, FMT, 2>(p, stream);
-  else if (p.M <= 64) launch_skinny<4, FMT, 2>(p, stream);
+  if (p.M <= 16) launch_skinny<1, FMT>(p, stream);
+  else if (p.M <= 32) launch_skinny<2, FMT>(p, stream);
+  else if (p.M <= 48) launch_skinny<3, FMT>(p, stream);
+  else if (p.M <= 64) launch_skinny<4, FMT>(p, stream);
   else {
     const unsigned grid = (unsigned)(cdiv(p.M, kBM) * cdiv(p.N, kBN));
     hipLaunchKernelGGL(gemm_tiled_kernel<FMT>, dim3(grid), dim3(256), 0, stream, p);

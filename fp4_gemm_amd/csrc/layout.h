@@ -19,18 +19,23 @@ constexpr size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 constexpr int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // ---- shrink -----------------------------------------------------------------
-// One workgroup = 4 waves over 16 tokens and a K range made of 128-wide
-// steps; the K range is split over `splits` workgroups whose partial sums are
-// combined in a fixed order by the last one to finish.
+// A workgroup covers 16 consecutive tokens and a range of 128-wide K steps;
+// the K range is split over `splits` workgroups whose partial sums are
+// combined in a fixed order by the last one to finish.  Splits give the chip
+// about 1024 workgroups, but no fewer than one (step, rank block) pair per
+// wave of a 4-wave workgroup.
 constexpr int kShrinkTokens = 16;
 constexpr int kShrinkStep = 128;
 
-inline int shrink_splits(int64_t M, int64_t K) {
+inline int shrink_splits(int64_t M, int64_t K, int32_t r) {
   const int64_t steps = cdiv(K, kShrinkStep);
   const int64_t tiles = cdiv(M, kShrinkTokens);
-  int64_t s = cdiv(steps, 4);              // at most one step per wave
-  const int64_t want = cdiv(1024, tiles);  // enough workgroups to fill the chip
+  const int64_t jb = r > 16 ? r / 16 : 1;
+  int64_t s = steps;
+  const int64_t want = cdiv(1024, tiles);
   if (s > want) s = want;
+  const int64_t fill = cdiv(steps * jb, 4);
+  if (s > fill) s = fill;
   if (s < 1) s = 1;
   return (int)s;
 }
@@ -44,7 +49,7 @@ struct ShrinkWs {
 inline ShrinkWs shrink_ws(size_t base, int64_t M, int64_t K, int32_t r) {
   ShrinkWs w;
   const int64_t tiles = cdiv(M, kShrinkTokens);
-  const int s = shrink_splits(M, K);
+  const int s = shrink_splits(M, K, r);
   w.counters = base;
   w.partials = align256(w.counters + 4 * (size_t)tiles);
   w.total = align256(w.partials + (s > 1 ? (size_t)s * M * r * 4 : 0));

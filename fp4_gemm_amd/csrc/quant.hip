@@ -7,18 +7,22 @@
 
 namespace epilora {
 
+constexpr int kQuantThreads = 256;
+
 __global__ __launch_bounds__(kQuantThreads) void quant_rows_kernel(
-    const uint16_t* __restrict__ x, int64_t K, int64_t ldx, uint8_t* __restrict__ xq,
+    const uint16_t* __restrict__ x, int64_t M, int64_t K, int64_t ldx, uint8_t* __restrict__ xq,
     int64_t ldq, float* __restrict__ scale_out) {
   __shared__ uint32_t red[kQuantThreads / kWave];
   const int64_t row = blockIdx.x;
-  quant_row(x + row * ldx, K, xq + row * ldq, scale_out + row, red);
+  const auto qr = make_rsrc(xq + row * ldq, (uint32_t)K);
+  const auto sr = make_rsrc(scale_out + row, 4u);
+  quant_row<kQuantThreads, kCached>(x + row * ldx, K, qr, 0u, sr, 0u, red);
 }
 
 hipError_t launch_quant_rows(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, uint8_t* xq,
                              int64_t ldq, float* scale, hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)M), dim3(kQuantThreads), 0, stream, x, K, ldx,
+  hipLaunchKernelGGL(quant_rows_kernel, dim3((unsigned)M), dim3(kQuantThreads), 0, stream, x, M, K, ldx,
                      xq, ldq, scale);
   return hipGetLastError();
 }
@@ -40,7 +44,7 @@ __global__ __launch_bounds__(256) void amax_kernel(const uint16_t* __restrict__ 
   const uint4* src = reinterpret_cast<const uint4*>(w);
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n_vec; i += (int64_t)gridDim.x * blockDim.x)
     m = max(m, absmax8(src[i]));
-  m = block_max_u32(m, red);
+  m = block_max_u32<256>(m, red);
   if (threadIdx.x == 0) atomicMax(amax_out, m);
 }
 

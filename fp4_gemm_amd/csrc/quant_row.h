@@ -7,16 +7,15 @@
 namespace epilora {
 
 // ---------------------------------------------------------------------------
-// Per-row dynamic E4M3.  One 256-thread workgroup per row.  Each thread holds
-// up to kRegVecs 16-byte vectors (8 bf16 each) of the row in registers, so a
-// row of up to 32768 elements is read from HBM once; longer rows are read a
-// second time for the encode pass.
+// Per-row dynamic E4M3.  One workgroup of NT threads per row.  Each thread
+// holds up to kRegVecs 16-byte vectors (8 bf16 each) of the row in registers,
+// so a row of up to 128 * NT elements is read from HBM once; longer rows are
+// read a second time for the encode pass.
 // amax: the largest |x| is the largest 15-bit bf16 magnitude, an integer max.
 // scale: amax / 448, an IEEE division (built with correctly rounded fp32
 // division); 1.0 for an all-zero row.  code: E4M3(x / scale), one IEEE
 // division per element.
 // ---------------------------------------------------------------------------
-constexpr int kQuantThreads = 256;
 constexpr int kRegVecs = 16;
 
 __device__ __forceinline__ uint32_t absmax8(const uint4& v) {
@@ -45,7 +44,8 @@ __device__ __forceinline__ uint2 encode8(const uint4& v, float s) {
   return make_uint2(out[0], out[1]);
 }
 
-// Block-wide max of a uint32 over 256 threads.
+// Block-wide max of a uint32 over NT threads (`red`: NT / 64 words of LDS).
+template <int NT>
 __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
   v = wave_max_u32(v);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -53,7 +53,7 @@ __device__ __forceinline__ uint32_t block_max_u32(uint32_t v, uint32_t* red) {
   __syncthreads();
   uint32_t m = red[0];
 #pragma unroll
-  for (int i = 1; i < kQuantThreads / kWave; ++i) m = m > red[i] ? m : red[i];
+  for (int i = 1; i < NT / kWave; ++i) m = m > red[i] ? m : red[i];
   return m;
 }
 
@@ -62,12 +62,15 @@ __device__ __forceinline__ float row_scale(uint32_t amax_bits) {
   return amax == 0.0f ? 1.0f : amax / 448.0f;
 }
 
-// Quantize one row of bf16 values into E4M3 codes and its scale, with the
-// 256 threads of the calling workgroup.  `red` is 4 words of LDS.
-__device__ __forceinline__ void quant_row(const uint16_t* __restrict__ xrow, int64_t K, uint8_t* __restrict__ qrow,
-                                          float* __restrict__ scale_out, uint32_t* red) {
+// Quantize one row of K bf16 values into E4M3 codes (to byte offset `qoff`
+// of buffer `qr`) and its scale (to byte offset `soff` of buffer `sr`), with
+// the NT threads of the calling workgroup; stores use cache policy POLICY.
+// `red` is NT / 64 words of LDS.  Each thread keeps up to kRegVecs 16-byte
+// vectors of the row in registers; a longer row is read twice.
+template <int NT, int POLICY>
+__device__ __forceinline__ void quant_row(const uint16_t* __restrict__ xrow, int64_t K, __amdgpu_buffer_rsrc_t qr,
+                                          uint32_t qoff, __amdgpu_buffer_rsrc_t sr, uint32_t soff, uint32_t* red) {
   const uint4* src = reinterpret_cast<const uint4*>(xrow);
-  uint2* dst = reinterpret_cast<uint2*>(qrow);
   const int nv = (int)(K / 8);
   const int tid = threadIdx.x;
 
@@ -75,22 +78,22 @@ __device__ __forceinline__ void quant_row(const uint16_t* __restrict__ xrow, int
   uint32_t amax = 0;
 #pragma unroll
   for (int i = 0; i < kRegVecs; ++i) {
-    const int j = tid + i * kQuantThreads;
+    const int j = tid + i * NT;
     if (j < nv) {
       v[i] = src[j];
       amax = max(amax, absmax8(v[i]));
     }
   }
-  for (int j = tid + kRegVecs * kQuantThreads; j < nv; j += kQuantThreads) amax = max(amax, absmax8(src[j]));
-  amax = block_max_u32(amax, red);
+  for (int j = tid + kRegVecs * NT; j < nv; j += NT) amax = max(amax, absmax8(src[j]));
+  amax = block_max_u32<NT>(amax, red);
   const float s = row_scale(amax);
-  if (tid == 0) *scale_out = s;
+  if (tid == 0) buf_store4<POLICY>(sr, soff, __float_as_uint(s));
 #pragma unroll
   for (int i = 0; i < kRegVecs; ++i) {
-    const int j = tid + i * kQuantThreads;
-    if (j < nv) dst[j] = encode8(v[i], s);
+    const int j = tid + i * NT;
+    if (j < nv) buf_store8<POLICY>(qr, qoff + 8 * j, encode8(v[i], s));
   }
-  for (int j = tid + kRegVecs * kQuantThreads; j < nv; j += kQuantThreads) dst[j] = encode8(src[j], s);
+  for (int j = tid + kRegVecs * NT; j < nv; j += NT) buf_store8<POLICY>(qr, qoff + 8 * j, encode8(src[j], s));
 }
 
 }  // namespace epilora

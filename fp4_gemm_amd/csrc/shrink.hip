@@ -4,12 +4,14 @@
 
 namespace epilora {
 
+constexpr int kShrinkThreads = 256;
+
 __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) {
   extern __shared__ float red[];  // [4 waves][16 tokens][r]
   int s_begin, s_end;
   shrink_range(p, blockIdx.y, s_begin, s_end);
-  shrink_tile(p, (int64_t)blockIdx.x * kShrinkTokens, s_begin, s_end, red, blockIdx.y == 0);
-  shrink_finish(p, blockIdx.x, blockIdx.y, red);
+  shrink_tile<4>(p, (int64_t)blockIdx.x * kShrinkTokens, s_begin, s_end, red, blockIdx.y == 0);
+  shrink_finish<4>(p, blockIdx.x, blockIdx.y, red);
 }
 
 hipError_t launch_shrink(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const AdapterArgs& ad,
@@ -21,9 +23,9 @@ hipError_t launch_shrink(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, c
   p.ctrl = reinterpret_cast<int*>(ws);
   p.counters = reinterpret_cast<int*>(reinterpret_cast<char*>(ws) + lay.counters);
   p.partials = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + lay.partials);
-  p.splits = shrink_splits(M, K);
+  p.splits = shrink_splits(M, K, ad.r);
   const dim3 grid((unsigned)cdiv(M, kShrinkTokens), (unsigned)p.splits);
-  const size_t lds = (size_t)4 * 16 * ad.r * sizeof(float);
+  const size_t lds = (size_t)kShrinkWaves * 16 * ad.r * sizeof(float);
   hipLaunchKernelGGL(shrink_kernel, grid, dim3(kShrinkThreads), lds, stream, p);
   return hipGetLastError();
 }

@@ -7,23 +7,29 @@
 
 namespace epilora {
 
-constexpr int kShrinkThreads = 256;
 constexpr int kMaxJB = 8;  // r <= 128 -> at most 8 blocks of 16 rank rows
+// The shrink's work is laid out over this many waves whatever the block size
+// (further waves of a larger block idle), so its sums round the same way in
+// the shrink kernel and in the fused decode kernel.
+constexpr int kShrinkWaves = 4;
 
 // ---------------------------------------------------------------------------
-// Shrink.  Workgroup (tile, split): 16 consecutive tokens and a range of
-// 128-wide K steps; its 4 waves take every 4th step.  For each adapter that
-// some token of the tile uses, a wave multiplies that adapter's A rows (16 at
-// a time, the matrix-core rows) by the bf16 activations of the tokens using
-// it (the other token columns are zero), on bf16 MFMA with fp32
-// accumulation.  Columns of different adapters are disjoint, so one set of
-// accumulators serves every adapter.  Lane l holds rank row (l % 16) of A and
-// token column (l % 16) of x, and elements [32 (l / 16), +32) of each
-// 128-wide step, 8 per MFMA: A and x use the same K positions, so each MFMA
-// pairs matching elements.
-// The 4 waves are summed in LDS in wave order; splits write fp32 partials
-// and the last workgroup of a tile (an agent-scope counter) adds them in
-// split order, so the result does not depend on timing.
+// Shrink tile.  A workgroup owns 16 consecutive tokens and a range of
+// 128-wide K steps.  For each adapter that some token of the tile uses, the
+// adapter's A rows (16 at a time, the matrix-core rows) multiply the bf16
+// activations of the tokens using it (the other token columns are zero), on
+// bf16 MFMA with fp32 accumulation; columns of different adapters are
+// disjoint, so one set of accumulators serves every adapter.  Lane l holds
+// rank row (l % 16) of A and token column (l % 16) of x, elements
+// [32 (l / 16), +32) of each step, 8 per MFMA: both operands see the same K
+// positions, so each MFMA pairs matching elements.
+// The waves form a WJ x WS grid: wave w takes the rank blocks jb with
+// jb % WJ == w % WJ and every WS-th step from w / WJ, so a small rank still
+// keeps every wave busy.  The waves are summed in LDS in wave order; split
+// workgroups publish fp32 partials with device-coherent stores, and the
+// last one of a tile (an agent-scope counter) adds them in a fixed order
+// (consecutive splits in chunks, then the chunks), so the result does not
+// depend on timing.
 // ---------------------------------------------------------------------------
 struct ShrinkParams {
   const uint16_t* x;
@@ -38,14 +44,21 @@ struct ShrinkParams {
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
-// One workgroup's contribution to z for 16 tokens; sums the waves and
-// leaves the [16][r] result in `out` (LDS).
-__device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int64_t t0, int s_begin, int s_end,
-                                            float* red, bool report) {
+// One workgroup's sums for 16 tokens over its K steps; leaves the [16][r]
+// result in `red` (LDS of kShrinkWaves * 16 * r floats).  Every thread of the
+// block must call it.
+template <int NW>
+__device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int64_t t0, int s_begin, int s_end, float* red,
+                                            bool report) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int r = p.ad.r;
   const int64_t K = p.K;
+  const int JB = r >> 4;
+  const int WJ = JB < kShrinkWaves ? JB : kShrinkWaves;
+  const int WS = kShrinkWaves / WJ;
+  const int wj = wave % WJ, ws = wave / WJ;
+  const bool working = wave < kShrinkWaves;
   int rank_c;
   const int a_c = resolve_token(t0 + col, p.M, p.ad, p.ctrl + kCtrlError, report && lane < 16 && wave == 0, rank_c);
 
@@ -53,7 +66,7 @@ __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int64_t t0, i
 #pragma unroll
   for (int j = 0; j < kMaxJB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint64_t pending = __ballot(lane < 16 && a_c >= 0);
+  uint64_t pending = working ? __ballot(lane < 16 && a_c >= 0) : 0;
   while (pending) {
     const int leader = __ffsll((unsigned long long)pending) - 1;
     const int a = __shfl(a_c, leader);
@@ -64,7 +77,7 @@ __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int64_t t0, i
     const int jbn = (rank + 15) >> 4;
     const uint16_t* Aa = p.ad.A + (int64_t)a * r * K;
     const uint16_t* xr = p.x + (t0 + col) * p.ldx;
-    for (int s = s_begin + wave; s < s_end; s += 4) {
+    for (int s = s_begin + ws; s < s_end; s += WS) {
       const int64_t k = (int64_t)s * kShrinkStep + grp * 32;
       uint4 xv[4];
 #pragma unroll
@@ -72,7 +85,7 @@ __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int64_t t0, i
         xv[i] = (member && k + i * 8 < K) ? ld16(xr + k + i * 8) : make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int jb = 0; jb < kMaxJB; ++jb) {
-        if (jb < jbn) {
+        if (jb < jbn && jb % WJ == wj) {
           const int j = jb * 16 + col;
           const bool rowok = j < rank;
           const uint16_t* ar = Aa + (int64_t)j * K + k;
@@ -87,56 +100,91 @@ __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int64_t t0, i
     }
   }
 
-  // acc[jb][v] = z[token col][jb*16 + 4*grp + v]; sum the 4 waves in order.
-  const int jbr = r >> 4;
+  // acc[jb][v] = z[token col][jb*16 + 4*grp + v]; sum the waves in order.
+  if (working) {
 #pragma unroll
-  for (int jb = 0; jb < kMaxJB; ++jb)
-    if (jb < jbr)
-      *reinterpret_cast<float4*>(&red[(wave * 16 + col) * r + jb * 16 + 4 * grp]) =
-          make_float4(acc[jb][0], acc[jb][1], acc[jb][2], acc[jb][3]);
+    for (int jb = 0; jb < kMaxJB; ++jb)
+      if (jb < JB)
+        *reinterpret_cast<float4*>(&red[(wave * 16 + col) * r + jb * 16 + 4 * grp]) =
+            make_float4(acc[jb][0], acc[jb][1], acc[jb][2], acc[jb][3]);
+  }
   __syncthreads();
-  for (int e = threadIdx.x; e < 16 * r; e += kShrinkThreads) {
+  for (int e = threadIdx.x; e < 16 * r; e += NW * kWave) {
     float v = red[e];
-    v += red[16 * r + e];
-    v += red[32 * r + e];
-    v += red[48 * r + e];
+#pragma unroll
+    for (int w = 1; w < kShrinkWaves; ++w) v += red[w * 16 * r + e];
     red[e] = v;
   }
   __syncthreads();
 }
 
 // Write this workgroup's [16][r] sums (in LDS `red`) to z, or to its split's
-// partial; the last split of a tile adds the partials in split order.
-// Returns true in the workgroup that wrote the tile's final z.
-__device__ __forceinline__ bool shrink_finish(const ShrinkParams& p, int tile, int split, const float* red) {
+// partial; the last split of a tile adds the partials in a fixed order.  z and
+// the partials are written and read device-coherently, so another workgroup
+// of the same grid may read z once the caller has published it.  Returns
+// true in the workgroup that wrote the tile's final z, after every one of
+// its z stores has completed.
+template <int NW>
+__device__ __forceinline__ bool shrink_finish(const ShrinkParams& p, int tile, int split, float* red) {
   __shared__ int last;
   const int64_t t0 = (int64_t)tile * kShrinkTokens;
   const int r = p.ad.r;
+  const int64_t rows = p.M - t0 < 16 ? p.M - t0 : 16;
+  const uint32_t tile_bytes = (uint32_t)(rows * r * 4);
+  const auto zr = make_rsrc(p.z + t0 * r, tile_bytes);
   if (p.splits == 1) {
-    for (int e = threadIdx.x; e < 16 * r; e += kShrinkThreads) {
-      const int64_t t = t0 + e / r;
-      if (t < p.M) p.z[t * r + e % r] = red[e];
-    }
+    for (int e = 4 * threadIdx.x; e < rows * r; e += 4 * NW * kWave)
+      buf_store16<kCoherent>(zr, 4 * e, *reinterpret_cast<const uint4*>(&red[e]));
+    wait_all_memory();
+    __syncthreads();
     return true;
   }
-  for (int e = threadIdx.x; e < 16 * r; e += kShrinkThreads) {
-    const int64_t t = t0 + e / r;
-    if (t < p.M) p.partials[((int64_t)split * p.M + t) * r + e % r] = red[e];
-  }
-  __threadfence();
+  const auto pr = make_rsrc(p.partials + ((int64_t)split * p.M + t0) * r, tile_bytes);
+  for (int e = 4 * threadIdx.x; e < rows * r; e += 4 * NW * kWave)
+    buf_store16<kCoherent>(pr, 4 * e, *reinterpret_cast<const uint4*>(&red[e]));
+  wait_all_memory();
   __syncthreads();
-  if (threadIdx.x == 0) last = atomic_add_acq_rel(&p.counters[tile], 1) == p.splits - 1;
+  if (threadIdx.x == 0) last = atomic_add_relaxed(&p.counters[tile], 1) == p.splits - 1;
   __syncthreads();
   if (!last) return false;
-  __threadfence();
-  for (int e = threadIdx.x; e < 16 * r; e += kShrinkThreads) {
-    const int64_t t = t0 + e / r;
-    if (t >= p.M) continue;
-    float v = 0.f;
-    for (int s = 0; s < p.splits; ++s) v += p.partials[((int64_t)s * p.M + t) * r + e % r];
-    p.z[t * r + e % r] = v;
+  // Combine: the quads (4 floats) of the tile times chunks of consecutive
+  // splits are spread over the workgroup; each chunk is summed in split
+  // order, then the chunk sums in chunk order, so the rounding is the same on
+  // every run.  `red` is free again and holds the chunk sums.
+  float* sums = red;
+  const int quads = (int)(rows * r / 4);
+  const int threads = kShrinkWaves * kWave;  // the chunking, not the block size
+  int chunks = threads / quads;
+  if (chunks < 1) chunks = 1;
+  if (chunks > p.splits) chunks = p.splits;
+  const int per = (p.splits + chunks - 1) / chunks;
+  for (int item = threadIdx.x; item < quads * chunks; item += NW * kWave) {
+    const int q = item % quads, c = item / quads;
+    const int s0 = c * per, s1 = min(p.splits, s0 + per);
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = s0; s < s1; ++s) {
+      const auto ps = make_rsrc(p.partials + ((int64_t)s * p.M + t0) * r, tile_bytes);
+      const uint4 u = buf_load16<kCoherent>(ps, 16u * q);
+      v.x += __uint_as_float(u.x);
+      v.y += __uint_as_float(u.y);
+      v.z += __uint_as_float(u.z);
+      v.w += __uint_as_float(u.w);
+    }
+    *reinterpret_cast<float4*>(&sums[4 * item]) = v;
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < quads; q += NW * kWave) {
+    float4 v = *reinterpret_cast<const float4*>(&sums[4 * q]);
+    for (int c = 1; c < chunks; ++c) {
+      const float4 w = *reinterpret_cast<const float4*>(&sums[4 * (c * quads + q)]);
+      v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+    }
+    buf_store16<kCoherent>(zr, 16u * q, make_uint4(__float_as_uint(v.x), __float_as_uint(v.y),
+                                                   __float_as_uint(v.z), __float_as_uint(v.w)));
   }
   if (threadIdx.x == 0) store_relaxed(&p.counters[tile], 0);
+  wait_all_memory();
+  __syncthreads();
   return true;
 }
 
@@ -144,7 +192,7 @@ __device__ __forceinline__ bool shrink_finish(const ShrinkParams& p, int tile, i
 __device__ __forceinline__ void shrink_range(const ShrinkParams& p, int split, int& s_begin, int& s_end) {
   const int steps = (int)cdiv(p.K, kShrinkStep);
   const int spw = (int)cdiv(steps, p.splits);
-  s_begin = split * spw;
+  s_begin = min(steps, split * spw);
   s_end = min(steps, s_begin + spw);
 }
 

@@ -1,0 +1,493 @@
+// The weight-streaming GEMM for small batches (M <= 64 tokens), shared by
+// the skinny GEMM kernel and the fused decode kernel.
+//
+// Persistent workgroups: workgroup g of G owns the 16-row tiles g, g + G,
+// g + 2G, ... of the output and streams them back to back.  Its NW waves
+// split the 128-wide K steps of every tile into NW contiguous ranges.  The
+// product is taken swap-AB: the weight rows are the 16-row operand of
+// v_mfma_f32_16x16x128_f8f6f4 and the tokens (up to MB blocks of 16) its
+// 16-column operand, so C[n][t] sits in lane (t % 16) + 16 * ((n % 16) / 4),
+// register n % 4.  Lane l takes 32 consecutive bytes of weight row l % 16 and
+// of token row l % 16 at the same K offset 32 * (l / 16): both operands see
+// the same K positions, so each MFMA pairs matching elements.
+//
+// Weights stream in batches of U steps through buffer resources
+// (out-of-range offsets read as zero) with two batches in flight, across tile
+// boundaries: the next tile's first batch is on its way while the current
+// tile's epilogue runs.  Small quantized activations (M * K <= 32 KB) sit in
+// LDS for the whole kernel; larger ones are loaded with the weights.
+//
+// A tile's epilogue sums the NW partial accumulators in wave order through
+// LDS, applies the scales, and adds the adapter term of each active token:
+// an fp32 dot over the rank, 16 lanes per output (lane j takes a contiguous
+// r / 16 slice of the rank) reduced by shuffles; the first pass of B slices
+// for a tile is requested during the previous tile.  In the fused decode
+// kernel z may not be ready when a tile finishes: the tile's reduced base
+// results then wait in an LDS stash and their epilogues run once z is
+// published, so the weight stream does not wait for the shrink.
+#pragma once
+
+#include "gemm_common.h"
+#include "occupancy.h"
+#include "quant_row.h"
+
+namespace epilora {
+
+constexpr int kXInLdsMax = 32768;  // bytes of quantized activations kept in LDS
+constexpr int kSelfQuantMaxM = 4;  // the fused kernel quantizes up to this many rows itself
+constexpr uint32_t kLdsBudget = 65536;
+
+// Tiles whose epilogue may wait for z in the fused kernel.
+template <int MB>
+struct StashCfg {
+  static constexpr int n = MB == 1 ? 8 : (MB == 2 ? 4 : 2);
+};
+
+template <int MB>
+struct SkinnyCfg {
+  static constexpr int U = MB == 1 ? 4 : (MB == 2 ? 2 : 1);  // steps per load batch
+  static constexpr int T = MB * 16;                            // token slots
+};
+
+__host__ __device__ inline uint32_t align16(uint32_t v) { return (v + 15u) & ~15u; }
+
+// LDS layout of a skinny workgroup (byte offsets); host and device agree.
+struct SkLayout {
+  uint32_t part, red, tbl, tok, sx, zs, xs, stash, stash_n0, total;
+};
+
+__host__ __device__ inline SkLayout sk_layout(int MB, int NW, int r, uint32_t xbytes, int nstash) {
+  const uint32_t T = MB * 16;
+  SkLayout L;
+  L.part = 0;                                            // float [NW][T][16]
+  L.red = align16(L.part + NW * T * 16 * 4);             // float [T][16]
+  L.tbl = align16(L.red + T * 16 * 4);                   // uint2 [256]
+  L.tok = align16(L.tbl + 256 * 8);                      // TokenSlot [T]
+  L.sx = align16(L.tok + T * 8);                         // float [T]
+  L.zs = align16(L.sx + T * 4);                          // float [T][r]
+  L.xs = align16(L.zs + T * r * 4);                      // uint8 [M][K]
+  L.stash = align16(L.xs + xbytes);                      // float [nstash][T][16]
+  L.stash_n0 = align16(L.stash + nstash * T * 16 * 4);   // int64 [nstash]
+  L.total = align16(L.stash_n0 + nstash * 8 + 16);       // + one flag word
+  return L;
+}
+
+// What a persistent skinny grid does.
+struct SkinnyJob {
+  GemmParams g;
+  int tiles;            // cdiv(N, 16)
+  int gwgs;             // persistent workgroups G (<= tiles)
+  const uint16_t* x;    // fused: the bf16 activations (self-quantized when kept in LDS)
+  int64_t ldx;
+  int* qflag;           // fused, activations not in LDS: rows quantized
+  int qtarget;
+  int* zflag;           // fused with adapters: z published
+  int ztarget;
+  int64_t wait_ticks;
+};
+
+template <int MB, int U>
+struct SkinnyBatch {
+  u32x4 wa[U], wb[U];        // FP8: 32 bytes; 4-bit: wa = 32 codes, wb.x = two block scales
+  u32x4 xa[U][MB], xb[U][MB];
+};
+
+// Thread 0 polls *flag (device-coherent loads, s_sleep between them) until it
+// reaches target, the wall-clock limit passes, or another workgroup has
+// already timed out; the verdict is broadcast through LDS.
+__device__ __forceinline__ bool wait_flag(int* flag, int target, int64_t ticks, int* err, int* verdict) {
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    if (load_relaxed(flag) < target) {
+      const int64_t start = wall_clock64();
+      while (load_relaxed(flag) < target) {
+        if (wall_clock64() - start > ticks || (load_relaxed(err) & EPILORA_DEV_WAIT_TIMEOUT)) {
+          ok = 0;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(8);
+      }
+    }
+    *verdict = ok;
+  }
+  __syncthreads();
+  return *verdict != 0;
+}
+
+// Quantize one row into LDS (codes and scale) with the NT threads of the
+// workgroup: the same arithmetic as quant_row, so the same bits.
+template <int NT>
+__device__ __forceinline__ void quant_row_lds(const uint16_t* __restrict__ xrow, int64_t K, uint8_t* qs, float* sxs,
+                                              uint32_t* red) {
+  const uint4* src = reinterpret_cast<const uint4*>(xrow);
+  const int nv = (int)(K / 8);
+  uint32_t amax = 0;
+  for (int j = threadIdx.x; j < nv; j += NT) amax = max(amax, absmax8(src[j]));
+  amax = block_max_u32<NT>(amax, red);
+  const float s = row_scale(amax);
+  if (threadIdx.x == 0) *sxs = s;
+  for (int j = threadIdx.x; j < nv; j += NT) *reinterpret_cast<uint2*>(qs + 8 * j) = encode8(src[j], s);
+  __syncthreads();
+}
+
+template <int MB, int FMT, int NW, bool XLDS, bool FUSED>
+struct Skinny {
+  static constexpr int U = SkinnyCfg<MB>::U;
+  static constexpr int T = MB * 16;
+  static constexpr int XPOL = FUSED ? kCoherent : kCached;
+
+  const SkinnyJob& J;
+  const GemmParams& p;
+  SkLayout L;
+  float *part, *red, *sxs, *zs, *stash;
+  int64_t* stash_n0;
+  uint2* tbl;
+  TokenSlot* tok;
+  uint8_t* xs;
+  int* verdict;
+  int g, lane, wave, row;
+  int sb, se, nb, total;
+  uint32_t kofs, xbase[MB];
+  __amdgpu_buffer_rsrc_t xr;
+  bool adapters;
+
+  __device__ __forceinline__ Skinny(const SkinnyJob& j, char* lds, int gidx) : J(j), p(j.g), g(gidx) {
+    const int64_t M = p.M, K = p.K;
+    L = sk_layout(MB, NW, p.ad.r, XLDS ? (uint32_t)(M * K) : 0u, FUSED ? StashCfg<MB>::n : 0);
+    part = reinterpret_cast<float*>(lds + L.part);
+    red = reinterpret_cast<float*>(lds + L.red);
+    tbl = reinterpret_cast<uint2*>(lds + L.tbl);
+    tok = reinterpret_cast<TokenSlot*>(lds + L.tok);
+    sxs = reinterpret_cast<float*>(lds + L.sx);
+    zs = reinterpret_cast<float*>(lds + L.zs);
+    xs = reinterpret_cast<uint8_t*>(lds + L.xs);
+    stash = reinterpret_cast<float*>(lds + L.stash);
+    stash_n0 = reinterpret_cast<int64_t*>(lds + L.stash_n0);
+    verdict = reinterpret_cast<int*>(lds + L.total - 16);
+    lane = threadIdx.x & 63;
+    wave = threadIdx.x >> 6;
+    row = lane & 15;
+    kofs = (uint32_t)(lane >> 4) * 32;
+    const int steps = (int)cdiv(K, 128);
+    const int spw = (int)cdiv(steps, NW);
+    sb = min(steps, wave * spw);
+    se = min(steps, sb + spw);
+    nb = (int)cdiv(spw, U);
+    const int mine = (int)cdiv(J.tiles - g, J.gwgs);
+    total = mine * nb;
+    adapters = p.z != nullptr;
+    xr = make_rsrc(p.xq, (uint32_t)((M - 1) * p.ldq + K));
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int64_t t = mb * 16 + row;
+      xbase[mb] = t < M ? (uint32_t)(t * (XLDS ? K : p.ldq)) : kOutOfRange;
+    }
+  }
+
+  __device__ __forceinline__ int64_t n0_of(int j) const { return (int64_t)(g + (j / nb) * J.gwgs) * 16; }
+
+  // ---- loads ----------------------------------------------------------------
+  __device__ __forceinline__ void load_w(SkinnyBatch<MB, U>& b, int j) const {
+    const bool live = j < total;
+    const int64_t K = p.K;
+    const int64_t n0 = live ? n0_of(j) : 0;
+    const int64_t rows = live ? (p.N - n0 < 16 ? p.N - n0 : 16) : 0;
+    const int64_t wrow = FMT == EPILORA_W_FP8 ? K : K / 2;
+    const auto wr = make_rsrc(p.wt.w + n0 * wrow, (uint32_t)(rows * wrow));
+    const auto sr = make_rsrc(FMT == EPILORA_W_FP4 ? p.wt.bs + n0 * (K / 16) : p.wt.w,
+                              FMT == EPILORA_W_FP4 ? (uint32_t)(rows * (K / 16)) : 0u);
+    const uint32_t wbase = row < rows ? (uint32_t)(row * wrow) : kOutOfRange;
+    const uint32_t sbase = row < rows ? (uint32_t)(row * (K / 16)) : kOutOfRange;
+    const int s0 = sb + (live ? j % nb : 0) * U;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t k = (uint32_t)(s0 + u) * 128u + kofs;
+      const bool ok = s0 + u < se && (int64_t)k < K;
+      if (FMT == EPILORA_W_FP8) {
+        const uint32_t off = ok ? wbase + k : kOutOfRange;
+        b.wa[u] = bufv_load16<kCached>(wr, off);
+        b.wb[u] = bufv_load16<kCached>(wr, off + 16);
+      } else {
+        b.wa[u] = bufv_load16<kCached>(wr, ok ? wbase + k / 2 : kOutOfRange);
+        b.wb[u] = u32x4{buf_load2<kCached>(sr, ok ? sbase + k / 16 : kOutOfRange), 0u, 0u, 0u};
+      }
+    }
+  }
+
+  __device__ __forceinline__ void load_x(SkinnyBatch<MB, U>& b, int j) const {
+    if (XLDS) return;
+    const int s0 = sb + (j < total ? j % nb : 0) * U;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t k = (uint32_t)(s0 + u) * 128u + kofs;
+      const bool ok = j < total && s0 + u < se && (int64_t)k < p.K;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const uint32_t off = ok ? xbase[mb] + k : kOutOfRange;
+        b.xa[u][mb] = bufv_load16<XPOL>(xr, off);
+        b.xb[u][mb] = bufv_load16<XPOL>(xr, off + 16);
+      }
+    }
+  }
+
+  // ---- multiply a batch (steps past the range were loaded as zeros) ---------
+  __device__ __forceinline__ void compute(const SkinnyBatch<MB, U>& b, int j, f32x4 (&acc)[MB]) const {
+    const int s0 = sb + (j < total ? j % nb : 0) * U;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      i32x8 wf;
+      if (FMT == EPILORA_W_FP8) {
+        wf = cat8(b.wa[u], b.wb[u]);
+      } else {
+        const uint32_t sc = b.wb[u].x;
+        const uint2 t0 = tbl[sc & 0xFFu], t1 = tbl[(sc >> 8) & 0xFFu];
+        uint32_t o[8];
+        fold8(b.wa[u].x, t0.x, t0.y, o[0], o[1]);
+        fold8(b.wa[u].y, t0.x, t0.y, o[2], o[3]);
+        fold8(b.wa[u].z, t1.x, t1.y, o[4], o[5]);
+        fold8(b.wa[u].w, t1.x, t1.y, o[6], o[7]);
+        wf = i32x8{(int)o[0], (int)o[1], (int)o[2], (int)o[3], (int)o[4], (int)o[5], (int)o[6], (int)o[7]};
+      }
+      const uint32_t k = (uint32_t)(s0 + u) * 128u + kofs;
+      const bool kin = s0 + u < se && (int64_t)k < p.K;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        i32x8 xf;
+        if (XLDS) {
+          const bool ok = kin && xbase[mb] != kOutOfRange;
+          const u32x4* q = reinterpret_cast<const u32x4*>(xs + (ok ? xbase[mb] + k : 0u));
+          const u32x4 zero = {0u, 0u, 0u, 0u};
+          const u32x4 q0 = q[0], q1 = q[1];
+          xf = cat8(ok ? q0 : zero, ok ? q1 : zero);
+        } else {
+          xf = cat8(b.xa[u][mb], b.xb[u][mb]);
+        }
+        acc[mb] = mfma_fp8_16x16x128(wf, xf, acc[mb]);
+      }
+    }
+  }
+
+  // ---- epilogue pieces --------------------------------------------------------
+  __device__ __forceinline__ void resolve_tokens(bool report) const {
+    for (int t = threadIdx.x; t < T; t += blockDim.x) {
+      int rk = 0;
+      const int a = adapters ? resolve_token(t, p.M, p.ad, p.ctrl + kCtrlError, report, rk) : -1;
+      tok[t] = TokenSlot{a, rk};
+    }
+  }
+
+  // The r / 16 bf16 values of B[a][n][jl * r / 16 ...] this lane needs for
+  // output o of the tile at n0 (zero past the rank or without an adapter).
+  __device__ __forceinline__ uint4 b_chunk(int64_t n0, int o) const {
+    uint4 v = zero4();
+    if (!adapters) return v;
+    const int jl = threadIdx.x & 15;
+    const int t = o >> 4;
+    const int64_t n = n0 + (o & 15);
+    if (t >= p.M || n >= p.N) return v;
+    const TokenSlot ts = tok[t];
+    if (ts.a < 0) return v;
+    const int r = p.ad.r;
+    const int ch = r >> 4;
+    const int j0 = jl * ch;
+    if (j0 >= ts.rank) return v;
+    const uint16_t* src = p.ad.B + ((int64_t)ts.a * p.N + n) * r + j0;
+    if (ch == 8) v = *reinterpret_cast<const uint4*>(src);
+    else if (ch == 4) { const uint2 w = *reinterpret_cast<const uint2*>(src); v.x = w.x; v.y = w.y; }
+    else if (ch == 2) v.x = *reinterpret_cast<const uint32_t*>(src);
+    else v.x = *src;
+    if (j0 + ch > ts.rank) {  // clear the elements past the rank
+      uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        if (e < ch && j0 + e >= ts.rank) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+      v = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+    return v;
+  }
+
+  // Outputs of the tile at n0 from its reduced accumulators `base` ([T][16]).
+  // `pre` holds this thread's first-pass B slice when have_pre.
+  __device__ __forceinline__ void outputs(int64_t n0, const float* base, bool have_pre, const uint4& pre) const {
+    const int jl = threadIdx.x & 15;
+    const int r = p.ad.r;
+    const int ch = r >> 4;
+    for (int o = threadIdx.x >> 4; o < p.M * 16; o += NW * 4) {
+      const int t = o >> 4;
+      const int64_t n = n0 + (o & 15);
+      float l = 0.f;
+      const bool lora = adapters && tok[t].a >= 0;
+      if (lora) {
+        const uint4 bv = (have_pre && o == (int)(threadIdx.x >> 4)) ? pre : b_chunk(n0, o);
+        const uint32_t w[4] = {bv.x, bv.y, bv.z, bv.w};
+        const float* zt = zs + t * r + jl * ch;
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (e < ch) l = fmaf((e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]), zt[e], l);
+      }
+      l += __shfl_xor(l, 8, 16);
+      l += __shfl_xor(l, 4, 16);
+      l += __shfl_xor(l, 2, 16);
+      l += __shfl_xor(l, 1, 16);
+      if (jl == 0 && n < p.N) {
+        float y = (base[o] * sxs[t]) * weight_scale<FMT>(p.wt, n);
+        if (lora) y = y + p.ad.scale * l;
+        p.y[(int64_t)t * p.ldy + n] = (uint16_t)f32_to_bf16(y);
+      }
+    }
+  }
+
+  // z (M x r fp32) into LDS, rows of inactive tokens as zero.
+  __device__ __forceinline__ void stage_z() const {
+    const int r = p.ad.r;
+    const auto zr = make_rsrc(p.z, (uint32_t)(p.M * r * 4));
+    for (int e = threadIdx.x; e < p.M * r; e += NW * kWave)
+      zs[e] = tok[e / r].a >= 0 ? __uint_as_float(buf_load4<XPOL>(zr, 4u * e)) : 0.f;
+  }
+
+  __device__ __forceinline__ void flush(int& nstash) const {
+    for (int s = 0; s < nstash; ++s) outputs(stash_n0[s], stash + s * T * 16, false, zero4());
+    nstash = 0;
+  }
+
+  // Tile j / nb is complete in `acc`: reduce it and write its outputs, or
+  // stash it until z is published.
+  __device__ __forceinline__ void tile_done(int j, f32x4 (&acc)[MB], uint4& pre, bool& zready, int& nstash,
+                                            bool& ok) {
+    const int64_t n0 = n0_of(j);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const int t = mb * 16 + row;
+      *reinterpret_cast<float4*>(&part[(wave * T + t) * 16 + 4 * (lane >> 4)]) =
+          make_float4(acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]);
+      acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    if (!zready && threadIdx.x == 0) *verdict = load_relaxed(J.zflag) >= J.ztarget;
+    __syncthreads();
+    const int outs = (int)p.M * 16;
+    for (int e = threadIdx.x; e < outs; e += NW * kWave) {
+      float v = part[e];
+#pragma unroll
+      for (int w = 1; w < NW; ++w) v += part[w * T * 16 + e];
+      red[e] = v;
+    }
+    const bool now = !zready && *verdict != 0;
+    __syncthreads();
+    if (now) {  // z has just been published: stage it, drain the stash
+      stage_z();
+      __syncthreads();
+      zready = true;
+      if (ok) flush(nstash);
+      nstash = 0;
+    }
+    if (zready) {
+      if (ok) outputs(n0, red, true, pre);
+    } else {
+      for (int e = threadIdx.x; e < outs; e += NW * kWave) stash[nstash * T * 16 + e] = red[e];
+      if (threadIdx.x == 0) stash_n0[nstash] = n0;
+      ++nstash;
+      if (nstash == StashCfg<MB>::n) {  // the stash is full: wait for z here
+        ok = ok && wait_flag(J.zflag, J.ztarget, J.wait_ticks, p.ctrl + kCtrlError, verdict);
+        if (ok) {
+          stage_z();
+          __syncthreads();
+          zready = true;
+          flush(nstash);
+        }
+        nstash = 0;
+      }
+    }
+    if (j + 1 < total) pre = b_chunk(n0_of(j + 1), threadIdx.x >> 4);
+  }
+
+  // ---- the whole job --------------------------------------------------------
+  __device__ __forceinline__ void run() {
+    const int64_t M = p.M, K = p.K;
+    int* err = p.ctrl != nullptr ? p.ctrl + kCtrlError : nullptr;
+    if (FMT == EPILORA_W_FP4) build_fold_table(tbl);
+    resolve_tokens(g == 0);
+    __syncthreads();  // tok[] is read below by threads of other waves
+    if (XLDS) {
+      if (FUSED) {
+        for (int t = 0; t < M; ++t)
+          quant_row_lds<NW * kWave>(J.x + t * J.ldx, K, xs + t * K, sxs + t, reinterpret_cast<uint32_t*>(red));
+      } else {
+        const int64_t nv = M * K / 16;
+        for (int64_t v = threadIdx.x; v < nv; v += NW * kWave) {
+          const int64_t t = v * 16 / K, k = v * 16 % K;
+          *reinterpret_cast<uint4*>(xs + 16 * v) = *reinterpret_cast<const uint4*>(p.xq + t * p.ldq + k);
+        }
+      }
+    }
+    if (!FUSED) {
+      for (int t = threadIdx.x; t < M; t += NW * kWave) sxs[t] = p.sx[t];
+      if (adapters) stage_z();
+    }
+    __syncthreads();
+
+    bool ok = true;
+    bool zready = !FUSED || !adapters;
+    int nstash = 0;
+    f32x4 acc[MB];
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    uint4 pre = b_chunk(n0_of(0), threadIdx.x >> 4);
+
+    SkinnyBatch<MB, U> A, B;
+    load_w(A, 0);
+    if (FUSED && !XLDS) {  // the quantized rows come from other workgroups
+      ok = wait_flag(J.qflag, J.qtarget, J.wait_ticks, err, verdict);
+      const auto sr = make_rsrc(p.sx, (uint32_t)(M * 4));
+      for (int t = threadIdx.x; t < M; t += NW * kWave) sxs[t] = __uint_as_float(buf_load4<kCoherent>(sr, 4u * t));
+      __syncthreads();
+    }
+    load_x(A, 0);
+
+    for (int j = 0; j < total; j += 2) {
+      load_w(B, j + 1);
+      load_x(B, j + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(A, j, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      if (j % nb == nb - 1) tile_done(j, acc, pre, zready, nstash, ok);
+      load_w(A, j + 2);
+      load_x(A, j + 2);
+      __builtin_amdgcn_sched_barrier(0);
+      compute(B, j + 1, acc);
+      __builtin_amdgcn_sched_barrier(0);
+      if (j + 1 < total && (j + 1) % nb == nb - 1) tile_done(j + 1, acc, pre, zready, nstash, ok);
+    }
+    if (nstash > 0) {  // z was not ready for the last tiles: wait for it once
+      ok = ok && wait_flag(J.zflag, J.ztarget, J.wait_ticks, err, verdict);
+      if (ok) {
+        stage_z();
+        __syncthreads();
+        flush(nstash);
+      }
+    }
+    if (!ok && threadIdx.x == 0 && err != nullptr) atomic_or_relaxed(err, EPILORA_DEV_WAIT_TIMEOUT);
+  }
+};
+
+// Host side: the launch shape of a persistent skinny grid.  Eight waves per
+// workgroup when there are at most 256 tiles and few tokens, else four; the
+// grid holds as many workgroups as can be resident (`resident`), at most one
+// per tile.
+inline int skinny_waves(int64_t N, int MB) { return (cdiv(N, 16) <= 256 && MB <= 2) ? 8 : 4; }
+inline int skinny_groups(int64_t N, int resident) {
+  const int64_t tiles = cdiv(N, 16);
+  return (int)(tiles < resident ? tiles : (resident > 0 ? resident : 1));
+}
+// Whether the quantized activations live in LDS (the fused kernel then
+// quantizes them itself), and the LDS bytes of the workgroup.
+inline bool skinny_x_in_lds(int64_t M, int64_t K, int MB, int NW, int r, bool fused) {
+  if (M * K > kXInLdsMax || (fused && M > kSelfQuantMaxM)) return false;
+  const int nstash = fused ? (MB == 1 ? 8 : (MB == 2 ? 4 : 2)) : 0;
+  return sk_layout(MB, NW, r, (uint32_t)(M * K), nstash).total <= kLdsBudget;
+}
+inline uint32_t skinny_lds(int64_t M, int64_t K, int MB, int NW, int r, bool fused, bool xlds) {
+  const int nstash = fused ? (MB == 1 ? 8 : (MB == 2 ? 4 : 2)) : 0;
+  return sk_layout(MB, NW, r, xlds ? (uint32_t)(M * K) : 0u, nstash).total;
+}
+
+}  // namespace epilora
