@@ -95,7 +95,7 @@ size_t epilora_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K, int3
   (void)N;
   if (M < 0 || K < 0 || r < 0) return 0;
   switch (op) {
-    case EPILORA_OP_SHRINK: return shrink_ws(kCtrlBytes, M, K, r).total;
+    case EPILORA_OP_SHRINK: return shrink_ws(kStateBytes, M, K, r).total;
     case EPILORA_OP_GEMM:
     case EPILORA_OP_EXPAND:
     case EPILORA_OP_QUANT_W4: return kCtrlBytes;
@@ -156,7 +156,8 @@ int epilora_lora_shrink(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, co
   if (st != EPILORA_OK) return st;
   if (ldx < K) return EPILORA_ERR_INVALID_ARG;
   if (K % 16 != 0 || ldx % 16 != 0 || !aligned(x, 16) || !aligned(z, 16)) return EPILORA_ERR_UNSUPPORTED;
-  st = check_ws(ws, ws_bytes, shrink_ws(kCtrlBytes, M, K, r).total);
+  if (cdiv(M, kShrinkTokens) > kMaxShrinkTiles) return EPILORA_ERR_UNSUPPORTED;
+  st = check_ws(ws, ws_bytes, shrink_ws(kStateBytes, M, K, r).total);
   if (st != EPILORA_OK) return st;
   AdapterArgs ad;
   ad.A = A; ad.B = nullptr; ad.ranks = ranks; ad.idx = idx; ad.mask = mask;

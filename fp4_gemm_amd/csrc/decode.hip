@@ -7,14 +7,18 @@
 // "Multi-adapter kernels", The decode path; Background, "Programmatic
 // dependent launch").  HIP has no programmatic dependent launch, so one grid
 // plays both kernels:
-//   workgroups [0, M)          quantize one token row each and count up the
-//                              quantized-rows flag;
+//   workgroups [0, nq)         quantize one token row each and count up the
+//                              quantized-rows flag (nq = 0 when every GEMM
+//                              workgroup quantizes the few rows into its own
+//                              LDS and the caller keeps no copy);
 //   the next tiles*splits      compute the shrink (bf16 x, fp32 partials,
-//                              fixed-order combine) and count up the z flag;
-//   the rest                   own 16 weight rows each: request their first
-//                              weight batch, wait for the quantized rows,
+//                              the last split of a tile adds them in a fixed
+//                              order) and count up the z flag;
+//   the rest                   own 16-row weight tiles: request their first
+//                              weight batch, obtain the quantized rows,
 //                              stream the weights through the matrix cores,
-//                              and wait for z only before the epilogue.
+//                              and wait for z only before an epilogue
+//                              (finished tiles wait in an LDS stash).
 // Data crosses workgroups only through device-coherent stores and loads
 // (sc1), and a producer bumps its flag (a relaxed agent-scope atomic) only
 // after its stores have completed, so no workgroup has to write back or
@@ -22,9 +26,9 @@
 // producers are resident before any consumer spins; every wait is bounded by
 // a wall-clock limit and a timeout raises EPILORA_DEV_WAIT_TIMEOUT instead of
 // hanging.  The last GEMM workgroup to finish puts the flags back to zero for
-// the next call.  The GEMM part runs the same main loop and epilogue code as
-// the skinny GEMM kernel, so every output is bitwise equal to the separate
-// quant + shrink + GEMM calls.
+// the next call.  The quantizer, shrink and GEMM arithmetic is the same code
+// as in the separate kernels, with the same summation orders, so every output
+// is bitwise equal to the separate quant + shrink + GEMM calls.
 #include "quant_row.h"
 #include "shrink_common.h"
 #include "skinny.h"
@@ -35,10 +39,13 @@ struct DecodeParams {
   SkinnyJob job;  // job.g.xq / job.g.sx: where the quantized rows go; job.g.z: ws z
   ShrinkParams s;
   int nq, ns, tiles;
+  int count_q;  // the GEMM workgroups wait for the quantized rows
+  int flags;    // some flag is counted: the GEMM workgroups reset them at the end
+  int* done;    // kDoneGroups sub-counters, kDoneStride words apart
 };
 
 template <int MB, int FMT, int NW, bool XLDS>
-__global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((XLDS && NW == 8) ? 4 : 2))) void decode_kernel(DecodeParams p) {
   extern __shared__ __align__(16) char smem[];
   const GemmParams& g = p.job.g;
   int* ctrl = g.ctrl;
@@ -49,9 +56,11 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     const auto sr = make_rsrc(g.sx + bid, 4u);
     quant_row<NW * 64, kCoherent>(p.job.x + (int64_t)bid * p.job.ldx, g.K, qr, 0u, sr, 0u,
                                   reinterpret_cast<uint32_t*>(smem));
-    wait_all_memory();
-    __syncthreads();
-    if (threadIdx.x == 0) atomic_add_relaxed(ctrl + kCtrlQuantDone, 1);
+    if (p.count_q) {
+      wait_all_memory();
+      __syncthreads();
+      if (threadIdx.x == 0) atomic_add_relaxed(ctrl + kCtrlQuantDone, 1);
+    }
     return;
   }
   if (bid < p.nq + p.ns) {  // ---- shrink
@@ -70,13 +79,25 @@ __global__ __launch_bounds__(NW * 64) void decode_kernel(DecodeParams p) {
     Skinny<MB, FMT, NW, XLDS, true> sk(p.job, smem, bid - p.nq - p.ns);
     sk.run();
   }
+  if (!p.flags) return;
+  // Every flag read of this workgroup is behind it: count it done.  The last
+  // of each group counts the group, and the last group puts the flags back to
+  // zero; each counter is reset by the one that completed it.
   __syncthreads();
   if (threadIdx.x == 0) {
+    const int gi = bid - p.nq - p.ns;
     const int ng = (int)gridDim.x - p.nq - p.ns;
-    if (atomic_add_relaxed(ctrl + kCtrlGemmDone, 1) == ng - 1) {
-      store_relaxed(ctrl + kCtrlQuantDone, 0);
-      store_relaxed(ctrl + kCtrlZDone, 0);
-      store_relaxed(ctrl + kCtrlGemmDone, 0);
+    const int groups = ng < kDoneGroups ? ng : kDoneGroups;
+    const int grp = gi % groups;
+    const int members = ng / groups + (grp < ng % groups ? 1 : 0);
+    int* sub = p.done + grp * kDoneStride;
+    if (atomic_add_relaxed(sub, 1) == members - 1) {
+      store_relaxed(sub, 0);
+      if (atomic_add_relaxed(ctrl + kCtrlGemmDone, 1) == groups - 1) {
+        store_relaxed(ctrl + kCtrlQuantDone, 0);
+        store_relaxed(ctrl + kCtrlZDone, 0);
+        store_relaxed(ctrl + kCtrlGemmDone, 0);
+      }
     }
   }
 }
@@ -87,11 +108,13 @@ static void launch_decode_x(DecodeParams& p, bool want_xq, hipStream_t stream) {
   const int r = p.s.ad.r;
   p.nq = (XLDS && !want_xq) ? 0 : (int)g.M;
   p.job.qtarget = (int)g.M;
+  p.count_q = XLDS ? 0 : 1;
+  p.flags = p.count_q || p.ns > 0;
   size_t lds = skinny_lds(g.M, g.K, MB, NW, r, true, XLDS);
   const size_t shrink_lds = (size_t)kShrinkWaves * 16 * r * sizeof(float);
   if (shrink_lds > lds) lds = shrink_lds;
-  // The quantizing and shrink workgroups hold slots only briefly, so the
-  // persistent GEMM workgroups take every resident slot.
+  // The quantizing and shrink workgroups are dispatched first and hold their
+  // slots only until they finish.
   p.job.gwgs = skinny_groups(g.N, resident_groups(decode_kernel<MB, FMT, NW, XLDS>, NW * 64, lds));
   const unsigned grid = (unsigned)(p.nq + p.ns + p.job.gwgs);
   hipLaunchKernelGGL((decode_kernel<MB, FMT, NW, XLDS>), dim3(grid), dim3(NW * 64), lds, stream, p);
@@ -147,6 +170,7 @@ hipError_t launch_decode_lora(const uint16_t* x, int64_t ldx, int64_t M, int64_t
   s.x = x; s.M = M; s.K = K; s.ldx = ldx; s.ad = ad;
   s.z = reinterpret_cast<float*>(wsb + lay.z);
   s.ctrl = ctrl;
+  p.done = reinterpret_cast<int*>(wsb + kDoneOffset);
   s.counters = reinterpret_cast<int*>(wsb + lay.shrink.counters);
   s.partials = reinterpret_cast<float*>(wsb + lay.shrink.partials);
   s.splits = shrink_splits(M, K, ad.r);

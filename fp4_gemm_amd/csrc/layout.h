@@ -18,6 +18,22 @@ constexpr int kCtrlGemmDone = 10;  // fused path: GEMM workgroups finished
 constexpr size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 constexpr int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Counters that must read zero at the start of a call sit at fixed offsets
+// right after the control block, whatever the call's shape, so that a
+// workspace can serve calls of different shapes: every counter is put back
+// to zero by the call that used it, and data regions never overlap them.
+//   done sub-counters: the fused path's GEMM workgroups count themselves done
+//   in kDoneGroups counters 256 bytes apart (one contended word would
+//   serialize hundreds of atomics), then the last of each group in the
+//   kCtrlGemmDone word;
+//   tile counters: the shrink's per-tile split counters.
+constexpr int kDoneGroups = 16;
+constexpr int kDoneStride = 64;  // int32 words
+constexpr size_t kDoneOffset = kCtrlBytes;
+constexpr int64_t kMaxShrinkTiles = 4096;  // the shrink takes M <= 65536 per call
+constexpr size_t kTileCounterOffset = kDoneOffset + (size_t)kDoneGroups * kDoneStride * 4;
+constexpr size_t kStateBytes = align256(kTileCounterOffset + 4 * (size_t)kMaxShrinkTiles);
+
 // ---- shrink -----------------------------------------------------------------
 // A workgroup covers 16 consecutive tokens and a range of 128-wide K steps;
 // the K range is split over `splits` workgroups whose partial sums are
@@ -41,17 +57,17 @@ inline int shrink_splits(int64_t M, int64_t K, int32_t r) {
 }
 
 struct ShrinkWs {
-  size_t counters;  // int32 [tiles]
+  size_t counters;  // int32 [tiles], at the fixed tile-counter offset
   size_t partials;  // float [splits][M][r]
   size_t total;
 };
 
+// `base`: where the shrink's data region may start (at least kStateBytes).
 inline ShrinkWs shrink_ws(size_t base, int64_t M, int64_t K, int32_t r) {
   ShrinkWs w;
-  const int64_t tiles = cdiv(M, kShrinkTokens);
   const int s = shrink_splits(M, K, r);
-  w.counters = base;
-  w.partials = align256(w.counters + 4 * (size_t)tiles);
+  w.counters = kTileCounterOffset;
+  w.partials = align256(base);
   w.total = align256(w.partials + (s > 1 ? (size_t)s * M * r * 4 : 0));
   return w;
 }
@@ -67,7 +83,7 @@ struct DecodeWs {
 
 inline DecodeWs decode_ws(int64_t M, int64_t K, int32_t r) {
   DecodeWs w;
-  w.xq = kCtrlBytes;
+  w.xq = kStateBytes;
   w.sx = align256(w.xq + (size_t)M * K);
   w.z = align256(w.sx + 4 * (size_t)M);
   w.shrink = shrink_ws(align256(w.z + 4 * (size_t)M * r), M, K, r);

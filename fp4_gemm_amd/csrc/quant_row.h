@@ -13,8 +13,8 @@ namespace epilora {
 // read a second time for the encode pass.
 // amax: the largest |x| is the largest 15-bit bf16 magnitude, an integer max.
 // scale: amax / 448, an IEEE division (built with correctly rounded fp32
-// division); 1.0 for an all-zero row.  code: E4M3(x / scale), one IEEE
-// division per element.
+// division); 1.0 for an all-zero row.  code: E4M3(RN(x / scale)), the
+// quotient rounded exactly as IEEE division rounds it (quot below).
 // ---------------------------------------------------------------------------
 constexpr int kRegVecs = 16;
 
@@ -30,16 +30,37 @@ __device__ __forceinline__ uint32_t absmax8(const uint4& v) {
   return m;
 }
 
-__device__ __forceinline__ uint2 encode8(const uint4& v, float s) {
+// The quotient x / s rounded to nearest even, bit for bit what IEEE division
+// gives, for a row scale s > 0 and |x| <= 448 s.  With rs = RN(1/s),
+// q0 = RN(x rs) is within one ulp of x / s, the residual x - q0 s is exact
+// under a fused multiply-add, and one correction q0 + (x - q0 s) rs rounds to
+// the correctly rounded quotient (Markstein's theorem on division with a
+// correctly rounded reciprocal).  The theorem needs the residual to stay
+// normal: s >= 2^-64 keeps it normal for every |x / s| >= 2^-11, and smaller
+// quotients (a +-1 ulp error there) all encode to a signed zero anyway.  The
+// sign of a zero quotient is x's, as IEEE division gives it.  Rows with
+// s < 2^-64 take the division (quot_recip returns 0 for them).
+__device__ __forceinline__ float quot_recip(float s) { return s >= 0x1p-64f ? 1.0f / s : 0.0f; }
+
+__device__ __forceinline__ float quot(float x, float s, float rs) {
+  if (rs == 0.0f) return x / s;
+  const float q0 = x * rs;
+  const float r = fmaf(-q0, s, x);
+  return copysignf(fmaf(r, rs, q0), x);
+}
+
+// Eight bf16 values to E4M3 codes: E4M3(RN(x / s)).  |x / s| <= 448 (1 + 2^-23)
+// here, so the hardware conversion (round to nearest even, OCP E4M3FN on this
+// target, signed zero kept) never meets its overflow range.
+__device__ __forceinline__ uint2 encode8(const uint4& v, float s, float rs) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   uint32_t out[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const uint32_t c0 = e4m3_encode(bf16_lo(w[2 * h]) / s);
-    const uint32_t c1 = e4m3_encode(bf16_hi(w[2 * h]) / s);
-    const uint32_t c2 = e4m3_encode(bf16_lo(w[2 * h + 1]) / s);
-    const uint32_t c3 = e4m3_encode(bf16_hi(w[2 * h + 1]) / s);
-    out[h] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    int c = __builtin_amdgcn_cvt_pk_fp8_f32(quot(bf16_lo(w[2 * h]), s, rs), quot(bf16_hi(w[2 * h]), s, rs), 0, false);
+    c = __builtin_amdgcn_cvt_pk_fp8_f32(quot(bf16_lo(w[2 * h + 1]), s, rs), quot(bf16_hi(w[2 * h + 1]), s, rs), c,
+                                        true);
+    out[h] = (uint32_t)c;
   }
   return make_uint2(out[0], out[1]);
 }
@@ -87,13 +108,14 @@ __device__ __forceinline__ void quant_row(const uint16_t* __restrict__ xrow, int
   for (int j = tid + kRegVecs * NT; j < nv; j += NT) amax = max(amax, absmax8(src[j]));
   amax = block_max_u32<NT>(amax, red);
   const float s = row_scale(amax);
+  const float rs = quot_recip(s);
   if (tid == 0) buf_store4<POLICY>(sr, soff, __float_as_uint(s));
 #pragma unroll
   for (int i = 0; i < kRegVecs; ++i) {
     const int j = tid + i * NT;
-    if (j < nv) buf_store8<POLICY>(qr, qoff + 8 * j, encode8(v[i], s));
+    if (j < nv) buf_store8<POLICY>(qr, qoff + 8 * j, encode8(v[i], s, rs));
   }
-  for (int j = tid + kRegVecs * NT; j < nv; j += NT) buf_store8<POLICY>(qr, qoff + 8 * j, encode8(src[j], s));
+  for (int j = tid + kRegVecs * NT; j < nv; j += NT) buf_store8<POLICY>(qr, qoff + 8 * j, encode8(src[j], s, rs));
 }
 
 }  // namespace epilora

@@ -17,7 +17,7 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
 hipError_t launch_shrink(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const AdapterArgs& ad,
                          float* z, void* ws, hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  const ShrinkWs lay = shrink_ws(kCtrlBytes, M, K, ad.r);
+  const ShrinkWs lay = shrink_ws(kStateBytes, M, K, ad.r);
   ShrinkParams p;
   p.x = x; p.M = M; p.K = K; p.ldx = ldx; p.ad = ad; p.z = z;
   p.ctrl = reinterpret_cast<int*>(ws);

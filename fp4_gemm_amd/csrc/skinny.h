@@ -40,7 +40,7 @@ constexpr uint32_t kLdsBudget = 65536;
 // Tiles whose epilogue may wait for z in the fused kernel.
 template <int MB>
 struct StashCfg {
-  static constexpr int n = MB == 1 ? 8 : (MB == 2 ? 4 : 2);
+  static constexpr int n = MB <= 2 ? 4 : 2;
 };
 
 template <int MB>
@@ -114,25 +114,110 @@ __device__ __forceinline__ bool wait_flag(int* flag, int target, int64_t ticks, 
   return *verdict != 0;
 }
 
-// Quantize one row into LDS (codes and scale) with the NT threads of the
-// workgroup: the same arithmetic as quant_row, so the same bits.
-template <int NT>
-__device__ __forceinline__ void quant_row_lds(const uint16_t* __restrict__ xrow, int64_t K, uint8_t* qs, float* sxs,
-                                              uint32_t* red) {
-  const uint4* src = reinterpret_cast<const uint4*>(xrow);
-  const int nv = (int)(K / 8);
-  uint32_t amax = 0;
-  for (int j = threadIdx.x; j < nv; j += NT) amax = max(amax, absmax8(src[j]));
-  amax = block_max_u32<NT>(amax, red);
-  const float s = row_scale(amax);
-  if (threadIdx.x == 0) *sxs = s;
-  for (int j = threadIdx.x; j < nv; j += NT) *reinterpret_cast<uint2*>(qs + 8 * j) = encode8(src[j], s);
-  __syncthreads();
-}
+// The fused kernel quantizes the M <= kSelfQuantMaxM bf16 rows of x into
+// LDS (codes [M][K], scales [M]) with quant_row's arithmetic, so the same
+// bits, in two phases: the loads are requested before the first weight
+// batches (vector loads return in order, so a load issued after the weights
+// would wait for them) and the rest runs once they are in.  The M rows are
+// one run of 16-byte vectors; each thread keeps up to RV of its vectors in
+// registers between the phases (a longer run is read again in the second
+// phase).  The row maxima meet in one LDS round; `red` is
+// kSelfQuantMaxM * NT / 64 words of LDS.
+template <int NT, int RV>
+struct SelfQuant {
+  uint4 v[RV];
+
+  __device__ __forceinline__ void issue(const uint16_t* __restrict__ x, int64_t ldx, int M, int64_t K) {
+    const int nv = (int)(K / 8);
+#pragma unroll
+    for (int i = 0; i < RV; ++i) {
+      const int j = threadIdx.x + i * NT;
+      if (j < M * nv) {
+        const int t = j / nv;
+        v[i] = *reinterpret_cast<const uint4*>(x + t * ldx + 8 * (j - t * nv));
+      }
+    }
+  }
+
+  // Ends with a barrier.
+  __device__ __forceinline__ void finish(const uint16_t* __restrict__ x, int64_t ldx, int M, int64_t K, uint8_t* qs,
+                                         float* sxs, uint32_t* red) const {
+    constexpr int W = NT / kWave;
+    const int nv = (int)(K / 8);
+    const int total = M * nv;
+    const int tid = threadIdx.x;
+    uint32_t m[kSelfQuantMaxM];
+#pragma unroll
+    for (int u = 0; u < kSelfQuantMaxM; ++u) m[u] = 0;
+#pragma unroll
+    for (int i = 0; i < RV; ++i) {
+      const int j = tid + i * NT;
+      if (j < total) {
+        const int t = j / nv;
+        const uint32_t a = absmax8(v[i]);
+#pragma unroll
+        for (int u = 0; u < kSelfQuantMaxM; ++u)
+          if (u == t) m[u] = max(m[u], a);
+      }
+    }
+    for (int j = tid + RV * NT; j < total; j += NT) {
+      const int t = j / nv;
+      const uint32_t a = absmax8(*reinterpret_cast<const uint4*>(x + t * ldx + 8 * (j - t * nv)));
+#pragma unroll
+      for (int u = 0; u < kSelfQuantMaxM; ++u)
+        if (u == t) m[u] = max(m[u], a);
+    }
+    const int lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+    for (int u = 0; u < kSelfQuantMaxM; ++u) {
+      if (u < M) {
+        const uint32_t w = wave_max_u32(m[u]);
+        if (lane == 0) red[u * W + wave] = w;
+      }
+    }
+    __syncthreads();
+    float sc[kSelfQuantMaxM], rc[kSelfQuantMaxM];
+#pragma unroll
+    for (int u = 0; u < kSelfQuantMaxM; ++u) {
+      uint32_t a = 0;
+      if (u < M) {
+#pragma unroll
+        for (int w = 0; w < W; ++w) a = max(a, red[u * W + w]);
+      }
+      sc[u] = row_scale(a);
+      rc[u] = quot_recip(sc[u]);
+      if (tid == 0 && u < M) sxs[u] = sc[u];
+    }
+#pragma unroll
+    for (int i = 0; i < RV; ++i) {
+      const int j = tid + i * NT;
+      if (j < total) {
+        const int t = j / nv;
+        float s = sc[0], rs = rc[0];
+#pragma unroll
+        for (int u = 1; u < kSelfQuantMaxM; ++u)
+          if (u == t) s = sc[u], rs = rc[u];
+        *reinterpret_cast<uint2*>(qs + 8 * j) = encode8(v[i], s, rs);
+      }
+    }
+    for (int j = tid + RV * NT; j < total; j += NT) {
+      const int t = j / nv;
+      float s = sc[0], rs = rc[0];
+#pragma unroll
+      for (int u = 1; u < kSelfQuantMaxM; ++u)
+        if (u == t) s = sc[u], rs = rc[u];
+      *reinterpret_cast<uint2*>(qs + 8 * j) =
+          encode8(*reinterpret_cast<const uint4*>(x + t * ldx + 8 * (j - t * nv)), s, rs);
+    }
+    __syncthreads();
+  }
+};
 
 template <int MB, int FMT, int NW, bool XLDS, bool FUSED>
 struct Skinny {
-  static constexpr int U = SkinnyCfg<MB>::U;
+  // The fused kernel's 8-wave workgroups take half batches so that two fit
+  // on a compute unit (four waves per SIMD), beside a producer workgroup.
+  static constexpr int U = (FUSED && NW == 8 && MB == 1) ? 2 : SkinnyCfg<MB>::U;
   static constexpr int T = MB * 16;
   static constexpr int XPOL = FUSED ? kCoherent : kCached;
 
@@ -150,6 +235,7 @@ struct Skinny {
   uint32_t kofs, xbase[MB];
   __amdgpu_buffer_rsrc_t xr;
   bool adapters;
+  float gscale;  // 4-bit weights: gs * 8
 
   __device__ __forceinline__ Skinny(const SkinnyJob& j, char* lds, int gidx) : J(j), p(j.g), g(gidx) {
     const int64_t M = p.M, K = p.K;
@@ -176,6 +262,7 @@ struct Skinny {
     const int mine = (int)cdiv(J.tiles - g, J.gwgs);
     total = mine * nb;
     adapters = p.z != nullptr;
+    gscale = FMT == EPILORA_W_FP4 ? weight_scale<FMT>(p.wt, 0) : 0.f;
     xr = make_rsrc(p.xq, (uint32_t)((M - 1) * p.ldq + K));
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -268,12 +355,39 @@ struct Skinny {
   }
 
   // ---- epilogue pieces --------------------------------------------------------
-  __device__ __forceinline__ void resolve_tokens(bool report) const {
-    for (int t = threadIdx.x; t < T; t += blockDim.x) {
-      int rk = 0;
-      const int a = adapters ? resolve_token(t, p.M, p.ad, p.ctrl + kCtrlError, report, rk) : -1;
-      tok[t] = TokenSlot{a, rk};
+  // Token t's index and mask byte, loaded by thread t before the weights are
+  // requested (a later load would return only after them), and resolved into
+  // tok[] afterwards, as resolve_token does it.
+  struct TokenLoad {
+    int a = -1, m = 1;
+  };
+  __device__ __forceinline__ TokenLoad load_token() const {
+    TokenLoad tl;
+    const int t = threadIdx.x;
+    if (adapters && t < T && t < p.M) {
+      tl.a = p.ad.idx[t];
+      if (p.ad.mask != nullptr) tl.m = p.ad.mask[t];
     }
+    return tl;
+  }
+  __device__ __forceinline__ void resolve_tokens(const TokenLoad& tl, bool report) const {
+    const int t = threadIdx.x;
+    if (t >= T) return;
+    int a = -1, rk = 0;
+    if (adapters && t < p.M) {
+      a = tl.a;
+      if (a < -1 || a >= p.ad.L) {
+        if (report) atomic_or_relaxed(p.ctrl + kCtrlError, EPILORA_DEV_BAD_INDEX);
+        a = -1;
+      }
+      if (a >= 0 && tl.m == 0) a = -1;
+      if (a >= 0) {
+        rk = p.ad.ranks != nullptr ? p.ad.ranks[a] : p.ad.r;
+        rk = rk < p.ad.r ? rk : p.ad.r;
+        if (rk <= 0) a = -1, rk = 0;
+      }
+    }
+    tok[t] = TokenSlot{a, rk};
   }
 
   // The r / 16 bf16 values of B[a][n][jl * r / 16 ...] this lane needs for
@@ -306,9 +420,19 @@ struct Skinny {
     return v;
   }
 
+  // The weight scale of the output row this thread writes in the tile at n0
+  // (the output loop's stride is a multiple of 16, so a thread meets one row).
+  __device__ __forceinline__ float row_wscale(int64_t n0) const {
+    if (FMT == EPILORA_W_FP4) return gscale;
+    const int64_t n = n0 + ((threadIdx.x >> 4) & 15);
+    return n < p.N ? p.wt.sw[n] : 0.f;
+  }
+
   // Outputs of the tile at n0 from its reduced accumulators `base` ([T][16]).
-  // `pre` holds this thread's first-pass B slice when have_pre.
-  __device__ __forceinline__ void outputs(int64_t n0, const float* base, bool have_pre, const uint4& pre) const {
+  // With have_pre, `pre` holds this thread's first-pass B slice and `pws` its
+  // row's weight scale, both loaded while the tile was streaming.
+  __device__ __forceinline__ void outputs(int64_t n0, const float* base, bool have_pre, const uint4& pre,
+                                          float pws) const {
     const int jl = threadIdx.x & 15;
     const int r = p.ad.r;
     const int ch = r >> 4;
@@ -330,30 +454,50 @@ struct Skinny {
       l += __shfl_xor(l, 2, 16);
       l += __shfl_xor(l, 1, 16);
       if (jl == 0 && n < p.N) {
-        float y = (base[o] * sxs[t]) * weight_scale<FMT>(p.wt, n);
+        float y = (base[o] * sxs[t]) * (have_pre ? pws : weight_scale<FMT>(p.wt, n));
         if (lora) y = y + p.ad.scale * l;
         p.y[(int64_t)t * p.ldy + n] = (uint16_t)f32_to_bf16(y);
       }
     }
   }
 
-  // z (M x r fp32) into LDS, rows of inactive tokens as zero.
+  // z (M x r fp32) into LDS, rows of inactive tokens as zero.  Ends with a
+  // barrier.
   __device__ __forceinline__ void stage_z() const {
     const int r = p.ad.r;
     const auto zr = make_rsrc(p.z, (uint32_t)(p.M * r * 4));
     for (int e = threadIdx.x; e < p.M * r; e += NW * kWave)
       zs[e] = tok[e / r].a >= 0 ? __uint_as_float(buf_load4<XPOL>(zr, 4u * e)) : 0.f;
+    __syncthreads();
   }
 
-  __device__ __forceinline__ void flush(int& nstash) const {
-    for (int s = 0; s < nstash; ++s) outputs(stash_n0[s], stash + s * T * 16, false, zero4());
+  // The B slices and weight scales the stashed tiles' epilogues need, all
+  // requested at once (before z is staged) instead of one tile after another.
+  struct StashPre {
+    uint4 b[StashCfg<MB>::n];
+    float w[StashCfg<MB>::n];
+  };
+  __device__ __forceinline__ void stash_prefetch(StashPre& sp, int nstash) const {
+#pragma unroll
+    for (int s = 0; s < StashCfg<MB>::n; ++s) {
+      if (s < nstash) {
+        sp.b[s] = b_chunk(stash_n0[s], threadIdx.x >> 4);
+        sp.w[s] = row_wscale(stash_n0[s]);
+      }
+    }
+  }
+  __device__ __forceinline__ void flush(const StashPre& sp, int& nstash) const {
+#pragma unroll
+    for (int s = 0; s < StashCfg<MB>::n; ++s)
+      if (s < nstash) outputs(stash_n0[s], stash + s * T * 16, true, sp.b[s], sp.w[s]);
     nstash = 0;
   }
 
   // Tile j / nb is complete in `acc`: reduce it and write its outputs, or
-  // stash it until z is published.
-  __device__ __forceinline__ void tile_done(int j, f32x4 (&acc)[MB], uint4& pre, bool& zready, int& nstash,
-                                            bool& ok) {
+  // stash it until z is published.  `zseen`: thread 0's reading of the z
+  // flag, loaded before the latest weight batch was requested.
+  __device__ __forceinline__ void tile_done(int j, f32x4 (&acc)[MB], uint4& pre, float& pws, int zseen,
+                                            bool& zready, int& nstash, bool& ok) {
     const int64_t n0 = n0_of(j);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
@@ -362,7 +506,7 @@ struct Skinny {
           make_float4(acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]);
       acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    if (!zready && threadIdx.x == 0) *verdict = load_relaxed(J.zflag) >= J.ztarget;
+    if (!zready && threadIdx.x == 0) *verdict = zseen >= J.ztarget;
     __syncthreads();
     const int outs = (int)p.M * 16;
     for (int e = threadIdx.x; e < outs; e += NW * kWave) {
@@ -374,14 +518,15 @@ struct Skinny {
     const bool now = !zready && *verdict != 0;
     __syncthreads();
     if (now) {  // z has just been published: stage it, drain the stash
+      StashPre sp;
+      stash_prefetch(sp, nstash);
       stage_z();
-      __syncthreads();
       zready = true;
-      if (ok) flush(nstash);
+      if (ok) flush(sp, nstash);
       nstash = 0;
     }
     if (zready) {
-      if (ok) outputs(n0, red, true, pre);
+      if (ok) outputs(n0, red, true, pre, pws);
     } else {
       for (int e = threadIdx.x; e < outs; e += NW * kWave) stash[nstash * T * 16 + e] = red[e];
       if (threadIdx.x == 0) stash_n0[nstash] = n0;
@@ -389,38 +534,50 @@ struct Skinny {
       if (nstash == StashCfg<MB>::n) {  // the stash is full: wait for z here
         ok = ok && wait_flag(J.zflag, J.ztarget, J.wait_ticks, p.ctrl + kCtrlError, verdict);
         if (ok) {
+          StashPre sp;
+          stash_prefetch(sp, nstash);
           stage_z();
-          __syncthreads();
           zready = true;
-          flush(nstash);
+          flush(sp, nstash);
         }
         nstash = 0;
       }
     }
-    if (j + 1 < total) pre = b_chunk(n0_of(j + 1), threadIdx.x >> 4);
+    if (j + 1 < total) {
+      pre = b_chunk(n0_of(j + 1), threadIdx.x >> 4);
+      pws = row_wscale(n0_of(j + 1));
+    }
   }
 
   // ---- the whole job --------------------------------------------------------
   __device__ __forceinline__ void run() {
+    constexpr int NT = NW * kWave;
+    constexpr int RV = NW == 8 ? 4 : 8;
     const int64_t M = p.M, K = p.K;
     int* err = p.ctrl != nullptr ? p.ctrl + kCtrlError : nullptr;
+    // Activation loads first, then the first two weight batches; the set-up
+    // below overlaps them.
+    SelfQuant<NT, RV> sq;
+    if (XLDS && FUSED) sq.issue(J.x, J.ldx, (int)M, K);
+    const TokenLoad tl = load_token();
+    __builtin_amdgcn_sched_barrier(0);
+    SkinnyBatch<MB, U> A, B;
+    load_w(A, 0);
+    load_w(B, 1);
+    __builtin_amdgcn_sched_barrier(0);
     if (FMT == EPILORA_W_FP4) build_fold_table(tbl);
-    resolve_tokens(g == 0);
+    resolve_tokens(tl, g == 0);
     __syncthreads();  // tok[] is read below by threads of other waves
-    if (XLDS) {
-      if (FUSED) {
-        for (int t = 0; t < M; ++t)
-          quant_row_lds<NW * kWave>(J.x + t * J.ldx, K, xs + t * K, sxs + t, reinterpret_cast<uint32_t*>(red));
-      } else {
-        const int64_t nv = M * K / 16;
-        for (int64_t v = threadIdx.x; v < nv; v += NW * kWave) {
-          const int64_t t = v * 16 / K, k = v * 16 % K;
-          *reinterpret_cast<uint4*>(xs + 16 * v) = *reinterpret_cast<const uint4*>(p.xq + t * p.ldq + k);
-        }
+    if (XLDS && FUSED) sq.finish(J.x, J.ldx, (int)M, K, xs, sxs, reinterpret_cast<uint32_t*>(red));
+    if (XLDS && !FUSED) {  // the skinny GEMM kernel: copy the quantized rows
+      const int64_t nv = M * K / 16;
+      for (int64_t v = threadIdx.x; v < nv; v += NT) {
+        const int64_t t = v * 16 / K, k = v * 16 % K;
+        *reinterpret_cast<uint4*>(xs + 16 * v) = *reinterpret_cast<const uint4*>(p.xq + t * p.ldq + k);
       }
     }
     if (!FUSED) {
-      for (int t = threadIdx.x; t < M; t += NW * kWave) sxs[t] = p.sx[t];
+      for (int t = threadIdx.x; t < M; t += NT) sxs[t] = p.sx[t];
       if (adapters) stage_z();
     }
     __syncthreads();
@@ -432,37 +589,53 @@ struct Skinny {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
     uint4 pre = b_chunk(n0_of(0), threadIdx.x >> 4);
+    float pws = row_wscale(n0_of(0));
 
-    SkinnyBatch<MB, U> A, B;
-    load_w(A, 0);
     if (FUSED && !XLDS) {  // the quantized rows come from other workgroups
       ok = wait_flag(J.qflag, J.qtarget, J.wait_ticks, err, verdict);
       const auto sr = make_rsrc(p.sx, (uint32_t)(M * 4));
-      for (int t = threadIdx.x; t < M; t += NW * kWave) sxs[t] = __uint_as_float(buf_load4<kCoherent>(sr, 4u * t));
+      for (int t = threadIdx.x; t < M; t += NT) sxs[t] = __uint_as_float(buf_load4<kCoherent>(sr, 4u * t));
       __syncthreads();
     }
     load_x(A, 0);
+    load_x(B, 1);
 
+    // Two batches in flight; a tile's epilogue runs before the batch that
+    // just finished is refilled.  The z flag for the next tile end is read
+    // before the batch preceding it is requested, so that the epilogue waits
+    // only for the flag, not for that batch.  (z is taken as not ready at the
+    // first tile end.)
+    int zseen = 0;
     for (int j = 0; j < total; j += 2) {
-      load_w(B, j + 1);
-      load_x(B, j + 1);
+      const bool endA = j % nb == nb - 1;
+      const bool endB = j + 1 < total && (j + 1) % nb == nb - 1;
+      const bool endA2 = j + 2 < total && (j + 2) % nb == nb - 1;
       __builtin_amdgcn_sched_barrier(0);
       compute(A, j, acc);
       __builtin_amdgcn_sched_barrier(0);
-      if (j % nb == nb - 1) tile_done(j, acc, pre, zready, nstash, ok);
+      if (endA) tile_done(j, acc, pre, pws, zseen, zready, nstash, ok);
+      zseen = 0;
+      if (endB && !zready && threadIdx.x == 0) zseen = load_relaxed(J.zflag);
+      __builtin_amdgcn_sched_barrier(0);
       load_w(A, j + 2);
       load_x(A, j + 2);
       __builtin_amdgcn_sched_barrier(0);
       compute(B, j + 1, acc);
       __builtin_amdgcn_sched_barrier(0);
-      if (j + 1 < total && (j + 1) % nb == nb - 1) tile_done(j + 1, acc, pre, zready, nstash, ok);
+      if (endB) tile_done(j + 1, acc, pre, pws, zseen, zready, nstash, ok);
+      zseen = 0;
+      if (endA2 && !zready && threadIdx.x == 0) zseen = load_relaxed(J.zflag);
+      __builtin_amdgcn_sched_barrier(0);
+      load_w(B, j + 3);
+      load_x(B, j + 3);
     }
     if (nstash > 0) {  // z was not ready for the last tiles: wait for it once
       ok = ok && wait_flag(J.zflag, J.ztarget, J.wait_ticks, err, verdict);
       if (ok) {
+        StashPre sp;
+        stash_prefetch(sp, nstash);
         stage_z();
-        __syncthreads();
-        flush(nstash);
+        flush(sp, nstash);
       }
     }
     if (!ok && threadIdx.x == 0 && err != nullptr) atomic_or_relaxed(err, EPILORA_DEV_WAIT_TIMEOUT);
@@ -470,23 +643,26 @@ struct Skinny {
 };
 
 // Host side: the launch shape of a persistent skinny grid.  Eight waves per
-// workgroup when there are at most 256 tiles and few tokens, else four; the
-// grid holds as many workgroups as can be resident (`resident`), at most one
-// per tile.
+// workgroup when there are at most 256 tiles and few tokens, else four.  The
+// grid takes as few rounds of tiles as the resident slots (`resident`) allow
+// and, for that many rounds, as few workgroups as give every workgroup the
+// same number of tiles to within one, so slots stay free for others.
 inline int skinny_waves(int64_t N, int MB) { return (cdiv(N, 16) <= 256 && MB <= 2) ? 8 : 4; }
 inline int skinny_groups(int64_t N, int resident) {
   const int64_t tiles = cdiv(N, 16);
-  return (int)(tiles < resident ? tiles : (resident > 0 ? resident : 1));
+  const int64_t slots = resident > 0 ? resident : 1;
+  const int64_t rounds = cdiv(tiles, slots);
+  return (int)cdiv(tiles, rounds);
 }
 // Whether the quantized activations live in LDS (the fused kernel then
 // quantizes them itself), and the LDS bytes of the workgroup.
 inline bool skinny_x_in_lds(int64_t M, int64_t K, int MB, int NW, int r, bool fused) {
   if (M * K > kXInLdsMax || (fused && M > kSelfQuantMaxM)) return false;
-  const int nstash = fused ? (MB == 1 ? 8 : (MB == 2 ? 4 : 2)) : 0;
+  const int nstash = fused ? (MB <= 2 ? 4 : 2) : 0;
   return sk_layout(MB, NW, r, (uint32_t)(M * K), nstash).total <= kLdsBudget;
 }
 inline uint32_t skinny_lds(int64_t M, int64_t K, int MB, int NW, int r, bool fused, bool xlds) {
-  const int nstash = fused ? (MB == 1 ? 8 : (MB == 2 ? 4 : 2)) : 0;
+  const int nstash = fused ? (MB <= 2 ? 4 : 2) : 0;
   return sk_layout(MB, NW, r, xlds ? (uint32_t)(M * K) : 0u, nstash).total;
 }
 

@@ -193,7 +193,8 @@ int epilora_quant_weight_fp4(const uint16_t* w, int64_t N, int64_t K,
  * [0, L), its mask byte (if any) is nonzero and its rank is positive.
  * Split-K partial sums are combined in a fixed order, so results are
  * deterministic ("The decode path").  x: bf16 [M][ldx]; A: bf16 [L][r][K];
- * z: fp32 [M][r].  K % 16 == 0, r % 16 == 0, r <= 128.
+ * z: fp32 [M][r].  K % 16 == 0, r % 16 == 0, r <= 128, M <= 65536 (else
+ * EPILORA_ERR_UNSUPPORTED; longer batches go in several calls).
  * Needs a workspace of EPILORA_OP_SHRINK. */
 int epilora_lora_shrink(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                         const uint16_t* A, int32_t L, int32_t r,
@@ -229,10 +230,11 @@ int epilora_lora_expand_add(const float* z, int64_t M, int64_t N,
 
 /* The fused small-batch (decode) path ("Multi-adapter kernels", The decode
  * path): quantization, shrink and the GEMM with its epilogue in ONE launch.
- * The lowest workgroups quantize x and compute z and publish each with a
- * device flag (release/acquire, agent scope); the GEMM workgroups stream
- * their weights meanwhile and wait for z only before the epilogue.  HIP has
- * no programmatic dependent launch; this persistent split replaces it.
+ * The lowest workgroups compute z (and quantize x where the GEMM workgroups
+ * do not do it themselves) and publish it with device-coherent stores and a
+ * counted device flag; the GEMM workgroups stream their weights meanwhile
+ * and wait for z only before the epilogue.  HIP has no programmatic
+ * dependent launch; this persistent split replaces it.
  * After a call that raised EPILORA_DEV_WAIT_TIMEOUT, re-initialise the
  * workspace (epilora_workspace_init) before using it again.
  * Same result as epilora_quant_act + epilora_lora_shrink +

@@ -42,6 +42,23 @@ def _special_rows(K, rng):
     rows.append((rng.standard_normal(K) * 1e-36).astype(np.float32))     # tiny values
     rows.append((rng.standard_normal(K) * 3e37).astype(np.float32))      # huge values
     rows.append(np.resize(np.array([1.0, -0.0, 0.0, 2.0 ** -20], np.float32), K))
+    # every bf16 value in [-448, 448] (as many as fit), at sx = 1: each one
+    # goes through the E4M3 conversion unchanged
+    allb = np.arange(0x10000, dtype=np.uint32)
+    vals = (allb << 16).view(np.float32)
+    vals = vals[np.isfinite(vals) & (np.abs(vals) <= 448)]
+    r = np.resize(rng.permutation(vals), K).astype(np.float32)
+    r[0] = 448.0
+    rows.append(r)
+    # scales either side of 2^-64 (the reciprocal-quotient threshold), and a
+    # scale that is no power of two with values spread over many binades
+    for amax in (448.0 * 2.0 ** -64 * 1.0078125, 448.0 * 2.0 ** -64 * 0.9921875):
+        r = (rng.standard_normal(K) * amax / 4).astype(np.float32)
+        r[0] = amax
+        rows.append(r)
+    r = (rng.choice([-1.0, 1.0], K) * 2.0 ** rng.uniform(-40, 6.8, K)).astype(np.float32)
+    r[0] = 113.37
+    rows.append(r)
     return np.stack(rows)
 
 
