@@ -145,19 +145,21 @@ class Proj:
         return 2 * self.M * self.N * self.K + sum(2 * rk(a) * (self.K + self.N) for a in act)
 
 
-def graph_of(fns, copies):
-    """Capture `copies` rounds of fns (round c uses weight copy c) in one graph."""
+def graph_of(fns, copies, only=None):
+    """Capture `copies` rounds of fns (round c uses weight copy c) in one graph,
+    or only round `only`."""
+    rounds = range(copies) if only is None else [only]
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):
-        for c in range(copies):  # warm (first-launch costs out of the capture)
+        for c in rounds:  # warm (first-launch costs out of the capture)
             for f in fns:
                 f(c)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for c in range(copies):
+        for c in rounds:
             for f in fns:
                 f(c)
     torch.cuda.synchronize()
@@ -179,14 +181,36 @@ def time_graph(g, rounds, warmup):
 
 
 def per_step_us(projs, fn_names, steps, warmup):
+    """Microseconds per step: one graph per weight copy (a step = fn_names
+    over projs), replayed in turn; `warmup` untimed steps, then exactly
+    `steps` timed ones between two synchronizations, timed with events on
+    the stream the graphs replay on."""
+    fns = [getattr(p, n) for p in projs for n in fn_names]
+    graphs = [graph_of(fns, ROTATE, only=c) for c in range(ROTATE)]
+    for i in range(warmup):
+        graphs[i % ROTATE].replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        graphs[i % ROTATE].replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return 1000.0 * e0.elapsed_time(e1) / steps, steps
+
+
+def per_call_us(projs, fn_names, steps, warmup):
+    """Microseconds per pass of fn_names over projs for the diagnostic
+    figures: one graph holds a pass over each weight copy, so that short
+    kernels are not paced by graph launches."""
     fns = [getattr(p, n) for p in projs for n in fn_names]
     g = graph_of(fns, ROTATE)
     rounds = max(1, steps // ROTATE)
     ms = time_graph(g, rounds, max(1, warmup // ROTATE))
-    return 1000.0 * ms / ROTATE, rounds * ROTATE
+    return 1000.0 * ms / ROTATE
 
 
-def cpu_baseline(layer, frac=8, min_seconds=10.0, max_reps=50):
+def cpu_baseline(layer, frac=4, min_seconds=10.0, max_reps=1000):
     """The oracle on a bounded sample of the decode layer: every frac-th
     output channel of each projection (its weights quantized by the oracle
     outside the timed region), repeated until about min_seconds of CPU work
@@ -217,6 +241,60 @@ def cpu_baseline(layer, frac=8, min_seconds=10.0, max_reps=50):
                       f"{timed:.1f} s timed, scaled x{frac}; host has {os.cpu_count()} cpus"}
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_gate_up_traffic.txt")
+CSRC = os.path.join(ROOT, "fp4_gemm_amd", "csrc")
+
+
+def kernel_source_digest():
+    """sha256 over the kernel sources, to tell whether recorded counters are
+    still those of the kernel that runs."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".h", ".hip")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 counter summary, or None when there is none or the kernel
+    sources have changed since it was taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split(":", 1) for line in f if ":" in line and not line.startswith("#"))
+        kv = {k.strip(): v.strip() for k, v in kv.items()}
+        if kv.get("kernel_source_sha256") != kernel_source_digest():
+            return None
+        return int(float(kv["traffic_bytes_per_launch"]))
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def traffic_probe(args):
+    """Dispatches for the HBM counters (run under rocprofv3 --pmc): a plain
+    copy of 1 GiB (the calibration kernel of known size), then the fused
+    gate_up projection over its rotated copies, eagerly (one dispatch per
+    call, no graph)."""
+    torch.cuda.set_device(0)
+    ep.lib()
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=DEV).fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    torch.cuda.empty_cache()
+    layer = config(2)
+    p = Proj([g for g in layer.gemms if g.name == "gate_up"][0])
+    for i in range(args.steps):
+        p.fused(i % ROTATE)
+    torch.cuda.synchronize()
+    print(json.dumps({"probe": "traffic", "copy_bytes": 1 << 30, "gate_up_launches": args.steps,
+                      "algorithmic_bytes_per_launch": p.bytes()}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -224,11 +302,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="only the dispatches the HBM-counter runs measure (see traffic_probe)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this layer shards by tensor parallelism, which is "
               "not part of this build; run with --gpus 1", file=sys.stderr)
         sys.exit(2)
+    if args.traffic_probe:
+        traffic_probe(args)
+        return
     torch.cuda.set_device(0)
     ep.lib()
 
@@ -239,12 +322,13 @@ def main():
     torch.cuda.synchronize()
     fused_us, timed_steps = per_step_us(projs, ["fused"], args.steps, args.warmup)
     base_us, _ = per_step_us(projs, ["fused_base"], args.steps, args.warmup)
-    serial_us, _ = per_step_us(projs, ["quant", "shrink", "gemm_lora"], args.steps, args.warmup)
-    separate_us, _ = per_step_us(projs, ["quant", "gemm_base", "shrink", "expand"], args.steps, args.warmup)
+    serial_us = per_call_us(projs, ["quant", "shrink", "gemm_lora"], args.steps, args.warmup)
+    separate_us = per_call_us(projs, ["quant", "gemm_base", "shrink", "expand"], args.steps, args.warmup)
+    gemm_only_us = per_call_us(projs, ["gemm_base"], args.steps, args.warmup)
     per_proj = {}
     for p in projs:
-        f_us, _ = per_step_us([p], ["fused"], args.steps, args.warmup)
-        b_us, _ = per_step_us([p], ["fused_base"], args.steps, args.warmup)
+        f_us = per_call_us([p], ["fused"], args.steps, args.warmup)
+        b_us = per_call_us([p], ["fused_base"], args.steps, args.warmup)
         per_proj[p.g.name] = {"fused_us": round(f_us, 2), "base_us": round(b_us, 2),
                               "bytes": p.bytes(), "GBps": round(p.bytes() / f_us / 1e3, 1)}
     layer_bytes = sum(p.bytes() for p in projs)
@@ -300,12 +384,14 @@ def main():
         "layer_bytes": layer_bytes,
         "base_only_us": round(base_us, 2),
         "fused_over_base": round(fused_us / base_us, 3),
+        "gemm_only_us": round(gemm_only_us, 2),
         "serialized_us": round(serial_us, 2),
         "separate_kernels_us": round(separate_us, 2),
         "per_projection": per_proj,
         "roofline": {"kernel": f"decode_kernel ({dom.g.name}, fused)", "bound": "hbm",
                      "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": None},
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
+                     "algorithmic_bytes": dom.bytes(), "launch_us": dom_us},
         "prefill": prefill,
         "cpu_baseline": cpu,
     }
