@@ -89,4 +89,7 @@ struct TokenSlot {
   int rank;
 };
 
+// The prefill GEMM (M > 64), gemm_wide.hip.
+void launch_gemm_wide(const GemmParams& p, hipStream_t stream);
+
 }  // namespace epilora

@@ -1,0 +1,447 @@
+// The prefill GEMM (M > 64) with the multi-adapter epilogue, on the FP8
+// matrix cores of gfx950.
+//
+// One workgroup of 4 waves computes a BM x BN tile of Y (tokens x outputs),
+// each wave a (BM/2) x (BN/2) quarter held as 16 x 16 accumulator blocks of
+// v_mfma_f32_16x16x128_f8f6f4 (up to 8 x 8 blocks: 256 accumulator registers
+// per lane, one wave per SIMD).  K advances in steps of 128: both operand
+// tiles (BM and BN rows of 128 bytes) are staged in LDS, double buffered,
+// each 128-byte row's 16-byte chunks XOR-swizzled by (row % 8) so that the 8
+// rows consecutive lanes read fall in distinct banks.  The next step's FP8
+// tiles go from memory straight into the other buffer (buffer loads with the
+// lds bit) while the current step is multiplied; one barrier per step.
+// 4-bit weights are loaded into registers and folded to FP8 bytes (a
+// per-block 8-entry table, v_perm_b32) as they are written to LDS, so the
+// inner loop is the same for both formats.
+//
+// Tiles are numbered so that each of the 8 XCDs (workgroups are dispatched to
+// them in turn) takes a contiguous run, M-tiles fastest: the workgroups one
+// XCD runs together share a few weight tiles in that XCD's L2.
+//
+// Epilogue: the accumulators are scaled in place, (acc * sx_t) * sw_n (or
+// gs * 8).  With adapters, z for the tile's tokens is staged in LDS as bf16
+// and the distinct adapters of the tile's tokens are taken in turn: every
+// 16-token block holding one of the adapter's tokens multiplies z (other
+// tokens zero) by the adapter's B rows on bf16 MFMA; only the adapter's own
+// tokens then add s * (B z), the other rows get no add at all.  The bf16 tile
+// goes out through LDS as full 16-byte row chunks.
+#include "gemm_common.h"
+
+namespace epilora {
+
+namespace {
+
+constexpr int kWideThreads = 256;
+constexpr int kStep = 128;
+
+__device__ __forceinline__ int swz8(int row, int chunk) { return row * 128 + ((chunk ^ (row & 7)) << 4); }
+
+}  // namespace
+
+template <int FMT, int BM, int BN>
+__global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(GemmParams p, int tiles_m, int tiles_n) {
+  constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 16, TN = WN / 16;
+  // Two operand buffers as distinct objects, so that the compiler sees that
+  // the loads filling one never alias the reads of the other (and does not
+  // wait for them before those reads).  Each holds A ([BM][128]) then B
+  // ([BN][128]).
+  // The epilogue reuses them: z (half the tile's tokens each, 512-byte rows,
+  // so at least BM / 2 x 512 bytes) and two 32 KB slots of B rows in buf1.
+  constexpr int kOps = (BM + BN) * kStep;
+  constexpr int kBuf0 = kOps > BM * 256 ? kOps : BM * 256;
+  constexpr int kBuf = kBuf0 > 2 * 32768 ? kBuf0 : 2 * 32768;
+  static_assert(BM / 2 * 512 <= kBuf && 2 * 32768 <= kBuf && BM * 256 <= kBuf, "epilogue LDS regions");
+  __shared__ __align__(16) uint8_t buf0[kBuf];
+  __shared__ __align__(16) uint8_t buf1[kBuf];
+  __shared__ uint2 tbl[FMT == EPILORA_W_FP4 ? 256 : 1];
+  __shared__ TokenSlot tok[BM];
+  __shared__ int groups[BM];  // the first token of each distinct adapter
+  __shared__ int counts[kWideThreads / 64];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave & 1, wn = wave >> 1;
+
+  // ---- tile of this workgroup: a contiguous run of tiles per XCD ----------
+  const int nt = tiles_m * tiles_n;
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  const int per = nt >> 3, rem = nt & 7;
+  const int tile = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + local;
+  const int64_t m0 = (int64_t)(tile % tiles_m) * BM, n0 = (int64_t)(tile / tiles_m) * BN;
+  const int64_t K = p.K;
+  if (FMT == EPILORA_W_FP4) build_fold_table(tbl);
+
+  // ---- staging -------------------------------------------------------------
+  // FP8 operands go straight from memory to LDS (buffer loads with the lds
+  // bit): one wave instruction fills 8 rows of 128 bytes, lane i the 16 bytes
+  // at slot i % 8 of row i / 8, so lane i fetches chunk (i % 8) ^ (i / 8) of
+  // that row to realize the swizzle.  Out-of-range rows fall outside the
+  // buffer resource and read as zero; chunks past K get an out-of-range
+  // offset.  4-bit weights go through registers and the fold.
+  const int rows_a = (int)(p.M - m0 < BM ? p.M - m0 : BM);
+  const int rows_b = (int)(p.N - n0 < BN ? p.N - n0 : BN);
+  const auto rA = make_rsrc(p.xq + m0 * p.ldq, (uint32_t)((rows_a - 1) * p.ldq + K));
+  const auto rB = make_rsrc(p.wt.w + n0 * (FMT == EPILORA_W_FP8 ? K : K / 2),
+                            (uint32_t)(rows_b * (FMT == EPILORA_W_FP8 ? K : K / 2)));
+  const auto rS = make_rsrc(FMT == EPILORA_W_FP4 ? p.wt.bs + n0 * (K / 16) : p.wt.w,
+                            FMT == EPILORA_W_FP4 ? (uint32_t)(rows_b * (K / 16)) : 0u);
+  const int dma_row = lane >> 3, dma_chunk = (lane & 7) ^ (lane >> 3);
+  auto dma = [&](__amdgpu_buffer_rsrc_t rsrc, int64_t ld, int per_wave, uint8_t* dst, int kt) {
+    const uint32_t k = (uint32_t)kt * kStep + 16u * dma_chunk;
+#pragma unroll
+    for (int q = 0; q < per_wave; ++q) {
+      const int j = wave * per_wave + q;
+      const uint32_t off = (int64_t)k < K ? (uint32_t)((8 * j + dma_row) * ld) + k : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(dst + j * 1024), 16,
+                                               off, 0, 0, 0);
+    }
+  };
+  constexpr int QB4 = BN * 4 / kWideThreads;  // 4-bit: 32-code chunks per thread
+  uint4 rb[FMT == EPILORA_W_FP4 ? QB4 : 1];
+  uint32_t rs[FMT == EPILORA_W_FP4 ? QB4 : 1];
+  auto load_b4 = [&](int kt) {
+#pragma unroll
+    for (int q = 0; q < QB4; ++q) {
+      const int row = (tid >> 2) + (kWideThreads / 4) * q, c = tid & 3;
+      const uint32_t k = (uint32_t)kt * kStep + 32u * c;
+      const bool ok = (int64_t)k < K;
+      rb[q] = buf_load16<kCached>(rB, ok ? (uint32_t)(row * (K / 2)) + k / 2 : kOutOfRange);
+      rs[q] = buf_load2<kCached>(rS, ok ? (uint32_t)(row * (K / 16)) + k / 16 : kOutOfRange);
+    }
+  };
+  auto store_b4 = [&](uint8_t* b) {
+#pragma unroll
+    for (int q = 0; q < QB4; ++q) {
+      const int row = (tid >> 2) + (kWideThreads / 4) * q, c = tid & 3;
+      RawW raw;
+      raw.a = rb[q];
+      raw.b = zero4();
+      raw.s = rs[q];
+      const i32x8 f = w_frag<EPILORA_W_FP4>(raw, tbl);
+      *reinterpret_cast<uint4*>(b + swz8(row, 2 * c)) = make_uint4(f[0], f[1], f[2], f[3]);
+      *reinterpret_cast<uint4*>(b + swz8(row, 2 * c + 1)) = make_uint4(f[4], f[5], f[6], f[7]);
+    }
+  };
+  auto stage = [&](int kt, uint8_t* buf) {  // request step kt's operands into buf
+    dma(rA, p.ldq, BM / 32, buf, kt);
+    if (FMT == EPILORA_W_FP8) dma(rB, K, BN / 32, buf + BM * kStep, kt);
+    else load_b4(kt);
+  };
+  f32x4 acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Each step reads all of its fragments first and only then requests the
+  // next step's operands into the other buffer: a fragment read placed after
+  // that request would have to wait for it (the compiler cannot tell the two
+  // buffers apart here).  Lane l reads 32 bytes of row l % 16 at K offset
+  // 32 * (l / 16) of the step (chunks c0, c0 + 1) for both operands: the two
+  // see the same K positions.
+  const int c0 = (lane >> 4) * 2;
+  // The tile's token indices and mask bytes, requested now and used only by
+  // the epilogue (thread t holds token m0 + t).
+  int pre_a = -1, pre_m = 1;
+  if (p.z != nullptr && tid < BM && m0 + tid < p.M) {
+    pre_a = p.ad.idx[m0 + tid];
+    if (p.ad.mask != nullptr) pre_m = p.ad.mask[m0 + tid];
+  }
+  const int nk = (int)cdiv(K, kStep);
+  stage(0, buf0);
+  if (FMT == EPILORA_W_FP4) {
+    __syncthreads();  // the fold table is built
+    store_b4(buf0 + BM * kStep);
+  }
+  wait_all_memory();
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    uint8_t* cur = (kt & 1) ? buf1 : buf0;
+    uint8_t* nxt = (kt & 1) ? buf0 : buf1;
+    const uint8_t* a = cur;
+    const uint8_t* b = cur + BM * kStep;
+    i32x8 af[TM], bf[TN];
+#pragma unroll
+    for (int nb = 0; nb < TN; ++nb) {
+      const int row = wn * WN + nb * 16 + (lane & 15);
+      bf[nb] = as_i32x8(*reinterpret_cast<const uint4*>(b + swz8(row, c0)),
+                        *reinterpret_cast<const uint4*>(b + swz8(row, c0 + 1)));
+    }
+#pragma unroll
+    for (int tb = 0; tb < TM; ++tb) {
+      const int row = wm * WM + tb * 16 + (lane & 15);
+      af[tb] = as_i32x8(*reinterpret_cast<const uint4*>(a + swz8(row, c0)),
+                        *reinterpret_cast<const uint4*>(a + swz8(row, c0 + 1)));
+    }
+    if (kt + 1 < nk) stage(kt + 1, nxt);
+#pragma unroll
+    for (int tb = 0; tb < TM; ++tb)
+#pragma unroll
+      for (int nb = 0; nb < TN; ++nb) acc[tb][nb] = mfma_fp8_16x16x128(af[tb], bf[nb], acc[tb][nb]);
+    if (FMT == EPILORA_W_FP4 && kt + 1 < nk) store_b4(nxt + BM * kStep);
+    wait_all_memory();  // the next step's operands have landed in LDS
+    __syncthreads();
+  }
+
+  // ---- epilogue: scales --------------------------------------------------
+  // acc[tb][nb][v]: token m0 + wm*WM + tb*16 + 4*(lane/16) + v,
+  //                 output n0 + wn*WN + nb*16 + lane%16.
+  const int64_t tw0 = m0 + wm * WM, nw0 = n0 + wn * WN;
+  {
+    float wsc[TN];
+#pragma unroll
+    for (int nb = 0; nb < TN; ++nb) {
+      const int64_t n = nw0 + nb * 16 + (lane & 15);
+      wsc[nb] = n < p.N ? weight_scale<FMT>(p.wt, n) : 0.f;
+    }
+#pragma unroll
+    for (int tb = 0; tb < TM; ++tb)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t t = tw0 + tb * 16 + 4 * (lane >> 4) + v;
+        const float xs = t < p.M ? p.sx[t] : 0.f;
+#pragma unroll
+        for (int nb = 0; nb < TN; ++nb) acc[tb][nb][v] = (acc[tb][nb][v] * xs) * wsc[nb];
+      }
+  }
+
+  // ---- epilogue: adapters ------------------------------------------------
+  // z for the tile's tokens goes to LDS once, straight from memory (tokens
+  // [0, BM/2) in buf0, the rest in buf1, 512-byte fp32 rows whose 16-byte
+  // chunks are XOR-swizzled by (token % 16)), and is rounded to bf16.
+  if (p.z != nullptr) {
+    const int r = p.ad.r;
+    {
+      const auto rZ = make_rsrc(p.z + m0 * r, (uint32_t)(rows_a * r * 4));
+#pragma unroll
+      for (int q = 0; q < BM / 8; ++q) {
+        const int j = wave * (BM / 8) + q;  // 2 rows of 512 bytes per wave instruction
+        const int row = 2 * j + (lane >> 5), c = (lane & 31) ^ (row & 15);
+        const uint32_t off = 16 * c < 4 * r ? (uint32_t)((row * r) * 4 + 16 * c) : kOutOfRange;
+        uint8_t* dst = j < BM / 4 ? buf0 + j * 1024 : buf1 + (j - BM / 4) * 1024;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rZ, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
+      }
+    }
+    // Resolve the tile's tokens (index and mask were loaded before the main
+    // loop), then list the distinct adapters in order of first appearance: a
+    // token starting a run of equal adapters is listed unless an earlier
+    // token has its adapter (checked 64 tokens at a time by the wave), and a
+    // wave-level prefix count places it.
+    if (tid < BM) {
+      int a = -1, rk = 0;
+      if (m0 + tid < p.M) {
+        a = pre_a;
+        if (a < -1 || a >= p.ad.L) {
+          if (n0 == 0) atomic_or_relaxed(p.ctrl + kCtrlError, EPILORA_DEV_BAD_INDEX);
+          a = -1;
+        }
+        if (a >= 0 && pre_m == 0) a = -1;
+        if (a >= 0) {
+          rk = p.ad.ranks != nullptr ? p.ad.ranks[a] : r;
+          rk = rk < r ? rk : r;
+          if (rk <= 0) a = -1, rk = 0;
+        }
+      }
+      tok[tid] = TokenSlot{a, rk};
+    }
+    __syncthreads();
+    bool first = false;
+    {
+      const int my_a = tid < BM ? tok[tid].a : -1;
+      const bool start = my_a >= 0 && (tid == 0 || tok[tid - 1].a != my_a);
+      uint64_t cand = __ballot(start);
+      while (cand) {
+        const int l = __ffsll((unsigned long long)cand) - 1;
+        cand &= cand - 1;
+        const int t = wave * 64 + l;
+        const int ac = __shfl(my_a, l);
+        bool dup = false;
+        for (int u0 = 0; u0 < t && !dup; u0 += 64) {
+          const int u = u0 + lane;
+          dup = __ballot(u < t && tok[u].a == ac) != 0;
+        }
+        if (lane == l) first = !dup;
+      }
+    }
+    const uint64_t fb = __ballot(first);
+    if (lane == 0) counts[wave] = __popcll(fb);
+    __syncthreads();
+    int base = 0;
+    for (int w = 0; w < wave; ++w) base += counts[w];
+    if (first) groups[base + __popcll(fb & ((1ull << lane) - 1))] = tid;  // the group's first token
+    int ngroups = 0;
+    for (int w = 0; w < kWideThreads / 64; ++w) ngroups += counts[w];
+    wait_all_memory();  // z (fp32) has landed
+    __syncthreads();
+    // z to bf16 (nearest even) in buf0: 256-byte rows (128 ranks), 16-byte
+    // chunks swizzled by (token % 16).  The first half's fp32 rows share
+    // buf0 with the bf16 rows, so all of them are read before any is written.
+    {
+      constexpr int H = BM / 2;
+      constexpr int IT = H * 16 / kWideThreads;  // bf16 chunks per thread per half
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint8_t* src = h ? buf1 : buf0;
+        uint4 cv[IT];
+#pragma unroll
+        for (int i = 0; i < IT; ++i) {
+          const int e = tid + i * kWideThreads;
+          const int t = e >> 4, cb = e & 15;  // token within the half, bf16 chunk
+          const float4 f0 = *reinterpret_cast<const float4*>(src + t * 512 + (((2 * cb) ^ (t & 15)) << 4));
+          const float4 f1 = *reinterpret_cast<const float4*>(src + t * 512 + (((2 * cb + 1) ^ (t & 15)) << 4));
+          cv[i] = make_uint4(f32_to_bf16(f0.x) | (f32_to_bf16(f0.y) << 16), f32_to_bf16(f0.z) | (f32_to_bf16(f0.w) << 16),
+                             f32_to_bf16(f1.x) | (f32_to_bf16(f1.y) << 16), f32_to_bf16(f1.z) | (f32_to_bf16(f1.w) << 16));
+        }
+        if (h == 0) __syncthreads();
+#pragma unroll
+        for (int i = 0; i < IT; ++i) {
+          const int e = tid + i * kWideThreads;
+          const int t = h * H + (e >> 4), cb = e & 15;
+          *reinterpret_cast<uint4*>(buf0 + t * 256 + ((cb ^ (t & 15)) << 4)) = cv[i];
+        }
+      }
+      __syncthreads();
+    }
+
+    // The adapters' B rows, PB output blocks of each wave at a time (a
+    // "unit": 128 rows of 256 bytes, 64 per half of the tile's outputs), go
+    // to one of two 32 KB slots in buf1 straight from memory; the next unit
+    // is requested once this unit's fragments are in registers, so it lands
+    // while this one is multiplied (z comes from buf0, a separate object, so
+    // those reads need not wait for it).
+    constexpr int PB = TN < 4 ? TN : 4;
+    constexpr int NPASS = TN / PB;
+    const int units = ngroups * NPASS;
+    auto b_dma = [&](int u, int slot) {
+      const TokenSlot lead = tok[groups[u / NPASS]];
+      const int pb = (u % NPASS) * PB;
+      const auto rBa = make_rsrc(p.ad.B + (int64_t)lead.a * p.N * r, (uint32_t)(p.N * r * 2));
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int j = wave * 8 + q;  // 4 rows of 256 bytes per wave instruction
+        const int R = 4 * j + (lane >> 4), c = (lane & 15) ^ (R & 15);
+        const int64_t n = n0 + (R >> 6) * WN + pb * 16 + (R & 63);
+        const uint32_t off = 8 * c < lead.rank ? (uint32_t)((n * r + 8 * c) * 2) : kOutOfRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rBa, (__attribute__((address_space(3))) void*)(buf1 + slot * 32768 + j * 1024), 16, off, 0, 0, 0);
+      }
+    };
+    if (units > 0) b_dma(0, 0);
+    for (int gi = 0; gi < ngroups; ++gi)
+#pragma unroll
+    for (int pass = 0; pass < NPASS; ++pass) {  // static, so acc is indexed statically
+      const int u = gi * NPASS + pass;
+      const int pb = pass * PB;
+      wait_all_memory();  // unit u has landed
+      __syncthreads();    // ... for every wave, and unit u - 1's slot is free
+      const TokenSlot lead = tok[groups[gi]];
+      const int a = lead.a, rank = lead.rank;
+      const int nch = (rank + 31) / 32;  // 32-rank chunks
+      uint8_t* slot = buf1 + (u & 1) * 32768;
+      if (rank & 7) {  // clear the ranks past the adapter's rank in its partial chunk
+        const int cp = rank >> 3;
+        for (int R = tid; R < 128; R += kWideThreads) {
+          uint16_t* q = reinterpret_cast<uint16_t*>(slot + R * 256 + ((cp ^ (R & 15)) << 4));
+          for (int e = rank & 7; e < 8; ++e) q[e] = 0;
+        }
+        __syncthreads();
+      }
+      uint4 bfr[PB][4];
+#pragma unroll
+      for (int i = 0; i < PB; ++i) {
+        const int R = wn * 64 + i * 16 + (lane & 15);
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc)
+          bfr[i][kc] = kc < nch ? *reinterpret_cast<const uint4*>(slot + R * 256 + (((kc * 4 + (lane >> 4)) ^ (R & 15)) << 4))
+                                : zero4();
+      }
+      if (u + 1 < units) b_dma(u + 1, (u + 1) & 1);
+#pragma unroll
+      for (int tb = 0; tb < TM; ++tb) {
+        const int tt = wm * WM + tb * 16 + (lane & 15);
+        const bool mem = tok[tt].a == a;
+        if (__ballot(mem) == 0) continue;
+        const uint8_t* zrow = buf0 + tt * 256;
+        f32x4 lacc[PB];
+#pragma unroll
+        for (int i = 0; i < PB; ++i) lacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kc = 0; kc < 4; ++kc) {
+          if (kc >= nch) break;
+          const int j0 = kc * 32 + (lane >> 4) * 8;
+          uint4 zq = *reinterpret_cast<const uint4*>(zrow + (((kc * 4 + (lane >> 4)) ^ (tt & 15)) << 4));
+          if (!mem || j0 >= rank) {
+            zq = zero4();
+          } else if (j0 + 8 > rank) {
+            uint32_t w[4] = {zq.x, zq.y, zq.z, zq.w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              if (j0 + e >= rank) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+            zq = make_uint4(w[0], w[1], w[2], w[3]);
+          }
+          const bf16x8 zf = as_bf16x8(zq);
+#pragma unroll
+          for (int i = 0; i < PB; ++i) lacc[i] = mfma_bf16_16x16x32(zf, as_bf16x8(bfr[i][kc]), lacc[i]);
+        }
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int tr = wm * WM + tb * 16 + 4 * (lane >> 4) + v;
+          if (tok[tr].a == a) {
+#pragma unroll
+            for (int i = 0; i < PB; ++i) acc[tb][pb + i][v] = acc[tb][pb + i][v] + p.ad.scale * lacc[i][v];
+          }
+        }
+      }
+    }
+    __syncthreads();  // z is read for the last time; the store below reuses the buffers
+  }
+
+  // ---- store: each wave's bf16 quarter through LDS as 16-byte row chunks --
+  uint16_t* sy = reinterpret_cast<uint16_t*>(wave < 2 ? buf0 : buf1) + (wave & 1) * (WM * WN);
+#pragma unroll
+  for (int tb = 0; tb < TM; ++tb)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = tb * 16 + 4 * (lane >> 4) + v;
+#pragma unroll
+      for (int nb = 0; nb < TN; ++nb) sy[row * WN + nb * 16 + (lane & 15)] = (uint16_t)f32_to_bf16(acc[tb][nb][v]);
+    }
+  __syncthreads();
+  const bool vec = (((uintptr_t)p.y | (uintptr_t)(p.ldy * 2)) & 15) == 0;
+  constexpr int CPR = WN / 8;  // 16-byte chunks per row of the quarter
+  for (int e = lane; e < WM * CPR; e += 64) {
+    const int row = e / CPR, c = e % CPR;
+    const int64_t t = tw0 + row, n = nw0 + c * 8;
+    if (t >= p.M || n >= p.N) continue;
+    const uint4 v = *reinterpret_cast<const uint4*>(sy + row * WN + c * 8);
+    uint16_t* dst = p.y + t * p.ldy + n;
+    if (vec && n + 8 <= p.N) {
+      *reinterpret_cast<uint4*>(dst) = v;
+    } else {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      for (int q = 0; q < 8 && n + q < p.N; ++q) dst[q] = (uint16_t)(w[q >> 1] >> (16 * (q & 1)));
+    }
+  }
+}
+
+template <int FMT, int BM, int BN>
+static void launch_wide(const GemmParams& p, hipStream_t stream) {
+  const int tm = (int)cdiv(p.M, BM), tn = (int)cdiv(p.N, BN);
+  hipLaunchKernelGGL((gemm_wide_kernel<FMT, BM, BN>), dim3(tm * tn), dim3(kWideThreads), 0, stream, p, tm, tn);
+}
+
+// Tile shape: the largest tile that still gives every compute unit a tile
+// in the first round.
+template <int FMT>
+static void dispatch_wide(const GemmParams& p, hipStream_t stream) {
+  const int64_t cus = 256;
+  if (cdiv(p.M, 256) * cdiv(p.N, 256) >= cus) launch_wide<FMT, 256, 256>(p, stream);
+  else if (cdiv(p.M, 256) * cdiv(p.N, 128) >= cus) launch_wide<FMT, 256, 128>(p, stream);
+  else launch_wide<FMT, 128, 128>(p, stream);
+}
+
+void launch_gemm_wide(const GemmParams& p, hipStream_t stream) {
+  if (p.wt.fmt == EPILORA_W_FP8) dispatch_wide<EPILORA_W_FP8>(p, stream);
+  else dispatch_wide<EPILORA_W_FP4>(p, stream);
+}
+
+}  // namespace epilora
