@@ -181,19 +181,26 @@ def time_graph(g, rounds, warmup):
 
 
 def per_step_us(projs, fn_names, steps, warmup):
-    """Microseconds per step: one graph per weight copy (a step = fn_names
-    over projs), replayed in turn; `warmup` untimed steps, then exactly
-    `steps` timed ones between two synchronizations, timed with events on
-    the stream the graphs replay on."""
+    """Microseconds per step (a step = fn_names over projs, on one weight
+    copy): `warmup` untimed steps, then exactly `steps` timed ones between
+    two synchronizations, timed with events on the stream the graphs replay
+    on.  Steps run from one graph that holds a step on each weight copy in
+    turn; a remainder of steps % copies runs from one-step graphs."""
     fns = [getattr(p, n) for p in projs for n in fn_names]
-    graphs = [graph_of(fns, ROTATE, only=c) for c in range(ROTATE)]
-    for i in range(warmup):
-        graphs[i % ROTATE].replay()
+    full = graph_of(fns, ROTATE)
+    single = [graph_of(fns, ROTATE, only=c) for c in range(ROTATE)]
+
+    def run(n):
+        for _ in range(n // ROTATE):
+            full.replay()
+        for c in range(n % ROTATE):
+            single[c].replay()
+
+    run(warmup)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
-    for i in range(steps):
-        graphs[i % ROTATE].replay()
+    run(steps)
     e1.record()
     torch.cuda.synchronize()
     return 1000.0 * e0.elapsed_time(e1) / steps, steps
