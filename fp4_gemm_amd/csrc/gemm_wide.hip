@@ -132,12 +132,17 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(GemmParams p, i
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // Each step reads all of its fragments first and only then requests the
-  // next step's operands into the other buffer: a fragment read placed after
-  // that request would have to wait for it (the compiler cannot tell the two
-  // buffers apart here).  Lane l reads 32 bytes of row l % 16 at K offset
-  // 32 * (l / 16) of the step (chunks c0, c0 + 1) for both operands: the two
-  // see the same K positions.
+  // Software pipeline over K steps, two operand buffers: while step k is
+  // multiplied from registers, step k+1's fragments are read from the other
+  // buffer and step k+2's operands stream into the buffer step k came from.
+  // One barrier per step: it makes step k+1's operands visible and frees the
+  // buffer of step k (whose fragments every wave has already read).  The loop
+  // body is unrolled twice so that each buffer's role is fixed in the code
+  // (the compiler then sees that the fragment reads never alias the incoming
+  // operands and does not wait for them); an odd step count is padded with
+  // a zero step.  Lane l reads 32 bytes of row l % 16 at K offset 32 * (l / 16)
+  // of a step (chunks c0, c0 + 1) for both operands: the two see the same K
+  // positions.
   const int c0 = (lane >> 4) * 2;
   // The tile's token indices and mask bytes, requested now and used only by
   // the epilogue (thread t holds token m0 + t).
@@ -147,40 +152,74 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(GemmParams p, i
     if (p.ad.mask != nullptr) pre_m = p.ad.mask[m0 + tid];
   }
   const int nk = (int)cdiv(K, kStep);
-  stage(0, buf0);
-  if (FMT == EPILORA_W_FP4) {
-    __syncthreads();  // the fold table is built
-    store_b4(buf0 + BM * kStep);
-  }
-  wait_all_memory();
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    uint8_t* cur = (kt & 1) ? buf1 : buf0;
-    uint8_t* nxt = (kt & 1) ? buf0 : buf1;
-    const uint8_t* a = cur;
-    const uint8_t* b = cur + BM * kStep;
-    i32x8 af[TM], bf[TN];
+  const int nk2 = nk + (nk & 1);
+  i32x8 af[TM], bf[TN];
+  auto read_frags = [&](const uint8_t* buf, i32x8 (&fa)[TM], i32x8 (&fb)[TN]) {
+    const uint8_t* a = buf;
+    const uint8_t* b = buf + BM * kStep;
 #pragma unroll
     for (int nb = 0; nb < TN; ++nb) {
       const int row = wn * WN + nb * 16 + (lane & 15);
-      bf[nb] = as_i32x8(*reinterpret_cast<const uint4*>(b + swz8(row, c0)),
+      fb[nb] = as_i32x8(*reinterpret_cast<const uint4*>(b + swz8(row, c0)),
                         *reinterpret_cast<const uint4*>(b + swz8(row, c0 + 1)));
     }
 #pragma unroll
     for (int tb = 0; tb < TM; ++tb) {
       const int row = wm * WM + tb * 16 + (lane & 15);
-      af[tb] = as_i32x8(*reinterpret_cast<const uint4*>(a + swz8(row, c0)),
+      fa[tb] = as_i32x8(*reinterpret_cast<const uint4*>(a + swz8(row, c0)),
                         *reinterpret_cast<const uint4*>(a + swz8(row, c0 + 1)));
     }
-    if (kt + 1 < nk) stage(kt + 1, nxt);
+  };
+  // Step k from registers, step k+1's fragments from `next` (when there is a
+  // step k+1), step k+2's operands into `self` (when there is one).
+  auto step = [&](int k, uint8_t* self, const uint8_t* next) {
+    wait_all_memory();  // step k+1's operands have landed
+    __syncthreads();
+    // Step k+2's requests, then the step's MFMAs with step k+1's A fragments
+    // read as each block's registers free up and its B fragments at the end.
+    // (At the last step the fragment reads fetch whatever the other buffer
+    // holds; they are never used.)
+    if (k + 2 < nk2) stage(k + 2, self);
+    const uint8_t* na = next;
+    const uint8_t* nbp = next + BM * kStep;
 #pragma unroll
-    for (int tb = 0; tb < TM; ++tb)
+    for (int tb = 0; tb < TM; ++tb) {
 #pragma unroll
       for (int nb = 0; nb < TN; ++nb) acc[tb][nb] = mfma_fp8_16x16x128(af[tb], bf[nb], acc[tb][nb]);
-    if (FMT == EPILORA_W_FP4 && kt + 1 < nk) store_b4(nxt + BM * kStep);
-    wait_all_memory();  // the next step's operands have landed in LDS
-    __syncthreads();
+      const int row = wm * WM + tb * 16 + (lane & 15);
+      af[tb] = as_i32x8(*reinterpret_cast<const uint4*>(na + swz8(row, c0)),
+                        *reinterpret_cast<const uint4*>(na + swz8(row, c0 + 1)));
+    }
+    i32x8 bn[TN];
+#pragma unroll
+    for (int nb = 0; nb < TN; ++nb) {
+      const int row = wn * WN + nb * 16 + (lane & 15);
+      bn[nb] = as_i32x8(*reinterpret_cast<const uint4*>(nbp + swz8(row, c0)),
+                        *reinterpret_cast<const uint4*>(nbp + swz8(row, c0 + 1)));
+    }
+#pragma unroll
+    for (int nb = 0; nb < TN; ++nb) bf[nb] = bn[nb];
+    if (FMT == EPILORA_W_FP4 && k + 2 < nk2) store_b4(self + BM * kStep);
+  };
+
+  stage(0, buf0);
+  if (FMT == EPILORA_W_FP4) {
+    __syncthreads();  // the fold table is built
+    store_b4(buf0 + BM * kStep);
   }
+  if (nk2 > 1) {
+    stage(1, buf1);
+    if (FMT == EPILORA_W_FP4) store_b4(buf1 + BM * kStep);
+  }
+  wait_all_memory();
+  __syncthreads();
+  read_frags(buf0, af, bf);
+  for (int kt = 0; kt < nk2; kt += 2) {
+    step(kt, buf0, buf1);
+    step(kt + 1, buf1, buf0);
+  }
+  wait_all_memory();
+  __syncthreads();  // every wave is done with the operand buffers
 
   // ---- epilogue: scales --------------------------------------------------
   // acc[tb][nb][v]: token m0 + wm*WM + tb*16 + 4*(lane/16) + v,
@@ -434,8 +473,7 @@ static void launch_wide(const GemmParams& p, hipStream_t stream) {
 template <int FMT>
 static void dispatch_wide(const GemmParams& p, hipStream_t stream) {
   const int64_t cus = 256;
-  if (cdiv(p.M, 256) * cdiv(p.N, 256) >= cus) launch_wide<FMT, 256, 256>(p, stream);
-  else if (cdiv(p.M, 256) * cdiv(p.N, 128) >= cus) launch_wide<FMT, 256, 128>(p, stream);
+  if (cdiv(p.M, 256) * cdiv(p.N, 128) >= cus) launch_wide<FMT, 256, 128>(p, stream);
   else launch_wide<FMT, 128, 128>(p, stream);
 }
 
