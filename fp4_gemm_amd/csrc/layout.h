@@ -35,16 +35,32 @@ constexpr size_t kTileCounterOffset = kDoneOffset + (size_t)kDoneGroups * kDoneS
 constexpr size_t kStateBytes = align256(kTileCounterOffset + 4 * (size_t)kMaxShrinkTiles);
 
 // ---- shrink -----------------------------------------------------------------
-// A workgroup covers 16 consecutive tokens and a range of 128-wide K steps;
-// the K range is split over `splits` workgroups whose partial sums are
-// combined in a fixed order by the last one to finish.  Splits give the chip
-// about 1024 workgroups, but no fewer than one (step, rank block) pair per
-// wave of a 4-wave workgroup.
+// A workgroup covers 16 consecutive tokens (64 for prefill batches, see
+// below) and a range of 128-wide K steps; the K range is split over `splits`
+// workgroups whose partial sums are combined in a fixed order by the last one
+// to finish.  For 16-token tiles, splits give the chip about 1024 workgroups,
+// but no fewer than one (step, rank block) pair per wave of a 4-wave
+// workgroup; for 64-token tiles about 512, with at least two steps each (the
+// next step's adapter rows load while the current one is multiplied).
 constexpr int kShrinkTokens = 16;
 constexpr int kShrinkStep = 128;
 
+// Batches of more than kShrinkWideM tokens (prefill) take tiles of
+// kShrinkWideTokens tokens whose adapter rows are shared through LDS.
+constexpr int kShrinkWideM = 64;
+constexpr int kShrinkWideTokens = 64;
+inline int shrink_tokens(int64_t M) { return M > kShrinkWideM ? kShrinkWideTokens : kShrinkTokens; }
+
 inline int shrink_splits(int64_t M, int64_t K, int32_t r) {
   const int64_t steps = cdiv(K, kShrinkStep);
+  if (M > kShrinkWideM) {  // about 512 workgroups, at least two steps each
+    const int64_t tiles = cdiv(M, kShrinkWideTokens);
+    int64_t s = cdiv(512, tiles);
+    const int64_t two = cdiv(steps, 2);
+    if (s > two) s = two;
+    if (s < 1) s = 1;
+    return (int)s;
+  }
   const int64_t tiles = cdiv(M, kShrinkTokens);
   const int64_t jb = r > 16 ? r / 16 : 1;
   int64_t s = steps;

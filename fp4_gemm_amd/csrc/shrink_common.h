@@ -118,18 +118,18 @@ __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int64_t t0, i
   __syncthreads();
 }
 
-// Write this workgroup's [16][r] sums (in LDS `red`) to z, or to its split's
+// Write this workgroup's [TT][r] sums (in LDS `red`) to z, or to its split's
 // partial; the last split of a tile adds the partials in a fixed order.  z and
 // the partials are written and read device-coherently, so another workgroup
 // of the same grid may read z once the caller has published it.  Returns
 // true in the workgroup that wrote the tile's final z, after every one of
 // its z stores has completed.
-template <int NW>
+template <int NW, int TT = kShrinkTokens>
 __device__ __forceinline__ bool shrink_finish(const ShrinkParams& p, int tile, int split, float* red) {
   __shared__ int last;
-  const int64_t t0 = (int64_t)tile * kShrinkTokens;
+  const int64_t t0 = (int64_t)tile * TT;
   const int r = p.ad.r;
-  const int64_t rows = p.M - t0 < 16 ? p.M - t0 : 16;
+  const int64_t rows = p.M - t0 < TT ? p.M - t0 : TT;
   const uint32_t tile_bytes = (uint32_t)(rows * r * 4);
   const auto zr = make_rsrc(p.z + t0 * r, tile_bytes);
   if (p.splits == 1) {
@@ -161,15 +161,26 @@ __device__ __forceinline__ bool shrink_finish(const ShrinkParams& p, int tile, i
   for (int item = threadIdx.x; item < quads * chunks; item += NW * kWave) {
     const int q = item % quads, c = item / quads;
     const int s0 = c * per, s1 = min(p.splits, s0 + per);
+    // Loads of up to 8 splits are in flight together; they are added in
+    // split order all the same.
     float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int s = s0; s < s1; ++s) {
-      const auto ps = make_rsrc(p.partials + ((int64_t)s * p.M + t0) * r, tile_bytes);
-      const uint4 u = buf_load16<kCoherent>(ps, 16u * q);
+    auto add = [&](uint4 u) {
       v.x += __uint_as_float(u.x);
       v.y += __uint_as_float(u.y);
       v.z += __uint_as_float(u.z);
       v.w += __uint_as_float(u.w);
+    };
+    int s = s0;
+    for (; s + 8 <= s1; s += 8) {
+      uint4 u[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        u[j] = buf_load16<kCoherent>(make_rsrc(p.partials + ((int64_t)(s + j) * p.M + t0) * r, tile_bytes), 16u * q);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) add(u[j]);
     }
+    for (; s < s1; ++s)
+      add(buf_load16<kCoherent>(make_rsrc(p.partials + ((int64_t)s * p.M + t0) * r, tile_bytes), 16u * q));
     *reinterpret_cast<float4*>(&sums[4 * item]) = v;
   }
   __syncthreads();

@@ -125,6 +125,11 @@ SHRINK_CASES = [
     (33, 4224, 6, 32, "mixed", False, True),
     (100, 512, 3, 128, "sorted", True, True),
     (16, 14336, 64, 64, "distinct", False, False),
+    # prefill batches: 64-token tiles, ragged token and K tails, many splits
+    (65, 256, 2, 16, "mixed", False, False),
+    (300, 4112, 8, 128, "mixed", True, True),
+    (517, 14336, 16, 16, "mixed", True, False),
+    (2048, 4096, 32, 64, "sorted", False, True),
 ]
 
 
