@@ -208,6 +208,27 @@ __device__ __forceinline__ i32x8 cat8(const u32x4& lo, const u32x4& hi) {
 // Wait until every memory access this wave issued has completed.
 __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
 
+// Wait until at most N vector-memory operations of this wave are still
+// outstanding (they complete in issue order) and every LDS operation has
+// completed.  s_waitcnt fields: vmcnt bits [3:0] and [15:14], expcnt [6:4]
+// (7: no wait), lgkmcnt [11:8] (0: wait for all).
+template <int N>
+__device__ __forceinline__ void wait_vm_keep() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// Workgroup barrier without the memory fence of __syncthreads (which waits
+// for every outstanding memory operation, loads into LDS included).  LDS
+// accesses are ordered by it as long as each wave has waited for its own
+// (lgkmcnt, and vmcnt for loads into LDS) before it; the empty asm keeps the
+// compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------
 // Agent-scope counters and flags (visible across the chip's XCDs)
 // ---------------------------------------------------------------------------

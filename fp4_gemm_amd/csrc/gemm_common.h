@@ -91,5 +91,9 @@ struct TokenSlot {
 
 // The prefill GEMM (M > 64), gemm_wide.hip.
 void launch_gemm_wide(const GemmParams& p, hipStream_t stream);
+// The prefill GEMM with 256 x 256 tiles, gemm_big.hip, for shapes that
+// gemm_big_fits accepts.
+bool gemm_big_fits(const GemmParams& p);
+void launch_gemm_big(const GemmParams& p, hipStream_t stream);
 
 }  // namespace epilora

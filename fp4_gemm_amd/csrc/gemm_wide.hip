@@ -45,18 +45,19 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(GemmParams p, i
   // the loads filling one never alias the reads of the other (and does not
   // wait for them before those reads).  Each holds A ([BM][128]) then B
   // ([BN][128]).
-  // The epilogue reuses them: z (half the tile's tokens each, 512-byte rows,
-  // so at least BM / 2 x 512 bytes) and two 32 KB slots of B rows in buf1.
+  // The epilogue reuses them: bf16 z rows (256 bytes per token) in buf0 and
+  // two 32 KB slots of B rows in buf1.
   constexpr int kOps = (BM + BN) * kStep;
   constexpr int kBuf0 = kOps > BM * 256 ? kOps : BM * 256;
   constexpr int kBuf = kBuf0 > 2 * 32768 ? kBuf0 : 2 * 32768;
-  static_assert(BM / 2 * 512 <= kBuf && 2 * 32768 <= kBuf && BM * 256 <= kBuf, "epilogue LDS regions");
+  static_assert(2 * 32768 <= kBuf && BM * 256 <= kBuf, "epilogue LDS regions");
   __shared__ __align__(16) uint8_t buf0[kBuf];
   __shared__ __align__(16) uint8_t buf1[kBuf];
   __shared__ uint2 tbl[FMT == EPILORA_W_FP4 ? 256 : 1];
   __shared__ TokenSlot tok[BM];
   __shared__ int groups[BM];  // the first token of each distinct adapter
   __shared__ int counts[kWideThreads / 64];
+  __shared__ float s_xs[BM], s_ws[BN];  // the tile's token and output scales
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 1, wn = wave >> 1;
@@ -202,6 +203,10 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(GemmParams p, i
     if (FMT == EPILORA_W_FP4 && k + 2 < nk2) store_b4(self + BM * kStep);
   };
 
+  // The tile's scales, requested now and put in LDS with the first operands.
+  float pre_xs = 0.f, pre_ws = 0.f;
+  if (tid < BM && m0 + tid < p.M) pre_xs = p.sx[m0 + tid];
+  if (tid < BN && n0 + tid < p.N) pre_ws = weight_scale<FMT>(p.wt, n0 + tid);
   stage(0, buf0);
   if (FMT == EPILORA_W_FP4) {
     __syncthreads();  // the fold table is built
@@ -212,6 +217,8 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(GemmParams p, i
     if (FMT == EPILORA_W_FP4) store_b4(buf1 + BM * kStep);
   }
   wait_all_memory();
+  if (tid < BM) s_xs[tid] = pre_xs;
+  if (tid < BN) s_ws[tid] = pre_ws;
   __syncthreads();
   read_frags(buf0, af, bf);
   for (int kt = 0; kt < nk2; kt += 2) {
@@ -228,38 +235,50 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(GemmParams p, i
   {
     float wsc[TN];
 #pragma unroll
-    for (int nb = 0; nb < TN; ++nb) {
-      const int64_t n = nw0 + nb * 16 + (lane & 15);
-      wsc[nb] = n < p.N ? weight_scale<FMT>(p.wt, n) : 0.f;
-    }
+    for (int nb = 0; nb < TN; ++nb) wsc[nb] = s_ws[wn * WN + nb * 16 + (lane & 15)];
 #pragma unroll
     for (int tb = 0; tb < TM; ++tb)
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
-        const int64_t t = tw0 + tb * 16 + 4 * (lane >> 4) + v;
-        const float xs = t < p.M ? p.sx[t] : 0.f;
+        const float xs = s_xs[wm * WM + tb * 16 + 4 * (lane >> 4) + v];
 #pragma unroll
         for (int nb = 0; nb < TN; ++nb) acc[tb][nb][v] = (acc[tb][nb][v] * xs) * wsc[nb];
       }
   }
 
   // ---- epilogue: adapters ------------------------------------------------
-  // z for the tile's tokens goes to LDS once, straight from memory (tokens
-  // [0, BM/2) in buf0, the rest in buf1, 512-byte fp32 rows whose 16-byte
-  // chunks are XOR-swizzled by (token % 16)), and is rounded to bf16.
+  // z rows of the tile's tokens are requested into registers first (their
+  // latency then overlaps the token bookkeeping and the first adapter's B
+  // request), then rounded to bf16 (nearest even) into buf0: 256-byte rows
+  // (128 ranks), 16-byte chunks swizzled by (token % 16).
   if (p.z != nullptr) {
     const int r = p.ad.r;
-    {
-      const auto rZ = make_rsrc(p.z + m0 * r, (uint32_t)(rows_a * r * 4));
+    constexpr int ZIT = BM * 16 / kWideThreads;  // bf16 chunks (8 ranks) per thread
+    constexpr int ZB = ZIT;                      // chunks in flight: all
+    float4 zf[ZB][2];
+    auto z_load = [&](int i0) {
 #pragma unroll
-      for (int q = 0; q < BM / 8; ++q) {
-        const int j = wave * (BM / 8) + q;  // 2 rows of 512 bytes per wave instruction
-        const int row = 2 * j + (lane >> 5), c = (lane & 31) ^ (row & 15);
-        const uint32_t off = 16 * c < 4 * r ? (uint32_t)((row * r) * 4 + 16 * c) : kOutOfRange;
-        uint8_t* dst = j < BM / 4 ? buf0 + j * 1024 : buf1 + (j - BM / 4) * 1024;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rZ, (__attribute__((address_space(3))) void*)dst, 16, off, 0, 0, 0);
+      for (int i = 0; i < ZB; ++i) {
+        const int e = tid + (i0 + i) * kWideThreads;
+        const int t = e >> 4, cb = e & 15;
+        const bool ok = m0 + t < p.M && 8 * cb < r;
+        const float4* src = reinterpret_cast<const float4*>(p.z + (m0 + t) * r + 8 * cb);
+        zf[i][0] = ok ? src[0] : make_float4(0.f, 0.f, 0.f, 0.f);
+        zf[i][1] = ok ? src[1] : make_float4(0.f, 0.f, 0.f, 0.f);
       }
-    }
+    };
+    auto z_store = [&](int i0) {
+#pragma unroll
+      for (int i = 0; i < ZB; ++i) {
+        const int e = tid + (i0 + i) * kWideThreads;
+        const int t = e >> 4, cb = e & 15;
+        const float4 f0 = zf[i][0], f1 = zf[i][1];
+        *reinterpret_cast<uint4*>(buf0 + t * 256 + ((cb ^ (t & 15)) << 4)) =
+            make_uint4(f32_to_bf16(f0.x) | (f32_to_bf16(f0.y) << 16), f32_to_bf16(f0.z) | (f32_to_bf16(f0.w) << 16),
+                       f32_to_bf16(f1.x) | (f32_to_bf16(f1.y) << 16), f32_to_bf16(f1.z) | (f32_to_bf16(f1.w) << 16));
+      }
+    };
+    z_load(0);
     // Resolve the tile's tokens (index and mask were loaded before the main
     // loop), then list the distinct adapters in order of first appearance: a
     // token starting a run of equal adapters is listed unless an earlier
@@ -309,44 +328,15 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(GemmParams p, i
     if (first) groups[base + __popcll(fb & ((1ull << lane) - 1))] = tid;  // the group's first token
     int ngroups = 0;
     for (int w = 0; w < kWideThreads / 64; ++w) ngroups += counts[w];
-    wait_all_memory();  // z (fp32) has landed
-    __syncthreads();
-    // z to bf16 (nearest even) in buf0: 256-byte rows (128 ranks), 16-byte
-    // chunks swizzled by (token % 16).  The first half's fp32 rows share
-    // buf0 with the bf16 rows, so all of them are read before any is written.
-    {
-      constexpr int H = BM / 2;
-      constexpr int IT = H * 16 / kWideThreads;  // bf16 chunks per thread per half
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint8_t* src = h ? buf1 : buf0;
-        uint4 cv[IT];
-#pragma unroll
-        for (int i = 0; i < IT; ++i) {
-          const int e = tid + i * kWideThreads;
-          const int t = e >> 4, cb = e & 15;  // token within the half, bf16 chunk
-          const float4 f0 = *reinterpret_cast<const float4*>(src + t * 512 + (((2 * cb) ^ (t & 15)) << 4));
-          const float4 f1 = *reinterpret_cast<const float4*>(src + t * 512 + (((2 * cb + 1) ^ (t & 15)) << 4));
-          cv[i] = make_uint4(f32_to_bf16(f0.x) | (f32_to_bf16(f0.y) << 16), f32_to_bf16(f0.z) | (f32_to_bf16(f0.w) << 16),
-                             f32_to_bf16(f1.x) | (f32_to_bf16(f1.y) << 16), f32_to_bf16(f1.z) | (f32_to_bf16(f1.w) << 16));
-        }
-        if (h == 0) __syncthreads();
-#pragma unroll
-        for (int i = 0; i < IT; ++i) {
-          const int e = tid + i * kWideThreads;
-          const int t = h * H + (e >> 4), cb = e & 15;
-          *reinterpret_cast<uint4*>(buf0 + t * 256 + ((cb ^ (t & 15)) << 4)) = cv[i];
-        }
-      }
-      __syncthreads();
-    }
-
+    wait_vm_keep<63>();  // the group list is written (z may still be loading)
+    lds_barrier();
     // The adapters' B rows, PB output blocks of each wave at a time (a
     // "unit": 128 rows of 256 bytes, 64 per half of the tile's outputs), go
-    // to one of two 32 KB slots in buf1 straight from memory; the next unit
-    // is requested once this unit's fragments are in registers, so it lands
-    // while this one is multiplied (z comes from buf0, a separate object, so
-    // those reads need not wait for it).
+    // to one of two 32 KB slots in buf1 straight from memory; the first unit
+    // is requested before z is written to LDS, and each next unit once this
+    // unit's fragments are in registers, so it lands while this one is
+    // multiplied (z comes from buf0, a separate object, so those accesses
+    // need not wait for it).
     constexpr int PB = TN < 4 ? TN : 4;
     constexpr int NPASS = TN / PB;
     const int units = ngroups * NPASS;
@@ -365,6 +355,12 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(GemmParams p, i
       }
     };
     if (units > 0) b_dma(0, 0);
+    z_store(0);
+#pragma unroll
+    for (int i0 = ZB; i0 < ZIT; i0 += ZB) {
+      z_load(i0);
+      z_store(i0);
+    }
     for (int gi = 0; gi < ngroups; ++gi)
 #pragma unroll
     for (int pass = 0; pass < NPASS; ++pass) {  // static, so acc is indexed statically
@@ -478,6 +474,10 @@ static void dispatch_wide(const GemmParams& p, hipStream_t stream) {
 }
 
 void launch_gemm_wide(const GemmParams& p, hipStream_t stream) {
+  if (gemm_big_fits(p)) {
+    launch_gemm_big(p, stream);
+    return;
+  }
   if (p.wt.fmt == EPILORA_W_FP8) dispatch_wide<EPILORA_W_FP8>(p, stream);
   else dispatch_wide<EPILORA_W_FP4>(p, stream);
 }

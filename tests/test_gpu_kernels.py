@@ -180,10 +180,13 @@ GEMM_CASES = [
     (1, 256, 512, 1, 16, "zero", False, False, "fp4"),
     (20, 4096, 512, 4, 64, "mixed", True, False, "fp4"),
     (150, 1024, 300, 6, 32, "sorted", False, True, "fp4"),
-    # enough tiles for the 256 x 256 and 256 x 128 prefill tiles, ragged edges
+    # enough tiles for the 256 x 128 prefill tiles, ragged edges
     (1100, 256, 13100, 6, 64, "sorted", True, True, "fp8"),
     (700, 384, 12000, 5, 32, "mixed", False, False, "fp4"),
     (1030, 160, 13100, 4, 16, "mixed", True, False, "fp4"),
+    # enough 256 x 256 tiles that the base-only call takes that kernel
+    (2048, 256, 16384, 8, 64, "sorted", False, False, "fp8"),
+    (2100, 160, 16000, 4, 32, "mixed", True, False, "fp4"),
 ]
 
 
