@@ -110,7 +110,7 @@ static void launch_decode_x(DecodeParams& p, bool want_xq, hipStream_t stream) {
   p.job.qtarget = (int)g.M;
   p.count_q = XLDS ? 0 : 1;
   p.flags = p.count_q || p.ns > 0;
-  size_t lds = skinny_lds(g.M, g.K, MB, NW, r, true, XLDS);
+  size_t lds = skinny_lds(g.M, g.K, MB, NW, r, true, XLDS, FMT);
   const size_t shrink_lds = (size_t)kShrinkWaves * 16 * r * sizeof(float);
   if (shrink_lds > lds) lds = shrink_lds;
   // The quantizing and shrink workgroups are dispatched first and hold their
@@ -124,10 +124,10 @@ template <int MB, int FMT>
 static void launch_decode_nw(DecodeParams& p, bool want_xq, hipStream_t stream) {
   const GemmParams& g = p.job.g;
   if (skinny_waves(g.N, MB) == 8) {
-    if (skinny_x_in_lds(g.M, g.K, MB, 8, p.s.ad.r, true)) launch_decode_x<MB, FMT, 8, true>(p, want_xq, stream);
+    if (skinny_x_in_lds(g.M, g.K, MB, 8, p.s.ad.r, true, FMT)) launch_decode_x<MB, FMT, 8, true>(p, want_xq, stream);
     else launch_decode_x<MB, FMT, 8, false>(p, want_xq, stream);
   } else {
-    if (skinny_x_in_lds(g.M, g.K, MB, 4, p.s.ad.r, true)) launch_decode_x<MB, FMT, 4, true>(p, want_xq, stream);
+    if (skinny_x_in_lds(g.M, g.K, MB, 4, p.s.ad.r, true, FMT)) launch_decode_x<MB, FMT, 4, true>(p, want_xq, stream);
     else launch_decode_x<MB, FMT, 4, false>(p, want_xq, stream);
   }
 }

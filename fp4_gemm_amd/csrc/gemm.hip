@@ -21,7 +21,7 @@ __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(SkinnyJob J) {
 template <int MB, int FMT, int NW, bool XLDS>
 static void launch_skinny_x(SkinnyJob& J, hipStream_t stream) {
   const GemmParams& p = J.g;
-  const size_t lds = skinny_lds(p.M, p.K, MB, NW, p.ad.r, false, XLDS);
+  const size_t lds = skinny_lds(p.M, p.K, MB, NW, p.ad.r, false, XLDS, FMT);
   J.gwgs = skinny_groups(p.N, resident_groups(gemm_skinny_kernel<MB, FMT, NW, XLDS>, NW * 64, lds));
   hipLaunchKernelGGL((gemm_skinny_kernel<MB, FMT, NW, XLDS>), dim3(J.gwgs), dim3(NW * 64), lds, stream, J);
 }
@@ -31,7 +31,7 @@ static void launch_skinny_nw(const GemmParams& p, hipStream_t stream) {
   SkinnyJob J{};
   J.g = p;
   J.tiles = (int)cdiv(p.N, 16);
-  if (skinny_x_in_lds(p.M, p.K, MB, NW, p.ad.r, false)) launch_skinny_x<MB, FMT, NW, true>(J, stream);
+  if (skinny_x_in_lds(p.M, p.K, MB, NW, p.ad.r, false, FMT)) launch_skinny_x<MB, FMT, NW, true>(J, stream);
   else launch_skinny_x<MB, FMT, NW, false>(J, stream);
 }
 

@@ -37,28 +37,43 @@ __device__ __forceinline__ uint32_t absmax8(const uint4& v) {
 // the correctly rounded quotient (Markstein's theorem on division with a
 // correctly rounded reciprocal).  The theorem needs the residual to stay
 // normal: s >= 2^-64 keeps it normal for every |x / s| >= 2^-11, and smaller
-// quotients (a +-1 ulp error there) all encode to a signed zero anyway.  The
-// sign of a zero quotient is x's, as IEEE division gives it.  Rows with
-// s < 2^-64 take the division (quot_recip returns 0 for them).
-__device__ __forceinline__ float quot_recip(float s) { return s >= 0x1p-64f ? 1.0f / s : 0.0f; }
+// quotients (a +-1 ulp error there) all encode to a signed zero anyway.  A
+// row with s < 2^-64 has every |x| <= 448 s < 2^-55, so both x and s are
+// multiplied by f = 2^127 first: exact (a power of two, no overflow, and
+// subnormals only gain precision), the same real quotient, and a divisor of
+// at least 2^-15.  One branch-free sequence thus serves every row.  The sign
+// of a zero quotient is x's, as IEEE division gives it.
+struct QuotRow {
+  float f;   // 1, or 2^127 for a row scale below 2^-64
+  float s;   // the row scale times f
+  float rs;  // RN(1 / s), an IEEE division once per row
+};
 
-__device__ __forceinline__ float quot(float x, float s, float rs) {
-  if (rs == 0.0f) return x / s;
-  const float q0 = x * rs;
-  const float r = fmaf(-q0, s, x);
-  return copysignf(fmaf(r, rs, q0), x);
+__device__ __forceinline__ QuotRow quot_consts(float s) {
+  QuotRow q;
+  q.f = s >= 0x1p-64f ? 1.0f : 0x1p127f;
+  q.s = s * q.f;
+  q.rs = 1.0f / q.s;
+  return q;
+}
+
+__device__ __forceinline__ float quot(float x, const QuotRow& q) {
+  const float xs = x * q.f;
+  const float q0 = xs * q.rs;
+  const float r = fmaf(-q0, q.s, xs);
+  return copysignf(fmaf(r, q.rs, q0), x);
 }
 
 // Eight bf16 values to E4M3 codes: E4M3(RN(x / s)).  |x / s| <= 448 (1 + 2^-23)
 // here, so the hardware conversion (round to nearest even, OCP E4M3FN on this
 // target, signed zero kept) never meets its overflow range.
-__device__ __forceinline__ uint2 encode8(const uint4& v, float s, float rs) {
+__device__ __forceinline__ uint2 encode8(const uint4& v, const QuotRow& q) {
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   uint32_t out[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    int c = __builtin_amdgcn_cvt_pk_fp8_f32(quot(bf16_lo(w[2 * h]), s, rs), quot(bf16_hi(w[2 * h]), s, rs), 0, false);
-    c = __builtin_amdgcn_cvt_pk_fp8_f32(quot(bf16_lo(w[2 * h + 1]), s, rs), quot(bf16_hi(w[2 * h + 1]), s, rs), c,
+    int c = __builtin_amdgcn_cvt_pk_fp8_f32(quot(bf16_lo(w[2 * h]), q), quot(bf16_hi(w[2 * h]), q), 0, false);
+    c = __builtin_amdgcn_cvt_pk_fp8_f32(quot(bf16_lo(w[2 * h + 1]), q), quot(bf16_hi(w[2 * h + 1]), q), c,
                                         true);
     out[h] = (uint32_t)c;
   }
@@ -108,14 +123,14 @@ __device__ __forceinline__ void quant_row(const uint16_t* __restrict__ xrow, int
   for (int j = tid + kRegVecs * NT; j < nv; j += NT) amax = max(amax, absmax8(src[j]));
   amax = block_max_u32<NT>(amax, red);
   const float s = row_scale(amax);
-  const float rs = quot_recip(s);
+  const QuotRow qc = quot_consts(s);
   if (tid == 0) buf_store4<POLICY>(sr, soff, __float_as_uint(s));
 #pragma unroll
   for (int i = 0; i < kRegVecs; ++i) {
     const int j = tid + i * NT;
-    if (j < nv) buf_store8<POLICY>(qr, qoff + 8 * j, encode8(v[i], s, rs));
+    if (j < nv) buf_store8<POLICY>(qr, qoff + 8 * j, encode8(v[i], qc));
   }
-  for (int j = tid + kRegVecs * NT; j < nv; j += NT) buf_store8<POLICY>(qr, qoff + 8 * j, encode8(src[j], s, rs));
+  for (int j = tid + kRegVecs * NT; j < nv; j += NT) buf_store8<POLICY>(qr, qoff + 8 * j, encode8(src[j], qc));
 }
 
 }  // namespace epilora

@@ -14,7 +14,13 @@
 // Weights stream in batches of U steps through buffer resources
 // (out-of-range offsets read as zero) with two batches in flight, across tile
 // boundaries: the next tile's first batch is on its way while the current
-// tile's epilogue runs.  Small quantized activations (M * K <= 32 KB) sit in
+// tile's epilogue runs.  FP8 weights are requested in whole 128-byte lines:
+// for each 128-byte K step, lane l loads 16 bytes of rows l / 8 and
+// 8 + l / 8 at chunk l % 8, so one load instruction covers eight full lines
+// (a wave spreading an instruction over sixteen half lines streams about a
+// quarter slower).  The wave then puts the step through its own 2 KB of LDS
+// (chunk c of row n at position c ^ (n % 8), no bank conflicts on either
+// side) and reads it back in the matrix-core layout above.  Small quantized activations (M * K <= 32 KB) sit in
 // LDS for the whole kernel; larger ones are loaded with the weights.
 //
 // A tile's epilogue sums the NW partial accumulators in wave order through
@@ -53,10 +59,12 @@ __host__ __device__ inline uint32_t align16(uint32_t v) { return (v + 15u) & ~15
 
 // LDS layout of a skinny workgroup (byte offsets); host and device agree.
 struct SkLayout {
-  uint32_t part, red, tbl, tok, sx, zs, xs, stash, stash_n0, total;
+  uint32_t part, red, tbl, tok, sx, zs, xs, stash, stash_n0, wst, total;
 };
 
-__host__ __device__ inline SkLayout sk_layout(int MB, int NW, int r, uint32_t xbytes, int nstash) {
+constexpr uint32_t kWaveStage = 2048;  // LDS per wave for one FP8 weight step (16 rows x 128 bytes)
+
+__host__ __device__ inline SkLayout sk_layout(int MB, int NW, int r, uint32_t xbytes, int nstash, int fmt) {
   const uint32_t T = MB * 16;
   SkLayout L;
   L.part = 0;                                            // float [NW][T][16]
@@ -68,7 +76,8 @@ __host__ __device__ inline SkLayout sk_layout(int MB, int NW, int r, uint32_t xb
   L.xs = align16(L.zs + T * r * 4);                      // uint8 [M][K]
   L.stash = align16(L.xs + xbytes);                      // float [nstash][T][16]
   L.stash_n0 = align16(L.stash + nstash * T * 16 * 4);   // int64 [nstash]
-  L.total = align16(L.stash_n0 + nstash * 8 + 16);       // + one flag word
+  L.wst = align16(L.stash_n0 + nstash * 8);              // uint8 [NW][kWaveStage] (FP8 weights)
+  L.total = align16(L.wst + (fmt == EPILORA_W_FP8 ? NW * kWaveStage : 0u) + 16);  // + one flag word
   return L;
 }
 
@@ -176,7 +185,8 @@ struct SelfQuant {
       }
     }
     __syncthreads();
-    float sc[kSelfQuantMaxM], rc[kSelfQuantMaxM];
+    float sc[kSelfQuantMaxM];
+    QuotRow qc[kSelfQuantMaxM];
 #pragma unroll
     for (int u = 0; u < kSelfQuantMaxM; ++u) {
       uint32_t a = 0;
@@ -185,7 +195,7 @@ struct SelfQuant {
         for (int w = 0; w < W; ++w) a = max(a, red[u * W + w]);
       }
       sc[u] = row_scale(a);
-      rc[u] = quot_recip(sc[u]);
+      qc[u] = quot_consts(sc[u]);
       if (tid == 0 && u < M) sxs[u] = sc[u];
     }
 #pragma unroll
@@ -193,21 +203,20 @@ struct SelfQuant {
       const int j = tid + i * NT;
       if (j < total) {
         const int t = j / nv;
-        float s = sc[0], rs = rc[0];
+        QuotRow q = qc[0];
 #pragma unroll
         for (int u = 1; u < kSelfQuantMaxM; ++u)
-          if (u == t) s = sc[u], rs = rc[u];
-        *reinterpret_cast<uint2*>(qs + 8 * j) = encode8(v[i], s, rs);
+          if (u == t) q = qc[u];
+        *reinterpret_cast<uint2*>(qs + 8 * j) = encode8(v[i], q);
       }
     }
     for (int j = tid + RV * NT; j < total; j += NT) {
       const int t = j / nv;
-      float s = sc[0], rs = rc[0];
+      QuotRow q = qc[0];
 #pragma unroll
       for (int u = 1; u < kSelfQuantMaxM; ++u)
-        if (u == t) s = sc[u], rs = rc[u];
-      *reinterpret_cast<uint2*>(qs + 8 * j) =
-          encode8(*reinterpret_cast<const uint4*>(x + t * ldx + 8 * (j - t * nv)), s, rs);
+        if (u == t) q = qc[u];
+      *reinterpret_cast<uint2*>(qs + 8 * j) = encode8(*reinterpret_cast<const uint4*>(x + t * ldx + 8 * (j - t * nv)), q);
     }
     __syncthreads();
   }
@@ -229,6 +238,7 @@ struct Skinny {
   uint2* tbl;
   TokenSlot* tok;
   uint8_t* xs;
+  uint8_t* wst;  // this wave's FP8 weight step
   int* verdict;
   int g, lane, wave, row;
   int sb, se, nb, total;
@@ -239,7 +249,7 @@ struct Skinny {
 
   __device__ __forceinline__ Skinny(const SkinnyJob& j, char* lds, int gidx) : J(j), p(j.g), g(gidx) {
     const int64_t M = p.M, K = p.K;
-    L = sk_layout(MB, NW, p.ad.r, XLDS ? (uint32_t)(M * K) : 0u, FUSED ? StashCfg<MB>::n : 0);
+    L = sk_layout(MB, NW, p.ad.r, XLDS ? (uint32_t)(M * K) : 0u, FUSED ? StashCfg<MB>::n : 0, FMT);
     part = reinterpret_cast<float*>(lds + L.part);
     red = reinterpret_cast<float*>(lds + L.red);
     tbl = reinterpret_cast<uint2*>(lds + L.tbl);
@@ -247,6 +257,7 @@ struct Skinny {
     sxs = reinterpret_cast<float*>(lds + L.sx);
     zs = reinterpret_cast<float*>(lds + L.zs);
     xs = reinterpret_cast<uint8_t*>(lds + L.xs);
+    wst = reinterpret_cast<uint8_t*>(lds + L.wst) + (threadIdx.x >> 6) * kWaveStage;
     stash = reinterpret_cast<float*>(lds + L.stash);
     stash_n0 = reinterpret_cast<int64_t*>(lds + L.stash_n0);
     verdict = reinterpret_cast<int*>(lds + L.total - 16);
@@ -285,16 +296,22 @@ struct Skinny {
                               FMT == EPILORA_W_FP4 ? (uint32_t)(rows * (K / 16)) : 0u);
     const uint32_t wbase = row < rows ? (uint32_t)(row * wrow) : kOutOfRange;
     const uint32_t sbase = row < rows ? (uint32_t)(row * (K / 16)) : kOutOfRange;
+    // FP8: rows l / 8 and 8 + l / 8, chunk l % 8 of each step
+    const int r0 = lane >> 3;
+    const uint32_t c16 = (uint32_t)(lane & 7) * 16u;
+    const uint32_t wbase0 = r0 < rows ? (uint32_t)(r0 * wrow) + c16 : kOutOfRange;
+    const uint32_t wbase1 = r0 + 8 < rows ? (uint32_t)((r0 + 8) * wrow) + c16 : kOutOfRange;
     const int s0 = sb + (live ? j % nb : 0) * U;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint32_t k = (uint32_t)(s0 + u) * 128u + kofs;
-      const bool ok = s0 + u < se && (int64_t)k < K;
       if (FMT == EPILORA_W_FP8) {
-        const uint32_t off = ok ? wbase + k : kOutOfRange;
-        b.wa[u] = bufv_load16<kCached>(wr, off);
-        b.wb[u] = bufv_load16<kCached>(wr, off + 16);
+        const uint32_t k = (uint32_t)(s0 + u) * 128u;
+        const bool ok = s0 + u < se && (int64_t)(k + c16) < K;
+        b.wa[u] = bufv_load16<kCached>(wr, ok ? wbase0 + k : kOutOfRange);
+        b.wb[u] = bufv_load16<kCached>(wr, ok ? wbase1 + k : kOutOfRange);
       } else {
+        const uint32_t k = (uint32_t)(s0 + u) * 128u + kofs;
+        const bool ok = s0 + u < se && (int64_t)k < K;
         b.wa[u] = bufv_load16<kCached>(wr, ok ? wbase + k / 2 : kOutOfRange);
         b.wb[u] = u32x4{buf_load2<kCached>(sr, ok ? sbase + k / 16 : kOutOfRange), 0u, 0u, 0u};
       }
@@ -324,7 +341,14 @@ struct Skinny {
     for (int u = 0; u < U; ++u) {
       i32x8 wf;
       if (FMT == EPILORA_W_FP8) {
-        wf = cat8(b.wa[u], b.wb[u]);
+        const int r0 = lane >> 3;
+        const uint32_t pw = (uint32_t)((lane & 7) ^ (r0 & 7)) * 16u;
+        *reinterpret_cast<u32x4*>(wst + r0 * 128 + pw) = b.wa[u];
+        *reinterpret_cast<u32x4*>(wst + (r0 + 8) * 128 + pw) = b.wb[u];
+        const uint32_t p0 = (uint32_t)((2 * (lane >> 4)) ^ (row & 7)) * 16u;
+        const u32x4 q0 = *reinterpret_cast<const u32x4*>(wst + row * 128 + p0);
+        const u32x4 q1 = *reinterpret_cast<const u32x4*>(wst + row * 128 + (p0 ^ 16u));
+        wf = cat8(q0, q1);
       } else {
         const uint32_t sc = b.wb[u].x;
         const uint2 t0 = tbl[sc & 0xFFu], t1 = tbl[(sc >> 8) & 0xFFu];
@@ -656,14 +680,14 @@ inline int skinny_groups(int64_t N, int resident) {
 }
 // Whether the quantized activations live in LDS (the fused kernel then
 // quantizes them itself), and the LDS bytes of the workgroup.
-inline bool skinny_x_in_lds(int64_t M, int64_t K, int MB, int NW, int r, bool fused) {
+inline bool skinny_x_in_lds(int64_t M, int64_t K, int MB, int NW, int r, bool fused, int fmt) {
   if (M * K > kXInLdsMax || (fused && M > kSelfQuantMaxM)) return false;
   const int nstash = fused ? (MB <= 2 ? 4 : 2) : 0;
-  return sk_layout(MB, NW, r, (uint32_t)(M * K), nstash).total <= kLdsBudget;
+  return sk_layout(MB, NW, r, (uint32_t)(M * K), nstash, fmt).total <= kLdsBudget;
 }
-inline uint32_t skinny_lds(int64_t M, int64_t K, int MB, int NW, int r, bool fused, bool xlds) {
+inline uint32_t skinny_lds(int64_t M, int64_t K, int MB, int NW, int r, bool fused, bool xlds, int fmt) {
   const int nstash = fused ? (MB <= 2 ? 4 : 2) : 0;
-  return sk_layout(MB, NW, r, xlds ? (uint32_t)(M * K) : 0u, nstash).total;
+  return sk_layout(MB, NW, r, xlds ? (uint32_t)(M * K) : 0u, nstash, fmt).total;
 }
 
 }  // namespace epilora
