@@ -16,9 +16,9 @@
 //                              order) and count up the z flag;
 //   the rest                   own 16-row weight tiles: request their first
 //                              weight batch, obtain the quantized rows,
-//                              stream the weights through the matrix cores,
-//                              and wait for z only before an epilogue
-//                              (finished tiles wait in an LDS stash).
+//                              stream the weights through the matrix cores
+//                              into an LDS stash, and wait for z only once
+//                              all their tiles are in, before the epilogues.
 // Data crosses workgroups only through device-coherent stores and loads
 // (sc1), and a producer bumps its flag (a relaxed agent-scope atomic) only
 // after its stores have completed, so no workgroup has to write back or
@@ -115,7 +115,7 @@ static void launch_decode_x(DecodeParams& p, bool want_xq, hipStream_t stream) {
   if (shrink_lds > lds) lds = shrink_lds;
   // The quantizing and shrink workgroups are dispatched first and hold their
   // slots only until they finish.
-  p.job.gwgs = skinny_groups(g.N, resident_groups(decode_kernel<MB, FMT, NW, XLDS>, NW * 64, lds));
+  p.job.gwgs = skinny_groups(g.N, resident_groups(decode_kernel<MB, FMT, NW, XLDS>, NW * 64, lds), StashCfg<MB>::n);
   const unsigned grid = (unsigned)(p.nq + p.ns + p.job.gwgs);
   hipLaunchKernelGGL((decode_kernel<MB, FMT, NW, XLDS>), dim3(grid), dim3(NW * 64), lds, stream, p);
 }

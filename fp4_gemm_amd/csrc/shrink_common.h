@@ -118,12 +118,89 @@ __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int64_t t0, i
   __syncthreads();
 }
 
+// The fixed-order sum of the split partials ([splits][M][r] fp32) of the
+// tile of `rows` tokens at t0, shared by the shrink's last split and by the
+// fused decode path's GEMM workgroups, so that both round identically.  The
+// quads (4 floats) of the tile times chunks of consecutive splits are spread
+// over the threads; each chunk is summed in split order, then the chunk sums
+// in chunk order (the chunking depends on the tile shape only, not on the
+// block size).  With one split the partial passes through unchanged.
+// `sums`: LDS of max(kShrinkWaves * kWave, rows * r / 4) float4s.
+// sink(q, v) receives quad q of the tile.  Every thread of the block calls
+// it; it ends with a barrier.
+template <int NTHREADS, typename Sink>
+__device__ __forceinline__ void combine_partials(const float* partials, int splits, int64_t M, int64_t t0,
+                                                 int64_t rows, int r, float* sums, Sink sink) {
+  const uint32_t tile_bytes = (uint32_t)(rows * r * 4);
+  const int quads = (int)(rows * r / 4);
+  auto part = [&](int s) { return make_rsrc(partials + ((int64_t)s * M + t0) * r, tile_bytes); };
+  if (splits == 1) {
+    for (int q = threadIdx.x; q < quads; q += NTHREADS) {
+      const uint4 u = buf_load16<kCoherent>(part(0), 16u * q);
+      sink(q, make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w)));
+    }
+    __syncthreads();
+    return;
+  }
+  const int threads = kShrinkWaves * kWave;  // the chunking, not the block size
+  int chunks = threads / quads;
+  if (chunks < 1) chunks = 1;
+  if (chunks > splits) chunks = splits;
+  const int per = (splits + chunks - 1) / chunks;
+  for (int item = threadIdx.x; item < quads * chunks; item += NTHREADS) {
+    const int q = item % quads, c = item / quads;
+    const int s0 = c * per, s1 = min(splits, s0 + per);
+    // Loads of up to 8 splits are in flight together; they are added in
+    // split order all the same.
+    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto add = [&](uint4 u) {
+      v.x += __uint_as_float(u.x);
+      v.y += __uint_as_float(u.y);
+      v.z += __uint_as_float(u.z);
+      v.w += __uint_as_float(u.w);
+    };
+    int s = s0;
+    for (; s + 8 <= s1; s += 8) {
+      uint4 u[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) u[j] = buf_load16<kCoherent>(part(s + j), 16u * q);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) add(u[j]);
+    }
+    for (; s < s1; ++s) add(buf_load16<kCoherent>(part(s), 16u * q));
+    *reinterpret_cast<float4*>(&sums[4 * item]) = v;
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < quads; q += NTHREADS) {
+    float4 v = *reinterpret_cast<const float4*>(&sums[4 * q]);
+    for (int c = 1; c < chunks; ++c) {
+      const float4 w = *reinterpret_cast<const float4*>(&sums[4 * (c * quads + q)]);
+      v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+    }
+    sink(q, v);
+  }
+  __syncthreads();
+}
+
+// Store this workgroup's [rows][r] sums (in LDS `red`) as its split's
+// partial with device-coherent stores; returns once they have completed.
+template <int NW, int TT = kShrinkTokens>
+__device__ __forceinline__ void shrink_store_partial(const ShrinkParams& p, int tile, int split, const float* red) {
+  const int64_t t0 = (int64_t)tile * TT;
+  const int r = p.ad.r;
+  const int64_t rows = p.M - t0 < TT ? p.M - t0 : TT;
+  const auto pr = make_rsrc(p.partials + ((int64_t)split * p.M + t0) * r, (uint32_t)(rows * r * 4));
+  for (int e = 4 * threadIdx.x; e < rows * r; e += 4 * NW * kWave)
+    buf_store16<kCoherent>(pr, 4 * e, *reinterpret_cast<const uint4*>(&red[e]));
+  wait_all_memory();
+  __syncthreads();
+}
+
 // Write this workgroup's [TT][r] sums (in LDS `red`) to z, or to its split's
-// partial; the last split of a tile adds the partials in a fixed order.  z and
-// the partials are written and read device-coherently, so another workgroup
-// of the same grid may read z once the caller has published it.  Returns
-// true in the workgroup that wrote the tile's final z, after every one of
-// its z stores has completed.
+// partial; the last split of a tile adds the partials (combine_partials).  z
+// and the partials are written and read device-coherently.  Returns true in
+// the workgroup that wrote the tile's final z, after every one of its z
+// stores has completed.
 template <int NW, int TT = kShrinkTokens>
 __device__ __forceinline__ bool shrink_finish(const ShrinkParams& p, int tile, int split, float* red) {
   __shared__ int last;
@@ -139,60 +216,15 @@ __device__ __forceinline__ bool shrink_finish(const ShrinkParams& p, int tile, i
     __syncthreads();
     return true;
   }
-  const auto pr = make_rsrc(p.partials + ((int64_t)split * p.M + t0) * r, tile_bytes);
-  for (int e = 4 * threadIdx.x; e < rows * r; e += 4 * NW * kWave)
-    buf_store16<kCoherent>(pr, 4 * e, *reinterpret_cast<const uint4*>(&red[e]));
-  wait_all_memory();
-  __syncthreads();
+  shrink_store_partial<NW, TT>(p, tile, split, red);
   if (threadIdx.x == 0) last = atomic_add_relaxed(&p.counters[tile], 1) == p.splits - 1;
   __syncthreads();
   if (!last) return false;
-  // Combine: the quads (4 floats) of the tile times chunks of consecutive
-  // splits are spread over the workgroup; each chunk is summed in split
-  // order, then the chunk sums in chunk order, so the rounding is the same on
-  // every run.  `red` is free again and holds the chunk sums.
-  float* sums = red;
-  const int quads = (int)(rows * r / 4);
-  const int threads = kShrinkWaves * kWave;  // the chunking, not the block size
-  int chunks = threads / quads;
-  if (chunks < 1) chunks = 1;
-  if (chunks > p.splits) chunks = p.splits;
-  const int per = (p.splits + chunks - 1) / chunks;
-  for (int item = threadIdx.x; item < quads * chunks; item += NW * kWave) {
-    const int q = item % quads, c = item / quads;
-    const int s0 = c * per, s1 = min(p.splits, s0 + per);
-    // Loads of up to 8 splits are in flight together; they are added in
-    // split order all the same.
-    float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
-    auto add = [&](uint4 u) {
-      v.x += __uint_as_float(u.x);
-      v.y += __uint_as_float(u.y);
-      v.z += __uint_as_float(u.z);
-      v.w += __uint_as_float(u.w);
-    };
-    int s = s0;
-    for (; s + 8 <= s1; s += 8) {
-      uint4 u[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        u[j] = buf_load16<kCoherent>(make_rsrc(p.partials + ((int64_t)(s + j) * p.M + t0) * r, tile_bytes), 16u * q);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) add(u[j]);
-    }
-    for (; s < s1; ++s)
-      add(buf_load16<kCoherent>(make_rsrc(p.partials + ((int64_t)s * p.M + t0) * r, tile_bytes), 16u * q));
-    *reinterpret_cast<float4*>(&sums[4 * item]) = v;
-  }
-  __syncthreads();
-  for (int q = threadIdx.x; q < quads; q += NW * kWave) {
-    float4 v = *reinterpret_cast<const float4*>(&sums[4 * q]);
-    for (int c = 1; c < chunks; ++c) {
-      const float4 w = *reinterpret_cast<const float4*>(&sums[4 * (c * quads + q)]);
-      v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
-    }
+  // `red` is free again and holds the chunk sums.
+  combine_partials<NW * kWave>(p.partials, p.splits, p.M, t0, rows, r, red, [&](int q, const float4& v) {
     buf_store16<kCoherent>(zr, 16u * q, make_uint4(__float_as_uint(v.x), __float_as_uint(v.y),
                                                    __float_as_uint(v.z), __float_as_uint(v.w)));
-  }
+  });
   if (threadIdx.x == 0) store_relaxed(&p.counters[tile], 0);
   wait_all_memory();
   __syncthreads();

@@ -28,9 +28,13 @@
 // an fp32 dot over the rank, 16 lanes per output (lane j takes a contiguous
 // r / 16 slice of the rank) reduced by shuffles; the first pass of B slices
 // for a tile is requested during the previous tile.  In the fused decode
-// kernel z may not be ready when a tile finishes: the tile's reduced base
-// results then wait in an LDS stash and their epilogues run once z is
-// published, so the weight stream does not wait for the shrink.
+// kernel z is produced by other workgroups of the same grid, so the
+// streaming loop only reduces each finished tile into an LDS stash (room for
+// kStashTiles tiles; the host never gives a workgroup more); once the last
+// tile is in, the workgroup requests the B slices of all its tiles, waits
+// once for z and runs the epilogues.  Keeping the wait, the hand-off and the
+// epilogues out of the loop keeps the loop's code small: a loop that also
+// carried them streamed measurably slower even when they never ran.
 #pragma once
 
 #include "gemm_common.h"
@@ -43,11 +47,12 @@ constexpr int kXInLdsMax = 32768;  // bytes of quantized activations kept in LDS
 constexpr int kSelfQuantMaxM = 4;  // the fused kernel quantizes up to this many rows itself
 constexpr uint32_t kLdsBudget = 65536;
 
-// Tiles whose epilogue may wait for z in the fused kernel.
+// Tiles of one fused workgroup, held in LDS until z is published.
 template <int MB>
 struct StashCfg {
-  static constexpr int n = MB <= 2 ? 4 : 2;
+  static constexpr int n = MB == 1 ? 8 : 4;
 };
+inline int stash_tiles(int MB) { return MB == 1 ? 8 : 4; }
 
 template <int MB>
 struct SkinnyCfg {
@@ -59,7 +64,7 @@ __host__ __device__ inline uint32_t align16(uint32_t v) { return (v + 15u) & ~15
 
 // LDS layout of a skinny workgroup (byte offsets); host and device agree.
 struct SkLayout {
-  uint32_t part, red, tbl, tok, sx, zs, xs, stash, stash_n0, wst, total;
+  uint32_t part, red, tbl, tok, sx, zs, xs, stash, wst, total;
 };
 
 constexpr uint32_t kWaveStage = 2048;  // LDS per wave for one FP8 weight step (16 rows x 128 bytes)
@@ -75,8 +80,7 @@ __host__ __device__ inline SkLayout sk_layout(int MB, int NW, int r, uint32_t xb
   L.zs = align16(L.sx + T * 4);                          // float [T][r]
   L.xs = align16(L.zs + T * r * 4);                      // uint8 [M][K]
   L.stash = align16(L.xs + xbytes);                      // float [nstash][T][16]
-  L.stash_n0 = align16(L.stash + nstash * T * 16 * 4);   // int64 [nstash]
-  L.wst = align16(L.stash_n0 + nstash * 8);              // uint8 [NW][kWaveStage] (FP8 weights)
+  L.wst = align16(L.stash + nstash * T * 16 * 4);        // uint8 [NW][kWaveStage] (FP8 weights)
   L.total = align16(L.wst + (fmt == EPILORA_W_FP8 ? NW * kWaveStage : 0u) + 16);  // + one flag word
   return L;
 }
@@ -234,7 +238,6 @@ struct Skinny {
   const GemmParams& p;
   SkLayout L;
   float *part, *red, *sxs, *zs, *stash;
-  int64_t* stash_n0;
   uint2* tbl;
   TokenSlot* tok;
   uint8_t* xs;
@@ -259,7 +262,6 @@ struct Skinny {
     xs = reinterpret_cast<uint8_t*>(lds + L.xs);
     wst = reinterpret_cast<uint8_t*>(lds + L.wst) + (threadIdx.x >> 6) * kWaveStage;
     stash = reinterpret_cast<float*>(lds + L.stash);
-    stash_n0 = reinterpret_cast<int64_t*>(lds + L.stash_n0);
     verdict = reinterpret_cast<int*>(lds + L.total - 16);
     lane = threadIdx.x & 63;
     wave = threadIdx.x >> 6;
@@ -270,7 +272,8 @@ struct Skinny {
     sb = min(steps, wave * spw);
     se = min(steps, sb + spw);
     nb = (int)cdiv(spw, U);
-    const int mine = (int)cdiv(J.tiles - g, J.gwgs);
+    int mine = (int)cdiv(J.tiles - g, J.gwgs);
+    if (FUSED && mine > StashCfg<MB>::n) mine = 0;  // never launched so (the stash holds n tiles)
     total = mine * nb;
     adapters = p.z != nullptr;
     gscale = FMT == EPILORA_W_FP4 ? weight_scale<FMT>(p.wt, 0) : 0.f;
@@ -495,34 +498,9 @@ struct Skinny {
     __syncthreads();
   }
 
-  // The B slices and weight scales the stashed tiles' epilogues need, all
-  // requested at once (before z is staged) instead of one tile after another.
-  struct StashPre {
-    uint4 b[StashCfg<MB>::n];
-    float w[StashCfg<MB>::n];
-  };
-  __device__ __forceinline__ void stash_prefetch(StashPre& sp, int nstash) const {
-#pragma unroll
-    for (int s = 0; s < StashCfg<MB>::n; ++s) {
-      if (s < nstash) {
-        sp.b[s] = b_chunk(stash_n0[s], threadIdx.x >> 4);
-        sp.w[s] = row_wscale(stash_n0[s]);
-      }
-    }
-  }
-  __device__ __forceinline__ void flush(const StashPre& sp, int& nstash) const {
-#pragma unroll
-    for (int s = 0; s < StashCfg<MB>::n; ++s)
-      if (s < nstash) outputs(stash_n0[s], stash + s * T * 16, true, sp.b[s], sp.w[s]);
-    nstash = 0;
-  }
-
-  // Tile j / nb is complete in `acc`: reduce it and write its outputs, or
-  // stash it until z is published.  `zseen`: thread 0's reading of the z
-  // flag, loaded before the latest weight batch was requested.
-  __device__ __forceinline__ void tile_done(int j, f32x4 (&acc)[MB], uint4& pre, float& pws, int zseen,
-                                            bool& zready, int& nstash, bool& ok) {
-    const int64_t n0 = n0_of(j);
+  // Sums the NW waves' partial accumulators of the finished tile into `dst`
+  // ([T][16], wave order) and clears the accumulators.  Ends with a barrier.
+  __device__ __forceinline__ void reduce_tile(f32x4 (&acc)[MB], float* dst) {
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
       const int t = mb * 16 + row;
@@ -530,47 +508,51 @@ struct Skinny {
           make_float4(acc[mb][0], acc[mb][1], acc[mb][2], acc[mb][3]);
       acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    if (!zready && threadIdx.x == 0) *verdict = zseen >= J.ztarget;
     __syncthreads();
     const int outs = (int)p.M * 16;
     for (int e = threadIdx.x; e < outs; e += NW * kWave) {
       float v = part[e];
 #pragma unroll
       for (int w = 1; w < NW; ++w) v += part[w * T * 16 + e];
-      red[e] = v;
+      dst[e] = v;
     }
-    const bool now = !zready && *verdict != 0;
     __syncthreads();
-    if (now) {  // z has just been published: stage it, drain the stash
-      StashPre sp;
-      stash_prefetch(sp, nstash);
-      stage_z();
-      zready = true;
-      if (ok) flush(sp, nstash);
-      nstash = 0;
+  }
+
+  // Tile j / nb is complete in `acc`.  Fused: reduce it into its stash slot.
+  // Otherwise z is ready: write its outputs, then request the next tile's
+  // first B slice and weight scale.
+  __device__ __forceinline__ void tile_done(int j, f32x4 (&acc)[MB], uint4& pre, float& pws) {
+    if (FUSED) {
+      reduce_tile(acc, stash + (j / nb) * T * 16);
+      return;
     }
-    if (zready) {
-      if (ok) outputs(n0, red, true, pre, pws);
-    } else {
-      for (int e = threadIdx.x; e < outs; e += NW * kWave) stash[nstash * T * 16 + e] = red[e];
-      if (threadIdx.x == 0) stash_n0[nstash] = n0;
-      ++nstash;
-      if (nstash == StashCfg<MB>::n) {  // the stash is full: wait for z here
-        ok = ok && wait_flag(J.zflag, J.ztarget, J.wait_ticks, p.ctrl + kCtrlError, verdict);
-        if (ok) {
-          StashPre sp;
-          stash_prefetch(sp, nstash);
-          stage_z();
-          zready = true;
-          flush(sp, nstash);
-        }
-        nstash = 0;
-      }
-    }
+    reduce_tile(acc, red);
+    outputs(n0_of(j), red, true, pre, pws);
     if (j + 1 < total) {
       pre = b_chunk(n0_of(j + 1), threadIdx.x >> 4);
       pws = row_wscale(n0_of(j + 1));
     }
+  }
+
+  // Fused: every tile of the workgroup is in the stash.  Request the first B
+  // slice of each, wait for z, stage it, write the outputs (pw: each tile's
+  // weight scale, requested at the start).
+  __device__ __forceinline__ void finish_stash(bool& ok, const float (&pw)[StashCfg<MB>::n]) {
+    constexpr int S = StashCfg<MB>::n;
+    const int mine = total / nb;
+    uint4 pb[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+      if (s < mine) pb[s] = b_chunk(n0_of(s * nb), threadIdx.x >> 4);
+    if (adapters) {
+      ok = wait_flag(J.zflag, J.ztarget, J.wait_ticks, p.ctrl + kCtrlError, verdict);
+      if (ok) stage_z();
+    }
+    if (!ok) return;
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+      if (s < mine) outputs(n0_of(s * nb), stash + s * T * 16, true, pb[s], pw[s]);
   }
 
   // ---- the whole job --------------------------------------------------------
@@ -607,13 +589,14 @@ struct Skinny {
     __syncthreads();
 
     bool ok = true;
-    bool zready = !FUSED || !adapters;
-    int nstash = 0;
     f32x4 acc[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    uint4 pre = b_chunk(n0_of(0), threadIdx.x >> 4);
-    float pws = row_wscale(n0_of(0));
+    uint4 pre = FUSED ? zero4() : b_chunk(n0_of(0), threadIdx.x >> 4);
+    float pws = FUSED ? 0.f : row_wscale(n0_of(0));
+    float pw[StashCfg<MB>::n];  // fused: the weight scale of each tile, needed after the stream
+#pragma unroll
+    for (int s = 0; s < StashCfg<MB>::n; ++s) pw[s] = (FUSED && s < total / nb) ? row_wscale(n0_of(s * nb)) : 0.f;
 
     if (FUSED && !XLDS) {  // the quantized rows come from other workgroups
       ok = wait_flag(J.qflag, J.qtarget, J.wait_ticks, err, verdict);
@@ -624,44 +607,27 @@ struct Skinny {
     load_x(A, 0);
     load_x(B, 1);
 
-    // Two batches in flight; a tile's epilogue runs before the batch that
-    // just finished is refilled.  The z flag for the next tile end is read
-    // before the batch preceding it is requested, so that the epilogue waits
-    // only for the flag, not for that batch.  (z is taken as not ready at the
-    // first tile end.)
-    int zseen = 0;
+    // Two batches in flight; a tile's reduction (and, unfused, its epilogue)
+    // runs before the batch that just finished is refilled.
     for (int j = 0; j < total; j += 2) {
       const bool endA = j % nb == nb - 1;
       const bool endB = j + 1 < total && (j + 1) % nb == nb - 1;
-      const bool endA2 = j + 2 < total && (j + 2) % nb == nb - 1;
       __builtin_amdgcn_sched_barrier(0);
       compute(A, j, acc);
       __builtin_amdgcn_sched_barrier(0);
-      if (endA) tile_done(j, acc, pre, pws, zseen, zready, nstash, ok);
-      zseen = 0;
-      if (endB && !zready && threadIdx.x == 0) zseen = load_relaxed(J.zflag);
+      if (endA) tile_done(j, acc, pre, pws);
       __builtin_amdgcn_sched_barrier(0);
       load_w(A, j + 2);
       load_x(A, j + 2);
       __builtin_amdgcn_sched_barrier(0);
       compute(B, j + 1, acc);
       __builtin_amdgcn_sched_barrier(0);
-      if (endB) tile_done(j + 1, acc, pre, pws, zseen, zready, nstash, ok);
-      zseen = 0;
-      if (endA2 && !zready && threadIdx.x == 0) zseen = load_relaxed(J.zflag);
+      if (endB) tile_done(j + 1, acc, pre, pws);
       __builtin_amdgcn_sched_barrier(0);
       load_w(B, j + 3);
       load_x(B, j + 3);
     }
-    if (nstash > 0) {  // z was not ready for the last tiles: wait for it once
-      ok = ok && wait_flag(J.zflag, J.ztarget, J.wait_ticks, err, verdict);
-      if (ok) {
-        StashPre sp;
-        stash_prefetch(sp, nstash);
-        stage_z();
-        flush(sp, nstash);
-      }
-    }
+    if (FUSED && ok) finish_stash(ok, pw);
     if (!ok && threadIdx.x == 0 && err != nullptr) atomic_or_relaxed(err, EPILORA_DEV_WAIT_TIMEOUT);
   }
 };
@@ -672,21 +638,25 @@ struct Skinny {
 // and, for that many rounds, as few workgroups as give every workgroup the
 // same number of tiles to within one, so slots stay free for others.
 inline int skinny_waves(int64_t N, int MB) { return (cdiv(N, 16) <= 256 && MB <= 2) ? 8 : 4; }
-inline int skinny_groups(int64_t N, int resident) {
+// `max_rounds` (> 0) caps the tiles of one workgroup (the fused kernel's
+// stash); the grid may then exceed the resident slots, which is safe because
+// a fused workgroup waits only on workgroups dispatched before it.
+inline int skinny_groups(int64_t N, int resident, int max_rounds = 0) {
   const int64_t tiles = cdiv(N, 16);
   const int64_t slots = resident > 0 ? resident : 1;
-  const int64_t rounds = cdiv(tiles, slots);
+  int64_t rounds = cdiv(tiles, slots);
+  if (max_rounds > 0 && rounds > max_rounds) rounds = max_rounds;
   return (int)cdiv(tiles, rounds);
 }
 // Whether the quantized activations live in LDS (the fused kernel then
 // quantizes them itself), and the LDS bytes of the workgroup.
 inline bool skinny_x_in_lds(int64_t M, int64_t K, int MB, int NW, int r, bool fused, int fmt) {
   if (M * K > kXInLdsMax || (fused && M > kSelfQuantMaxM)) return false;
-  const int nstash = fused ? (MB <= 2 ? 4 : 2) : 0;
+  const int nstash = fused ? stash_tiles(MB) : 0;
   return sk_layout(MB, NW, r, (uint32_t)(M * K), nstash, fmt).total <= kLdsBudget;
 }
 inline uint32_t skinny_lds(int64_t M, int64_t K, int MB, int NW, int r, bool fused, bool xlds, int fmt) {
-  const int nstash = fused ? (MB <= 2 ? 4 : 2) : 0;
+  const int nstash = fused ? stash_tiles(MB) : 0;
   return sk_layout(MB, NW, r, xlds ? (uint32_t)(M * K) : 0u, nstash, fmt).total;
 }
 
