@@ -13,20 +13,23 @@
 //                              LDS and the caller keeps no copy);
 //   the next tiles*splits      compute the shrink (bf16 x, fp32 partials,
 //                              the last split of a tile adds them in a fixed
-//                              order) and count up the z flag;
+//                              order) and store z in place, each word as its
+//                              bitwise complement into a region that reads
+//                              zero until then;
 //   the rest                   own 16-row weight tiles: request their first
 //                              weight batch, obtain the quantized rows,
 //                              stream the weights through the matrix cores
-//                              into an LDS stash, and wait for z only once
-//                              all their tiles are in, before the epilogues.
+//                              into an LDS stash, and poll z itself (no flag)
+//                              only once all their tiles are in, before the
+//                              epilogues.
 // Data crosses workgroups only through device-coherent stores and loads
 // (sc1), and a producer bumps its flag (a relaxed agent-scope atomic) only
 // after its stores have completed, so no workgroup has to write back or
 // invalidate its L2.  Workgroups are dispatched in index order, so the
 // producers are resident before any consumer spins; every wait is bounded by
 // a wall-clock limit and a timeout raises EPILORA_DEV_WAIT_TIMEOUT instead of
-// hanging.  The last GEMM workgroup to finish puts the flags back to zero for
-// the next call.  The quantizer, shrink and GEMM arithmetic is the same code
+// hanging.  The last GEMM workgroup to finish puts the flags back to zero and
+// clears z for the next call.  The quantizer, shrink and GEMM arithmetic is the same code
 // as in the separate kernels, with the same summation orders, so every output
 // is bitwise equal to the separate quant + shrink + GEMM calls.
 #include "quant_row.h"
@@ -70,7 +73,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((XLDS &
     shrink_range(p.s, split, s_begin, s_end);
     float* red = reinterpret_cast<float*>(smem);
     shrink_tile<NW>(p.s, (int64_t)tile * kShrinkTokens, s_begin, s_end, red, split == 0);
-    if (shrink_finish<NW>(p.s, tile, split, red) && threadIdx.x == 0) atomic_add_relaxed(ctrl + kCtrlZDone, 1);
+    shrink_finish<NW>(p.s, tile, split, red);
     return;
   }
 
@@ -80,10 +83,13 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((XLDS &
     sk.run();
   }
   if (!p.flags) return;
-  // Every flag read of this workgroup is behind it: count it done.  The last
-  // of each group counts the group, and the last group puts the flags back to
-  // zero; each counter is reset by the one that completed it.
+  // Every flag and z read of this workgroup is behind it: count it done.
+  // The last of each group counts the group, and the last group puts the
+  // flags back to zero and clears z; each counter is reset by the one that
+  // completed it.
+  int* last = reinterpret_cast<int*>(smem);
   __syncthreads();
+  if (threadIdx.x == 0) *last = 0;
   if (threadIdx.x == 0) {
     const int gi = bid - p.nq - p.ns;
     const int ng = (int)gridDim.x - p.nq - p.ns;
@@ -95,10 +101,16 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((XLDS &
       store_relaxed(sub, 0);
       if (atomic_add_relaxed(ctrl + kCtrlGemmDone, 1) == groups - 1) {
         store_relaxed(ctrl + kCtrlQuantDone, 0);
-        store_relaxed(ctrl + kCtrlZDone, 0);
         store_relaxed(ctrl + kCtrlGemmDone, 0);
+        *last = 1;
       }
     }
+  }
+  __syncthreads();
+  if (*last != 0 && p.ns > 0) {
+    const int n = (int)(g.M * p.s.ad.r);
+    const auto zr = make_rsrc(g.z, (uint32_t)(n * 4));
+    for (int e = 4 * threadIdx.x; e < n; e += 4 * NW * 64) buf_store16<kCoherent>(zr, 4u * e, make_uint4(0u, 0u, 0u, 0u));
   }
 }
 
@@ -157,18 +169,18 @@ hipError_t launch_decode_lora(const uint16_t* x, int64_t ldx, int64_t M, int64_t
   g.M = M; g.N = N; g.K = K;
   g.wt = wt; g.ad = ad;
   const bool adapters = ad.idx != nullptr;
-  g.z = adapters ? reinterpret_cast<float*>(wsb + lay.z) : nullptr;
+  g.z = adapters ? reinterpret_cast<float*>(wsb + kZOffset) : nullptr;
   g.y = y; g.ldy = ldy;
   g.ctrl = ctrl;
   J.tiles = (int)cdiv(N, 16);
   J.x = x;
   J.ldx = ldx;
   J.qflag = ctrl + kCtrlQuantDone;
-  J.zflag = ctrl + kCtrlZDone;
   J.wait_ticks = 100000000;  // 1 s at the 100 MHz constant wall clock
   ShrinkParams& s = p.s;
   s.x = x; s.M = M; s.K = K; s.ldx = ldx; s.ad = ad;
-  s.z = reinterpret_cast<float*>(wsb + lay.z);
+  s.z = reinterpret_cast<float*>(wsb + kZOffset);
+  s.zflip = ~0u;
   s.ctrl = ctrl;
   p.done = reinterpret_cast<int*>(wsb + kDoneOffset);
   s.counters = reinterpret_cast<int*>(wsb + lay.shrink.counters);
@@ -176,7 +188,6 @@ hipError_t launch_decode_lora(const uint16_t* x, int64_t ldx, int64_t M, int64_t
   s.splits = shrink_splits(M, K, ad.r);
   p.tiles = (int)cdiv(M, kShrinkTokens);
   p.ns = adapters ? p.tiles * s.splits : 0;
-  J.ztarget = p.tiles;
   const bool want_xq = xq_out != nullptr || sx_out != nullptr;
   if (wt.fmt == EPILORA_W_FP8) dispatch_decode<EPILORA_W_FP8>(p, want_xq, stream);
   else dispatch_decode<EPILORA_W_FP4>(p, want_xq, stream);

@@ -12,7 +12,6 @@ constexpr size_t kCtrlBytes = 256;
 constexpr int kCtrlError = 0;      // device error word (sticky bits)
 constexpr int kCtrlAmax = 1;       // 4-bit weight quantizer: global amax bits
 constexpr int kCtrlQuantDone = 8;  // fused path: rows quantized
-constexpr int kCtrlZDone = 9;      // fused path: shrink tiles combined
 constexpr int kCtrlGemmDone = 10;  // fused path: GEMM workgroups finished
 
 constexpr size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
@@ -26,13 +25,18 @@ constexpr int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 //   in kDoneGroups counters 256 bytes apart (one contended word would
 //   serialize hundreds of atomics), then the last of each group in the
 //   kCtrlGemmDone word;
-//   tile counters: the shrink's per-tile split counters.
+//   tile counters: the shrink's per-tile split counters;
+//   the fused path's z ([M][r] fp32 words, M <= 64, r <= 128): a word reads
+//   zero until its producer stores it, as its bitwise complement, so GEMM
+//   workgroups poll z itself; the last of them clears it again.
 constexpr int kDoneGroups = 16;
 constexpr int kDoneStride = 64;  // int32 words
 constexpr size_t kDoneOffset = kCtrlBytes;
 constexpr int64_t kMaxShrinkTiles = 4096;  // the shrink takes M <= 65536 per call
 constexpr size_t kTileCounterOffset = kDoneOffset + (size_t)kDoneGroups * kDoneStride * 4;
-constexpr size_t kStateBytes = align256(kTileCounterOffset + 4 * (size_t)kMaxShrinkTiles);
+constexpr size_t kZOffset = align256(kTileCounterOffset + 4 * (size_t)kMaxShrinkTiles);
+constexpr size_t kZBytes = 64 * 128 * 4;
+constexpr size_t kStateBytes = align256(kZOffset + kZBytes);
 
 // ---- shrink -----------------------------------------------------------------
 // A workgroup covers 16 consecutive tokens (64 for prefill batches, see

@@ -125,6 +125,7 @@ hipError_t launch_shrink(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, c
   p.counters = reinterpret_cast<int*>(reinterpret_cast<char*>(ws) + lay.counters);
   p.partials = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + lay.partials);
   p.splits = shrink_splits(M, K, ad.r);
+  p.zflip = 0u;
   if (M > kShrinkWideM) {
     const dim3 grid((unsigned)cdiv(M, kShrinkWideTokens), (unsigned)p.splits);
     hipLaunchKernelGGL(shrink_wide_kernel, grid, dim3(kShrinkThreads), 0, stream, p);

@@ -40,6 +40,7 @@ struct ShrinkParams {
   int* counters;
   float* partials;
   int splits;
+  uint32_t zflip;  // z words are stored XOR this (the fused path stores complements)
 };
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
@@ -209,9 +210,12 @@ __device__ __forceinline__ bool shrink_finish(const ShrinkParams& p, int tile, i
   const int64_t rows = p.M - t0 < TT ? p.M - t0 : TT;
   const uint32_t tile_bytes = (uint32_t)(rows * r * 4);
   const auto zr = make_rsrc(p.z + t0 * r, tile_bytes);
+  const uint32_t f = p.zflip;
   if (p.splits == 1) {
-    for (int e = 4 * threadIdx.x; e < rows * r; e += 4 * NW * kWave)
-      buf_store16<kCoherent>(zr, 4 * e, *reinterpret_cast<const uint4*>(&red[e]));
+    for (int e = 4 * threadIdx.x; e < rows * r; e += 4 * NW * kWave) {
+      const uint4 v = *reinterpret_cast<const uint4*>(&red[e]);
+      buf_store16<kCoherent>(zr, 4 * e, make_uint4(v.x ^ f, v.y ^ f, v.z ^ f, v.w ^ f));
+    }
     wait_all_memory();
     __syncthreads();
     return true;
@@ -222,8 +226,8 @@ __device__ __forceinline__ bool shrink_finish(const ShrinkParams& p, int tile, i
   if (!last) return false;
   // `red` is free again and holds the chunk sums.
   combine_partials<NW * kWave>(p.partials, p.splits, p.M, t0, rows, r, red, [&](int q, const float4& v) {
-    buf_store16<kCoherent>(zr, 16u * q, make_uint4(__float_as_uint(v.x), __float_as_uint(v.y),
-                                                   __float_as_uint(v.z), __float_as_uint(v.w)));
+    buf_store16<kCoherent>(zr, 16u * q, make_uint4(__float_as_uint(v.x) ^ f, __float_as_uint(v.y) ^ f,
+                                                   __float_as_uint(v.z) ^ f, __float_as_uint(v.w) ^ f));
   });
   if (threadIdx.x == 0) store_relaxed(&p.counters[tile], 0);
   wait_all_memory();

@@ -94,8 +94,6 @@ struct SkinnyJob {
   int64_t ldx;
   int* qflag;           // fused, activations not in LDS: rows quantized
   int qtarget;
-  int* zflag;           // fused with adapters: z published
-  int ztarget;
   int64_t wait_ticks;
 };
 
@@ -488,6 +486,47 @@ struct Skinny {
     }
   }
 
+  // Fused: z is published in place.  Every word of the z region reads zero
+  // until its producer stores it (as its bitwise complement), so the
+  // workgroup polls the words of its active tokens until none is missing,
+  // staging them into LDS (rows of inactive tokens as zero), under the
+  // wall-clock limit.  Returns false on a timeout.  Ends with a barrier.
+  __device__ __forceinline__ bool poll_z() const {
+    const int r = p.ad.r;
+    const int n = (int)p.M * r;
+    const auto zr = make_rsrc(p.z, (uint32_t)(n * 4));
+    int* err = p.ctrl + kCtrlError;
+    const int64_t start = wall_clock64();
+    for (;;) {
+      int missing = 0;
+      for (int e = threadIdx.x; e < n; e += NW * kWave) {
+        if (tok[e / r].a < 0) {
+          zs[e] = 0.f;
+        } else {
+          const uint32_t w = buf_load4<kCoherent>(zr, 4u * e);
+          if (w == 0u) missing = 1;
+          else zs[e] = __uint_as_float(~w);
+        }
+      }
+      if (threadIdx.x == 0) *verdict = 0;
+      __syncthreads();
+      if (missing) *verdict = 1;
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        int state = *verdict;  // 0: complete, 1: poll again, 2: give up
+        if (state != 0 && (wall_clock64() - start > J.wait_ticks || (load_relaxed(err) & EPILORA_DEV_WAIT_TIMEOUT)))
+          state = 2;
+        *verdict = state;
+      }
+      __syncthreads();
+      const int state = *verdict;
+      __syncthreads();
+      if (state == 0) return true;
+      if (state == 2) return false;
+      __builtin_amdgcn_s_sleep(2);
+    }
+  }
+
   // z (M x r fp32) into LDS, rows of inactive tokens as zero.  Ends with a
   // barrier.
   __device__ __forceinline__ void stage_z() const {
@@ -536,8 +575,8 @@ struct Skinny {
   }
 
   // Fused: every tile of the workgroup is in the stash.  Request the first B
-  // slice of each, wait for z, stage it, write the outputs (pw: each tile's
-  // weight scale, requested at the start).
+  // slice of each, poll z into LDS, write the outputs (pw: each tile's weight
+  // scale, requested at the start).
   __device__ __forceinline__ void finish_stash(bool& ok, const float (&pw)[StashCfg<MB>::n]) {
     constexpr int S = StashCfg<MB>::n;
     const int mine = total / nb;
@@ -545,10 +584,7 @@ struct Skinny {
 #pragma unroll
     for (int s = 0; s < S; ++s)
       if (s < mine) pb[s] = b_chunk(n0_of(s * nb), threadIdx.x >> 4);
-    if (adapters) {
-      ok = wait_flag(J.zflag, J.ztarget, J.wait_ticks, p.ctrl + kCtrlError, verdict);
-      if (ok) stage_z();
-    }
+    if (adapters) ok = poll_z();
     if (!ok) return;
 #pragma unroll
     for (int s = 0; s < S; ++s)
