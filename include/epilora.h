@@ -231,10 +231,13 @@ int epilora_lora_expand_add(const float* z, int64_t M, int64_t N,
 /* The fused small-batch (decode) path ("Multi-adapter kernels", The decode
  * path): quantization, shrink and the GEMM with its epilogue in ONE launch.
  * The lowest workgroups compute z (and quantize x where the GEMM workgroups
- * do not do it themselves) and publish it with device-coherent stores and a
- * counted device flag; the GEMM workgroups stream their weights meanwhile
- * and wait for z only before the epilogue.  HIP has no programmatic
- * dependent launch; this persistent split replaces it.
+ * do not do it themselves) and publish z in place, with device-coherent
+ * stores into a workspace region that reads zero until written; the GEMM
+ * workgroups stream their weights meanwhile, hold finished tiles in LDS and
+ * poll z only before the epilogues.  HIP has no programmatic dependent
+ * launch; this persistent split replaces it.  Inputs must be finite (a z
+ * word that is a NaN with an all-ones payload would never count as
+ * written: the wait would time out).
  * After a call that raised EPILORA_DEV_WAIT_TIMEOUT, re-initialise the
  * workspace (epilora_workspace_init) before using it again.
  * Same result as epilora_quant_act + epilora_lora_shrink +
