@@ -383,16 +383,20 @@ struct Skinny {
   // Token t's index and mask byte, loaded by thread t before the weights are
   // requested (a later load would return only after them), and resolved into
   // tok[] afterwards, as resolve_token does it.
+  // The loads are unconditional and bounds-checked (past M, without adapters
+  // or without a mask they read zero) and nothing tests their values before
+  // resolve_tokens: a load under a branch let the compiler test the mask byte
+  // at once, which held the weight requests behind it.
   struct TokenLoad {
-    int a = -1, m = 1;
+    int a, m;
   };
   __device__ __forceinline__ TokenLoad load_token() const {
     TokenLoad tl;
-    const int t = threadIdx.x;
-    if (adapters && t < T && t < p.M) {
-      tl.a = p.ad.idx[t];
-      if (p.ad.mask != nullptr) tl.m = p.ad.mask[t];
-    }
+    const uint32_t t = threadIdx.x < T ? threadIdx.x : 0u;
+    const auto ir = make_rsrc(p.ad.idx, adapters ? (uint32_t)(p.M * 4) : 0u);
+    const auto mr = make_rsrc(p.ad.mask, (adapters && p.ad.mask != nullptr) ? (uint32_t)p.M : 0u);
+    tl.a = (int)buf_load4<kCached>(ir, 4u * t);
+    tl.m = (int)__builtin_amdgcn_raw_buffer_load_b8(mr, t, 0, 0);
     return tl;
   }
   __device__ __forceinline__ void resolve_tokens(const TokenLoad& tl, bool report) const {
@@ -405,7 +409,7 @@ struct Skinny {
         if (report) atomic_or_relaxed(p.ctrl + kCtrlError, EPILORA_DEV_BAD_INDEX);
         a = -1;
       }
-      if (a >= 0 && tl.m == 0) a = -1;
+      if (a >= 0 && p.ad.mask != nullptr && tl.m == 0) a = -1;
       if (a >= 0) {
         rk = p.ad.ranks != nullptr ? p.ad.ranks[a] : p.ad.r;
         rk = rk < p.ad.r ? rk : p.ad.r;
