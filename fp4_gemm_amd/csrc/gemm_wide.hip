@@ -39,18 +39,21 @@ __device__ __forceinline__ int swz8(int row, int chunk) { return row * 128 + ((c
 }  // namespace
 
 template <int FMT, int BM, int BN>
-__global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(GemmParams p, int tiles_m, int tiles_n) {
+__global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(BM == 128 ? 2 : 1))) void gemm_wide_kernel(GemmParams p, int tiles_m, int tiles_n) {
   constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 16, TN = WN / 16;
   // Two operand buffers as distinct objects, so that the compiler sees that
   // the loads filling one never alias the reads of the other (and does not
   // wait for them before those reads).  Each holds A ([BM][128]) then B
   // ([BN][128]).
   // The epilogue reuses them: bf16 z rows (256 bytes per token) in buf0 and
-  // two 32 KB slots of B rows in buf1.
+  // NSLOT 32 KB slots of B rows in buf1.  128-row tiles take one slot, so the
+  // workgroup holds 64 KB of LDS and two run on a compute unit: one's
+  // epilogue (a chain of memory round trips) overlaps the other's main loop.
+  constexpr int NSLOT = BM == 128 ? 1 : 2;
   constexpr int kOps = (BM + BN) * kStep;
   constexpr int kBuf0 = kOps > BM * 256 ? kOps : BM * 256;
-  constexpr int kBuf = kBuf0 > 2 * 32768 ? kBuf0 : 2 * 32768;
-  static_assert(2 * 32768 <= kBuf && BM * 256 <= kBuf, "epilogue LDS regions");
+  constexpr int kBuf = kBuf0 > NSLOT * 32768 ? kBuf0 : NSLOT * 32768;
+  static_assert(NSLOT * 32768 <= kBuf && BM * 256 <= kBuf, "epilogue LDS regions");
   __shared__ __align__(16) uint8_t buf0[kBuf];
   __shared__ __align__(16) uint8_t buf1[kBuf];
   __shared__ uint2 tbl[FMT == EPILORA_W_FP4 ? 256 : 1];
@@ -371,7 +374,7 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(GemmParams p, i
       const TokenSlot lead = tok[groups[gi]];
       const int a = lead.a, rank = lead.rank;
       const int nch = (rank + 31) / 32;  // 32-rank chunks
-      uint8_t* slot = buf1 + (u & 1) * 32768;
+      uint8_t* slot = buf1 + (NSLOT == 2 ? (u & 1) : 0) * 32768;
       if (rank & 7) {  // clear the ranks past the adapter's rank in its partial chunk
         const int cp = rank >> 3;
         for (int R = tid; R < 128; R += kWideThreads) {
@@ -389,7 +392,10 @@ __global__ __launch_bounds__(kWideThreads) void gemm_wide_kernel(GemmParams p, i
           bfr[i][kc] = kc < nch ? *reinterpret_cast<const uint4*>(slot + R * 256 + (((kc * 4 + (lane >> 4)) ^ (R & 15)) << 4))
                                 : zero4();
       }
-      if (u + 1 < units) b_dma(u + 1, (u + 1) & 1);
+      if (u + 1 < units) {
+        if (NSLOT == 1) __syncthreads();  // every wave has read the slot
+        b_dma(u + 1, NSLOT == 2 ? (u + 1) & 1 : 0);
+      }
 #pragma unroll
       for (int tb = 0; tb < TM; ++tb) {
         const int tt = wm * WM + tb * 16 + (lane & 15);
@@ -464,12 +470,13 @@ static void launch_wide(const GemmParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((gemm_wide_kernel<FMT, BM, BN>), dim3(tm * tn), dim3(kWideThreads), 0, stream, p, tm, tn);
 }
 
-// Tile shape: the largest tile that still gives every compute unit a tile
-// in the first round.
+// Tile shape: with adapters 128 x 128 (two workgroups per compute unit hide
+// each other's epilogue); otherwise the largest tile that still gives every
+// compute unit a tile in the first round.
 template <int FMT>
 static void dispatch_wide(const GemmParams& p, hipStream_t stream) {
   const int64_t cus = 256;
-  if (cdiv(p.M, 256) * cdiv(p.N, 128) >= cus) launch_wide<FMT, 256, 128>(p, stream);
+  if (p.z == nullptr && cdiv(p.M, 256) * cdiv(p.N, 128) >= cus) launch_wide<FMT, 256, 128>(p, stream);
   else launch_wide<FMT, 128, 128>(p, stream);
 }
 
