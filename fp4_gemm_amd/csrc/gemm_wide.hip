@@ -470,13 +470,15 @@ static void launch_wide(const GemmParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((gemm_wide_kernel<FMT, BM, BN>), dim3(tm * tn), dim3(kWideThreads), 0, stream, p, tm, tn);
 }
 
-// Tile shape: with adapters 128 x 128 (two workgroups per compute unit hide
-// each other's epilogue); otherwise the largest tile that still gives every
-// compute unit a tile in the first round.
+// Tile shape: the largest tile that still gives every compute unit a tile
+// in the first round; but with adapters, where 256 x 128 tiles would take
+// several rounds, 128 x 128 (two workgroups per compute unit hide each
+// other's epilogue).
 template <int FMT>
 static void dispatch_wide(const GemmParams& p, hipStream_t stream) {
   const int64_t cus = 256;
-  if (p.z == nullptr && cdiv(p.M, 256) * cdiv(p.N, 128) >= cus) launch_wide<FMT, 256, 128>(p, stream);
+  const int64_t wide_tiles = cdiv(p.M, 256) * cdiv(p.N, 128);
+  if (wide_tiles >= cus && (p.z == nullptr || wide_tiles <= cus)) launch_wide<FMT, 256, 128>(p, stream);
   else launch_wide<FMT, 128, 128>(p, stream);
 }
 
