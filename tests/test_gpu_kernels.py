@@ -291,6 +291,23 @@ def test_decode_matches_separate_and_oracle(M, K, N, L, r, kind, use_mask, use_r
     assert ep.epilora_device_error(fused["ws"]) == 0
 
 
+def test_decode_workspace_shared_by_different_calls():
+    # The fused path hands z over in the workspace: every call must see only
+    # its own z.  Two layers of one shape and one of another share a
+    # workspace; each call equals its own separate calls bit for bit (a z
+    # left over from the previous call would change y).
+    say("decode: one workspace, different inputs and shapes in turn")
+    d1 = DeviceGemm(custom_layer("w1", 1201, 16, 2048, 512, 4, 64, [0, 1, 2, 3] * 4).gemms[0])
+    d2 = DeviceGemm(custom_layer("w2", 1202, 16, 2048, 512, 4, 64, [3, 2, -1, 0] * 4).gemms[0])
+    d3 = DeviceGemm(custom_layer("w3", 1203, 3, 256, 384, 2, 16, [1, 0, 1]).gemms[0])
+    ws = ep.new_workspace(ep.OP_DECODE, 16, 512, 2048, 64)
+    for d in (d1, d2, d3, d1, d2):
+        fused = d.decode(ws=ws)
+        sep = d.separate()
+        assert torch.equal(fused["y"], sep["y"])
+        assert ep.epilora_device_error(ws) == 0
+
+
 def test_decode_base_only():
     lay = custom_layer("db", 950, 3, 512, 256, 1, 16, [-1, -1, -1])
     d = DeviceGemm(lay.gemms[0])
