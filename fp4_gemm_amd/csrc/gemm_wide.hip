@@ -149,12 +149,17 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(BM
   // positions.
   const int c0 = (lane >> 4) * 2;
   // The tile's token indices and mask bytes, requested now and used only by
-  // the epilogue (thread t holds token m0 + t).
-  int pre_a = -1, pre_m = 1;
-  if (p.z != nullptr && tid < BM && m0 + tid < p.M) {
-    pre_a = p.ad.idx[m0 + tid];
-    if (p.ad.mask != nullptr) pre_m = p.ad.mask[m0 + tid];
-  }
+  // the epilogue (thread t holds token m0 + t).  The loads are unconditional
+  // and bounds-checked (past M, without adapters or without a mask they read
+  // zero) and nothing tests them before the epilogue: a load under a branch
+  // let the compiler test the mask byte at once, which held the operand
+  // requests behind it.
+  const uint32_t tok_rows = p.z != nullptr ? (uint32_t)rows_a : 0u;
+  const auto rI = make_rsrc(p.z != nullptr ? p.ad.idx + m0 : nullptr, 4u * tok_rows);
+  const auto rM = make_rsrc(p.ad.mask != nullptr ? p.ad.mask + m0 : nullptr, p.ad.mask != nullptr ? tok_rows : 0u);
+  const uint32_t tt0 = tid < BM ? (uint32_t)tid : 0u;
+  const int pre_a = (int)buf_load4<kCached>(rI, 4u * tt0);
+  const int pre_m = (int)__builtin_amdgcn_raw_buffer_load_b8(rM, tt0, 0, 0);
   const int nk = (int)cdiv(K, kStep);
   const int nk2 = nk + (nk & 1);
   i32x8 af[TM], bf[TN];
@@ -295,7 +300,7 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(BM
           if (n0 == 0) atomic_or_relaxed(p.ctrl + kCtrlError, EPILORA_DEV_BAD_INDEX);
           a = -1;
         }
-        if (a >= 0 && pre_m == 0) a = -1;
+        if (a >= 0 && p.ad.mask != nullptr && pre_m == 0) a = -1;
         if (a >= 0) {
           rk = p.ad.ranks != nullptr ? p.ad.ranks[a] : r;
           rk = rk < r ? rk : r;
