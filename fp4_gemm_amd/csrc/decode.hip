@@ -23,9 +23,9 @@
 //                              only once all their tiles are in, before the
 //                              epilogues.
 // Data crosses workgroups only through device-coherent stores and loads
-// (sc1), and a producer bumps its flag (a relaxed agent-scope atomic) only
-// after its stores have completed, so no workgroup has to write back or
-// invalidate its L2.  Workgroups are dispatched in index order, so the
+// (sc1): z words in place, the quantized rows behind a flag that their
+// producer bumps (a relaxed agent-scope atomic) only after its stores have
+// completed, so no workgroup has to write back or invalidate its L2.  Workgroups are dispatched in index order, so the
 // producers are resident before any consumer spins; every wait is bounded by
 // a wall-clock limit and a timeout raises EPILORA_DEV_WAIT_TIMEOUT instead of
 // hanging.  The last GEMM workgroup to finish puts the flags back to zero and
@@ -43,7 +43,7 @@ struct DecodeParams {
   ShrinkParams s;
   int nq, ns, tiles;
   int count_q;  // the GEMM workgroups wait for the quantized rows
-  int flags;    // some flag is counted: the GEMM workgroups reset them at the end
+  int flags;    // a flag is counted or z handed over: the GEMM workgroups reset / clear at the end
   int* done;    // kDoneGroups sub-counters, kDoneStride words apart
 };
 
