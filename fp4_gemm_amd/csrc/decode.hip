@@ -47,7 +47,7 @@ struct DecodeParams {
   int* done;    // kDoneGroups sub-counters, kDoneStride words apart
 };
 
-template <int MB, int FMT, int NW, bool XLDS>
+template <int MB, int FMT, int NW, bool XLDS, int UB = 0>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((XLDS && NW == 8) ? 4 : 2))) void decode_kernel(DecodeParams p) {
   extern __shared__ __align__(16) char smem[];
   const GemmParams& g = p.job.g;
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((XLDS &
 
   // ---- GEMM workgroup (persistent over its tiles)
   {
-    Skinny<MB, FMT, NW, XLDS, true> sk(p.job, smem, bid - p.nq - p.ns);
+    Skinny<MB, FMT, NW, XLDS, true, UB> sk(p.job, smem, bid - p.nq - p.ns);
     sk.run();
   }
   if (!p.flags) return;
@@ -114,8 +114,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((XLDS &
   }
 }
 
-template <int MB, int FMT, int NW, bool XLDS>
-static void launch_decode_x(DecodeParams& p, bool want_xq, hipStream_t stream) {
+template <int MB, int FMT, int NW, bool XLDS, int UB>
+static void launch_decode_u(DecodeParams& p, bool want_xq, hipStream_t stream) {
   const GemmParams& g = p.job.g;
   const int r = p.s.ad.r;
   p.nq = (XLDS && !want_xq) ? 0 : (int)g.M;
@@ -127,9 +127,19 @@ static void launch_decode_x(DecodeParams& p, bool want_xq, hipStream_t stream) {
   if (shrink_lds > lds) lds = shrink_lds;
   // The quantizing and shrink workgroups are dispatched first and hold their
   // slots only until they finish.
-  p.job.gwgs = skinny_groups(g.N, resident_groups(decode_kernel<MB, FMT, NW, XLDS>, NW * 64, lds), StashCfg<MB>::n);
+  p.job.gwgs = skinny_groups(g.N, resident_groups(decode_kernel<MB, FMT, NW, XLDS, UB>, NW * 64, lds), StashCfg<MB>::n);
   const unsigned grid = (unsigned)(p.nq + p.ns + p.job.gwgs);
-  hipLaunchKernelGGL((decode_kernel<MB, FMT, NW, XLDS>), dim3(grid), dim3(NW * 64), lds, stream, p);
+  hipLaunchKernelGGL((decode_kernel<MB, FMT, NW, XLDS, UB>), dim3(grid), dim3(NW * 64), lds, stream, p);
+}
+
+// Single-token-block eight-wave grids over short K and at most 512 tiles
+// (the Llama-8B qkv and o projections) stream faster in single-step batches;
+// longer streams (gate_up, down) in two-step batches, as measured.
+template <int MB, int FMT, int NW, bool XLDS>
+static void launch_decode_x(DecodeParams& p, bool want_xq, hipStream_t stream) {
+  const GemmParams& g = p.job.g;
+  if (MB == 1 && NW == 8 && g.K <= 4096 && cdiv(g.N, 16) <= 512) launch_decode_u<MB, FMT, NW, XLDS, 1>(p, want_xq, stream);
+  else launch_decode_u<MB, FMT, NW, XLDS, 0>(p, want_xq, stream);
 }
 
 template <int MB, int FMT>

@@ -224,11 +224,12 @@ struct SelfQuant {
   }
 };
 
-template <int MB, int FMT, int NW, bool XLDS, bool FUSED>
+// UB (> 0) overrides the steps per load batch.
+template <int MB, int FMT, int NW, bool XLDS, bool FUSED, int UB = 0>
 struct Skinny {
   // The fused kernel's 8-wave workgroups take half batches so that two fit
   // on a compute unit (four waves per SIMD), beside a producer workgroup.
-  static constexpr int U = (FUSED && NW == 8 && MB == 1) ? 2 : SkinnyCfg<MB>::U;
+  static constexpr int U = UB > 0 ? UB : ((FUSED && NW == 8 && MB == 1) ? 2 : SkinnyCfg<MB>::U);
   static constexpr int T = MB * 16;
   static constexpr int XPOL = FUSED ? kCoherent : kCached;
 
