@@ -91,35 +91,56 @@ class Proj:
         self.ws_shr = ep.new_workspace(ep.OP_SHRINK, self.M, self.N, self.K, self.r)
         self.copies = copies
 
+    def with_batch(self, g):
+        """The same projection (the same device weights and adapters) for the
+        batch of another layer of the same shapes."""
+        q = Proj.__new__(Proj)
+        q.__dict__.update(self.__dict__)
+        lay = g.layer
+        q.g, q.M = g, g.M
+        q.x = dev(g.x())
+        q.idx = dev(lay.idx.astype(np.int32))
+        q.mask = None if lay.mask is None else dev(lay.mask.astype(np.uint8))
+        q.ranks = None if lay.ranks is None else dev(lay.ranks.astype(np.int32))
+        q.y = torch.empty(q.M, q.N, dtype=torch.bfloat16, device=DEV)
+        q.xq = torch.empty(q.M, q.K, dtype=torch.uint8, device=DEV)
+        q.sx = torch.empty(q.M, dtype=torch.float32, device=DEV)
+        q.z = torch.empty(q.M, q.r, dtype=torch.float32, device=DEV)
+        q.ws_dec = ep.new_workspace(ep.OP_DECODE, q.M, q.N, q.K, q.r)
+        q.ws_shr = ep.new_workspace(ep.OP_SHRINK, q.M, q.N, q.K, q.r)
+        return q
+
     def adapters(self, c):
+        c %= self.copies
         return dict(B=self.B[c], idx=self.idx, ranks=self.ranks, mask=self.mask, scale=self.scale)
 
     # paths ------------------------------------------------------------------
     def fused(self, c):
-        w, kw = self.w[c]
-        ep.epilora_decode_lora(self.x, w, self.y, A=self.A[c], ws=self.ws_dec, xq_out=self.xq, sx_out=self.sx,
-                               **self.adapters(c), **kw)
+        w, kw = self.w[c % self.copies]
+        ep.epilora_decode_lora(self.x, w, self.y, A=self.A[c % self.copies], ws=self.ws_dec, xq_out=self.xq,
+                               sx_out=self.sx, **self.adapters(c), **kw)
 
     def fused_base(self, c):
-        w, kw = self.w[c]
+        w, kw = self.w[c % self.copies]
         ep.epilora_decode_lora(self.x, w, self.y, ws=self.ws_dec, xq_out=self.xq, sx_out=self.sx, **kw)
 
     def quant(self, c):
         ep.epilora_quant_act(self.x, self.xq, self.sx)
 
     def shrink(self, c):
-        ep.epilora_lora_shrink(self.x, self.A[c], self.idx, self.z, self.ws_shr, ranks=self.ranks, mask=self.mask)
+        ep.epilora_lora_shrink(self.x, self.A[c % self.copies], self.idx, self.z, self.ws_shr, ranks=self.ranks,
+                               mask=self.mask)
 
     def gemm_lora(self, c):
-        w, kw = self.w[c]
+        w, kw = self.w[c % self.copies]
         ep.epilora_gemm_lora(self.xq, self.sx, w, self.y, z=self.z, ws=self.ws_shr, **self.adapters(c), **kw)
 
     def gemm_base(self, c):
-        w, kw = self.w[c]
+        w, kw = self.w[c % self.copies]
         ep.epilora_gemm_lora(self.xq, self.sx, w, self.y, **kw)
 
     def expand(self, c):
-        ep.epilora_lora_expand_add(self.z, self.B[c], self.idx, self.scale, self.y, self.ws_shr,
+        ep.epilora_lora_expand_add(self.z, self.B[c % self.copies], self.idx, self.scale, self.y, self.ws_shr,
                                    ranks=self.ranks, mask=self.mask)
 
     # algorithmic counts -------------------------------------------------------
@@ -217,6 +238,37 @@ def per_call_us(projs, fn_names, steps, warmup):
     return 1000.0 * ms / ROTATE
 
 
+def decode_72b(steps, warmup):
+    """The 72B-shaped PreFT decode layer (qkv 8192->10240, o 8192->8192,
+    gate_up 8192->59136, down 29568->8192; 512 rank-16 adapters, Zipf(1.1)
+    tenants, the first ceil(0.75 M) tokens adapted) through the fused path at
+    M = 1, 8 and 64: microseconds per layer and the fraction of HBM peak over
+    the layer's algorithmic bytes.  One copy of the weights (878 MB per layer,
+    more than the 256 MB Infinity Cache) serves every batch."""
+    out = {}
+    base = None
+    for M in (1, 8, 64):
+        layer = config(4, M=M)
+        log(f"72B decode layer M={M} ...")
+        if base is None:
+            base = [Proj(g, copies=1) for g in layer.gemms]
+            projs = base
+        else:
+            projs = [p.with_batch(g) for p, g in zip(base, layer.gemms)]
+        torch.cuda.synchronize()
+        us, _ = per_step_us(projs, ["fused"], steps, warmup)
+        nbytes = sum(p.bytes() for p in projs)
+        out[f"M{M}"] = {"fused_us": round(us, 2), "bytes": nbytes, "GBps": round(nbytes / us / 1e3, 1),
+                        "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+                        "adapted_tokens": int((layer.mask != 0).sum()),
+                        "distinct_tenants": len(projs[0].adapter_ranks()[1])}
+        if projs is not base:
+            del projs
+    del base
+    torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(layer, frac=4, min_seconds=10.0, max_reps=1000):
     """The oracle on a bounded sample of the decode layer: every frac-th
     output channel of each projection (its weights quantized by the oracle
@@ -309,6 +361,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-72b", action="store_true", help="skip the 72B-shaped decode layer")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only the dispatches the HBM-counter runs measure (see traffic_probe)")
     args = ap.parse_args()
@@ -364,6 +417,10 @@ def main():
                 del p
                 torch.cuda.empty_cache()
 
+    d72 = None
+    if not args.no_72b:
+        d72 = decode_72b(max(20, args.steps // 4), max(4, args.warmup // 4))
+
     cpu = None
     if not args.no_cpu:
         log("timing the CPU oracle on a sample ...")
@@ -400,6 +457,7 @@ def main():
                      "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
                      "algorithmic_bytes": dom.bytes(), "launch_us": dom_us},
         "prefill": prefill,
+        "decode_72b_preft": d72,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
