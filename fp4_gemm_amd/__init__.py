@@ -18,7 +18,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libepilora.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
-DEV_BAD_INDEX, DEV_WAIT_TIMEOUT = 1, 2
+DEV_BAD_INDEX, DEV_WAIT_TIMEOUT, DEV_INTERNAL = 1, 2, 4
 W_FP8, W_FP4 = 0, 1
 OP_SHRINK, OP_GEMM, OP_EXPAND, OP_DECODE, OP_QUANT_W4 = 1, 2, 3, 4, 5
 DECODE_MAX_M = 64
@@ -58,6 +58,7 @@ SIGNATURES = {
     "epilora_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "epilora_workspace_bytes": (_SZ, [_I32, _I64, _I64, _I64, _I32]),
     "epilora_workspace_init": (ctypes.c_int, [_P, _SZ, _P]),
+    "epilora_workspace_force_timeout": (ctypes.c_int, [_P, _SZ, _I32, _P]),
     "epilora_device_error": (ctypes.c_int, [_P, _I32, ctypes.POINTER(_I32), _P]),
     "epilora_quant_act": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _I64, _P, _P]),
     "epilora_quant_weight_fp8": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
@@ -126,6 +127,12 @@ def new_workspace(op, M, N, K, r, device="cuda"):
     ws = torch.empty(max(epilora_workspace_bytes(op, M, N, K, r), 256), dtype=torch.uint8, device=device)
     epilora_workspace_init(ws)
     return ws
+
+
+def epilora_workspace_force_timeout(ws, on, stream=None):
+    _need(ws, torch.uint8, "ws")
+    _check("epilora_workspace_force_timeout",
+           lib().epilora_workspace_force_timeout(_ptr(ws), ws.numel(), int(bool(on)), _stream(stream)))
 
 
 def epilora_device_error(ws, clear=True, stream=None):

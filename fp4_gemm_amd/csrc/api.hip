@@ -110,6 +110,13 @@ int epilora_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   return hip_status(launch_fill_u32(ws, 0u, (int64_t)(ws_bytes / 4), as_stream(stream)));
 }
 
+int epilora_workspace_force_timeout(void* ws, size_t ws_bytes, int32_t on, void* stream) {
+  if (ws == nullptr || ws_bytes < kCtrlBytes) return EPILORA_ERR_WORKSPACE;
+  if (!aligned(ws, 256)) return EPILORA_ERR_UNSUPPORTED;
+  int* word = reinterpret_cast<int*>(ws) + kCtrlForceTimeout;
+  return hip_status(launch_fill_u32(word, on != 0 ? 1u : 0u, 1, as_stream(stream)));
+}
+
 int epilora_device_error(void* ws, int32_t clear, int32_t* out_code, void* stream) {
   if (ws == nullptr || out_code == nullptr) return EPILORA_ERR_INVALID_ARG;
   hipStream_t s = as_stream(stream);

@@ -72,8 +72,8 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((XLDS &
     int s_begin, s_end;
     shrink_range(p.s, split, s_begin, s_end);
     float* red = reinterpret_cast<float*>(smem);
-    shrink_tile<NW>(p.s, (int64_t)tile * kShrinkTokens, s_begin, s_end, red, split == 0);
-    shrink_finish<NW>(p.s, tile, split, red);
+    const uint64_t active = shrink_tile<NW>(p.s, (int64_t)tile * kShrinkTokens, s_begin, s_end, red, split == 0);
+    shrink_finish<NW>(p.s, tile, split, red, active);
     return;
   }
 

@@ -11,6 +11,7 @@ namespace epilora {
 constexpr size_t kCtrlBytes = 256;
 constexpr int kCtrlError = 0;      // device error word (sticky bits)
 constexpr int kCtrlAmax = 1;       // 4-bit weight quantizer: global amax bits
+constexpr int kCtrlForceTimeout = 2;  // nonzero: the fused path's bounded waits give up at once
 constexpr int kCtrlQuantDone = 8;  // fused path: rows quantized
 constexpr int kCtrlGemmDone = 10;  // fused path: GEMM workgroups finished
 

@@ -10,8 +10,8 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
   extern __shared__ float red[];  // [4 waves][16 tokens][r]
   int s_begin, s_end;
   shrink_range(p, blockIdx.y, s_begin, s_end);
-  shrink_tile<4>(p, (int64_t)blockIdx.x * kShrinkTokens, s_begin, s_end, red, blockIdx.y == 0);
-  shrink_finish<4>(p, blockIdx.x, blockIdx.y, red);
+  const uint64_t active = shrink_tile<4>(p, (int64_t)blockIdx.x * kShrinkTokens, s_begin, s_end, red, blockIdx.y == 0);
+  shrink_finish<4>(p, blockIdx.x, blockIdx.y, red, active);
 }
 
 // ---------------------------------------------------------------------------
@@ -112,7 +112,7 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_wide_kernel(ShrinkParam
       *reinterpret_cast<float4*>(&red[(16 * wave + col) * r + jb * 16 + 4 * grp]) =
           make_float4(acc[jb][0], acc[jb][1], acc[jb][2], acc[jb][3]);
   __syncthreads();
-  shrink_finish<4, kShrinkWideTokens>(p, tile, split, red);
+  shrink_finish<4, kShrinkWideTokens>(p, tile, split, red, __ballot(a_l >= 0));
 }
 
 hipError_t launch_shrink(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const AdapterArgs& ad,

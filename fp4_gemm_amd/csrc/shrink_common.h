@@ -46,10 +46,11 @@ struct ShrinkParams {
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
 // One workgroup's sums for 16 tokens over its K steps; leaves the [16][r]
-// result in `red` (LDS of kShrinkWaves * 16 * r floats).  Every thread of the
-// block must call it.
+// result in `red` (LDS of kShrinkWaves * 16 * r floats) and returns the
+// tile's active tokens as a bit mask (bit i: token t0 + i).  Every thread of
+// the block must call it.
 template <int NW>
-__device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int64_t t0, int s_begin, int s_end, float* red,
+__device__ __forceinline__ uint64_t shrink_tile(const ShrinkParams& p, int64_t t0, int s_begin, int s_end, float* red,
                                             bool report) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
@@ -67,7 +68,8 @@ __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int64_t t0, i
 #pragma unroll
   for (int j = 0; j < kMaxJB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  uint64_t pending = working ? __ballot(lane < 16 && a_c >= 0) : 0;
+  const uint64_t active = __ballot(lane < 16 && a_c >= 0);
+  uint64_t pending = working ? active : 0;
   while (pending) {
     const int leader = __ffsll((unsigned long long)pending) - 1;
     const int a = __shfl(a_c, leader);
@@ -117,6 +119,7 @@ __device__ __forceinline__ void shrink_tile(const ShrinkParams& p, int64_t t0, i
     red[e] = v;
   }
   __syncthreads();
+  return active;
 }
 
 // The fixed-order sum of the split partials ([splits][M][r] fp32) of the
@@ -202,8 +205,17 @@ __device__ __forceinline__ void shrink_store_partial(const ShrinkParams& p, int 
 // and the partials are written and read device-coherently.  Returns true in
 // the workgroup that wrote the tile's final z, after every one of its z
 // stores has completed.
+// `active`: the tile's active tokens (bit i: token t0 + i).  The separate
+// shrink writes every row (zeros for inactive tokens).  The fused path
+// (zflip != 0) stores only the rows of active tokens: those are exactly the
+// words every consumer polls, so each z store of a call has been seen by
+// every consumer before any of them counts itself done, and the clear of the
+// region by the last one is ordered after all of them.  A store to a row no
+// consumer polls could otherwise land after that clear and survive, as a
+// stale nonzero word, into the next call on the same workspace.
 template <int NW, int TT = kShrinkTokens>
-__device__ __forceinline__ bool shrink_finish(const ShrinkParams& p, int tile, int split, float* red) {
+__device__ __forceinline__ bool shrink_finish(const ShrinkParams& p, int tile, int split, float* red,
+                                              uint64_t active) {
   __shared__ int last;
   const int64_t t0 = (int64_t)tile * TT;
   const int r = p.ad.r;
@@ -211,10 +223,11 @@ __device__ __forceinline__ bool shrink_finish(const ShrinkParams& p, int tile, i
   const uint32_t tile_bytes = (uint32_t)(rows * r * 4);
   const auto zr = make_rsrc(p.z + t0 * r, tile_bytes);
   const uint32_t f = p.zflip;
+  auto keep = [&](int e) { return f == 0u || ((active >> (e / r)) & 1ull) != 0; };  // e: a word of the tile
   if (p.splits == 1) {
     for (int e = 4 * threadIdx.x; e < rows * r; e += 4 * NW * kWave) {
       const uint4 v = *reinterpret_cast<const uint4*>(&red[e]);
-      buf_store16<kCoherent>(zr, 4 * e, make_uint4(v.x ^ f, v.y ^ f, v.z ^ f, v.w ^ f));
+      if (keep(e)) buf_store16<kCoherent>(zr, 4 * e, make_uint4(v.x ^ f, v.y ^ f, v.z ^ f, v.w ^ f));
     }
     wait_all_memory();
     __syncthreads();
@@ -226,8 +239,9 @@ __device__ __forceinline__ bool shrink_finish(const ShrinkParams& p, int tile, i
   if (!last) return false;
   // `red` is free again and holds the chunk sums.
   combine_partials<NW * kWave>(p.partials, p.splits, p.M, t0, rows, r, red, [&](int q, const float4& v) {
-    buf_store16<kCoherent>(zr, 16u * q, make_uint4(__float_as_uint(v.x) ^ f, __float_as_uint(v.y) ^ f,
-                                                   __float_as_uint(v.z) ^ f, __float_as_uint(v.w) ^ f));
+    if (keep(4 * q))
+      buf_store16<kCoherent>(zr, 16u * q, make_uint4(__float_as_uint(v.x) ^ f, __float_as_uint(v.y) ^ f,
+                                                     __float_as_uint(v.z) ^ f, __float_as_uint(v.w) ^ f));
   });
   if (threadIdx.x == 0) store_relaxed(&p.counters[tile], 0);
   wait_all_memory();

@@ -105,11 +105,16 @@ struct SkinnyBatch {
 
 // Thread 0 polls *flag (device-coherent loads, s_sleep between them) until it
 // reaches target, the wall-clock limit passes, or another workgroup has
-// already timed out; the verdict is broadcast through LDS.
-__device__ __forceinline__ bool wait_flag(int* flag, int target, int64_t ticks, int* err, int* verdict) {
+// already timed out; the verdict is broadcast through LDS.  A nonzero
+// `force` word (set from the host to test the timeout path) ends the wait at
+// once as expired.
+__device__ __forceinline__ bool wait_flag(int* flag, int target, int64_t ticks, int* err, int* force, int* verdict) {
   if (threadIdx.x == 0) {
     int ok = 1;
-    if (load_relaxed(flag) < target) {
+    const int forced = load_relaxed(force);
+    if (forced != 0) {
+      ok = 0;
+    } else if (load_relaxed(flag) < target) {
       const int64_t start = wall_clock64();
       while (load_relaxed(flag) < target) {
         if (wall_clock64() - start > ticks || (load_relaxed(err) & EPILORA_DEV_WAIT_TIMEOUT)) {
@@ -272,7 +277,10 @@ struct Skinny {
     se = min(steps, sb + spw);
     nb = (int)cdiv(spw, U);
     int mine = (int)cdiv(J.tiles - g, J.gwgs);
-    if (FUSED && mine > StashCfg<MB>::n) mine = 0;  // never launched so (the stash holds n tiles)
+    if (FUSED && mine > StashCfg<MB>::n) {  // the host never launches so (the stash holds n tiles)
+      mine = 0;
+      if (threadIdx.x == 0 && p.ctrl != nullptr) atomic_or_relaxed(p.ctrl + kCtrlError, EPILORA_DEV_INTERNAL);
+    }
     total = mine * nb;
     adapters = p.z != nullptr;
     gscale = FMT == EPILORA_W_FP4 ? weight_scale<FMT>(p.wt, 0) : 0.f;
@@ -495,7 +503,9 @@ struct Skinny {
   // until its producer stores it (as its bitwise complement), so the
   // workgroup polls the words of its active tokens until none is missing,
   // staging them into LDS (rows of inactive tokens as zero), under the
-  // wall-clock limit.  Returns false on a timeout.  Ends with a barrier.
+  // wall-clock limit.  Returns false on a timeout (or when the host has set
+  // the workspace's force-timeout word, read with the first poll).  Ends with
+  // a barrier.
   __device__ __forceinline__ bool poll_z() const {
     const int r = p.ad.r;
     const int n = (int)p.M * r;
@@ -503,6 +513,7 @@ struct Skinny {
     int* err = p.ctrl + kCtrlError;
     const int64_t start = wall_clock64();
     for (;;) {
+      const int forced = threadIdx.x == 0 ? load_relaxed(p.ctrl + kCtrlForceTimeout) : 0;
       int missing = 0;
       for (int e = threadIdx.x; e < n; e += NW * kWave) {
         if (tok[e / r].a < 0) {
@@ -519,7 +530,8 @@ struct Skinny {
       __syncthreads();
       if (threadIdx.x == 0) {
         int state = *verdict;  // 0: complete, 1: poll again, 2: give up
-        if (state != 0 && (wall_clock64() - start > J.wait_ticks || (load_relaxed(err) & EPILORA_DEV_WAIT_TIMEOUT)))
+        if (forced != 0 ||
+            (state != 0 && (wall_clock64() - start > J.wait_ticks || (load_relaxed(err) & EPILORA_DEV_WAIT_TIMEOUT))))
           state = 2;
         *verdict = state;
       }
@@ -640,7 +652,7 @@ struct Skinny {
     for (int s = 0; s < StashCfg<MB>::n; ++s) pw[s] = (FUSED && s < total / nb) ? row_wscale(n0_of(s * nb)) : 0.f;
 
     if (FUSED && !XLDS) {  // the quantized rows come from other workgroups
-      ok = wait_flag(J.qflag, J.qtarget, J.wait_ticks, err, verdict);
+      ok = wait_flag(J.qflag, J.qtarget, J.wait_ticks, err, p.ctrl + kCtrlForceTimeout, verdict);
       const auto sr = make_rsrc(p.sx, (uint32_t)(M * 4));
       for (int t = threadIdx.x; t < M; t += NT) sxs[t] = __uint_as_float(buf_load4<kCoherent>(sr, 4u * t));
       __syncthreads();

@@ -69,8 +69,11 @@ enum epilora_status {
 /* Bits of the device error word kept in a workspace (sticky until cleared). */
 enum epilora_device_error_bits {
   EPILORA_DEV_BAD_INDEX = 1,   /* an index outside [-1, L) was treated as -1 */
-  EPILORA_DEV_WAIT_TIMEOUT = 2 /* the fused path's bounded wait expired; the
-                                  outputs of that call are not valid */
+  EPILORA_DEV_WAIT_TIMEOUT = 2, /* the fused path's bounded wait expired; the
+                                   outputs of that call are not valid */
+  EPILORA_DEV_INTERNAL = 4      /* a workgroup was given more output tiles
+                                   than it can hold (a library bug, never
+                                   expected); the outputs are not valid */
 };
 
 /* Weight formats. */
@@ -154,6 +157,15 @@ size_t epilora_workspace_bytes(int32_t op, int64_t M, int64_t N, int64_t K,
 /* Zero a workspace (a fill kernel, safe inside graph capture).  Required once
  * after allocation; every call leaves its counters at zero again. */
 int epilora_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Test hook for the failure path of the fused decode path: with on != 0,
+ * every bounded wait of epilora_decode_lora calls on this workspace gives up
+ * at once, as if its wall-clock bound had expired (the kernels still run to
+ * their end; the call raises EPILORA_DEV_WAIT_TIMEOUT and its outputs are
+ * not valid).  Sets one word of the workspace's control block with a fill
+ * kernel on `stream`; epilora_workspace_init clears it again. */
+int epilora_workspace_force_timeout(void* ws, size_t ws_bytes, int32_t on,
+                                    void* stream);
 
 /* Read the device error word of a workspace into *out_code: enqueues a copy
  * on `stream` and waits for it (a synchronizing diagnostic, not for use

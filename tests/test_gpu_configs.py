@@ -106,13 +106,30 @@ def test_config4_72b_preft(name):
 
 @pytest.mark.parametrize("wfmt,segments,name", [
     ("fp8", 16, "gate_up"), ("fp8", 16, "down"), ("fp4", 16, "gate_up"), ("fp4", 16, "down"),
-    ("fp8", 32, "gate_up"),
+    ("fp8", 32, "gate_up"), ("fp8", 32, "down"), ("fp4", 32, "gate_up"), ("fp4", 32, "down"),
 ])
 def test_config5_prefill(wfmt, segments, name):
     say(f"config 5 {wfmt} {segments} segments {name}")
     lay = config(5, segments=segments, wfmt=wfmt)
     d = DeviceGemm(lay.gemm(name), wfmt)
     out = d.separate()
-    rows = sample(d.M, 128, 50 + segments)
-    check(d, out, rows=rows, seed=51, what=f"cfg5 {wfmt} {name}")
+    # a seeded sample plus the first and last token of every segment
+    starts = np.flatnonzero(np.r_[True, lay.idx[1:] != lay.idx[:-1]])
+    ends = np.r_[starts[1:] - 1, d.M - 1]
+    rows = np.unique(np.concatenate([sample(d.M, 96, 50 + segments), starts, ends]))
+    ref = check(d, out, rows=rows, seed=51, what=f"cfg5 {wfmt} {name}")
     assert ep.epilora_device_error(out["ws"]) == 0
+    if wfmt == "fp4":
+        # Diagnostic: how far the GPU's 4-bit path (weights folded to FP8
+        # bytes) lies from exact NVFP4 arithmetic on the same codes.
+        import oracle
+        wc, bs, gs = ref["w"]["wc"], ref["w"]["bs"], ref["w"]["gs"]
+        wx = oracle.exact_decode_fp4(wc, bs, gs)
+        xq = to_np(out["xq"])[rows]
+        sx = to_np(out["sx"])[rows].astype(np.float64)
+        exact = (oracle.e4m3_decode(xq) @ wx.T) * sx[:, None]
+        base = ref["base"]
+        dev = np.abs(base - exact)
+        rms = np.sqrt(np.mean(exact ** 2))
+        say(f"  4-bit fold vs exact NVFP4 (base term): max|d|/rms {dev.max() / rms:.3e}  "
+            f"mean rel {dev.sum() / np.abs(exact).sum():.3e}")

@@ -316,3 +316,88 @@ def test_decode_base_only():
     ep.epilora_decode_lora(d.x, d.wq, y, sw=d.sw, ws=ws)
     xq, sx = d.quant()
     assert torch.equal(y, d.gemm(xq, sx))
+
+
+def test_decode_inactive_tiles_leave_no_stale_z():
+    # A fused call whose batch has one whole 16-token shrink tile without an
+    # active token (tokens 16-31) and one partly inactive tile (tokens 0-15),
+    # then calls on the same workspace in which those tokens are active: a z
+    # word left behind by the first call would be taken as the second call's
+    # published z.  Each call must equal its separate calls bit for bit.
+    say("decode: inactive shrink tiles, then the same tokens active")
+    M, K, N, L, r = 40, 1024, 256, 5, 32
+    idx_a = np.array([0, -1, 1, -1, 2, -1, 3, -1] * 2 + [-1] * 16 + [4, 0, 1, 2, 3, 4, 0, 1], np.int32)
+    mask_a = np.ones(M, np.uint8)
+    mask_a[8:16] = 0
+    idx_b = np.array([(t % L) for t in range(M)], np.int32)
+    ws = ep.new_workspace(ep.OP_DECODE, M, N, K, r)
+    da = DeviceGemm(custom_layer("stale_a", 1301, M, K, N, L, r, idx_a, mask=mask_a).gemms[0])
+    db = DeviceGemm(custom_layer("stale_b", 1302, M, K, N, L, r, idx_b).gemms[0])
+    for d in (da, db, da, db, db):
+        fused = d.decode(ws=ws)
+        sep = d.separate()
+        assert torch.equal(fused["y"], sep["y"])
+        assert ep.epilora_device_error(ws) == 0
+
+
+@pytest.mark.parametrize("M", [1, 24])
+def test_decode_forced_timeout_then_recovers(M):
+    # The failure path of the bounded waits, forced from the host: every wait
+    # gives up at once (M = 1: the wait for z; M = 24: also the wait for the
+    # quantized rows), every kernel still runs to its end, the call raises
+    # EPILORA_DEV_WAIT_TIMEOUT, and after epilora_workspace_init the next call
+    # on the workspace is bitwise correct again.
+    say(f"decode: forced timeout M={M}")
+    L, r = 3, 16
+    idx = np.arange(M, dtype=np.int32) % L
+    d = DeviceGemm(custom_layer("timeout", 1400 + M, M, 512, 384, L, r, idx).gemms[0])
+    ws = ep.new_workspace(ep.OP_DECODE, M, 384, 512, r)
+    ep.epilora_workspace_force_timeout(ws, True)
+    d.decode(ws=ws)
+    torch.cuda.synchronize()
+    assert ep.epilora_device_error(ws) & ep.DEV_WAIT_TIMEOUT
+    ep.epilora_workspace_init(ws)
+    fused = d.decode(ws=ws)
+    sep = d.separate()
+    assert torch.equal(fused["y"], sep["y"])
+    assert ep.epilora_device_error(ws) == 0
+
+
+def test_decode_graph_replays_are_deterministic():
+    # Bitwise reproducibility of the fused path over many replays of one
+    # captured graph (a layer's four projections on one shared workspace),
+    # with eager work and synchronizations between replays; stops at the
+    # first replay that differs.
+    say("decode: 200 graph replays, bitwise equal")
+    from workloads import config
+    lay = config(3)
+    ds = [DeviceGemm(g) for g in lay.gemms]
+    ws = ep.new_workspace(ep.OP_DECODE, lay.M, max(d.N for d in ds), max(d.K for d in ds), lay.r)
+    ys = [torch.empty(d.M, d.N, dtype=torch.bfloat16, device=DEV) for d in ds]
+
+    def step():
+        for d, y in zip(ds, ys):
+            ep.epilora_decode_lora(d.x, d.wq, y, A=d.A, B=d.B, idx=d.idx, ranks=d.ranks, mask=d.mask,
+                                   scale=d.scale, ws=ws, **d.wkw)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    ref = [y.clone() for y in ys]
+    for d, y in zip(ds, ref):
+        assert torch.equal(y, d.separate()["y"])
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for i in range(200):
+        for y in ys:
+            y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        for j, (y, y0) in enumerate(zip(ys, ref)):
+            assert torch.equal(y, y0), f"replay {i}, projection {j}"
+    assert ep.epilora_device_error(ws) == 0
