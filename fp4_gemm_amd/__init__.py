@@ -67,6 +67,7 @@ SIGNATURES = {
     "epilora_gemm_lora": (ctypes.c_int, [ctypes.POINTER(LayerArgs), _P]),
     "epilora_lora_expand_add": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _I32, _P, _P, _P, _F, _P, _I64, _P, _SZ, _P]),
     "epilora_decode_lora": (ctypes.c_int, [ctypes.POINTER(LayerArgs), _P]),
+    "epilora_decode_lora_noalloc": (ctypes.c_int, [ctypes.POINTER(LayerArgs), _P]),
 }
 
 
@@ -230,9 +231,22 @@ def epilora_gemm_lora(xq, sx, w, y, *, sw=None, bs=None, gs=None, z=None, B=None
     _check("epilora_gemm_lora", lib().epilora_gemm_lora(ctypes.byref(a), _stream(stream)))
 
 
+def epilora_decode_lora_noalloc(x, w, y, *, sw=None, bs=None, gs=None, A=None, B=None, idx=None, ranks=None,
+                                mask=None, scale=1.0, xq_out=None, sx_out=None, stream=None):
+    """The fused decode path on the library's fixed per-GPU scratch (no
+    workspace argument; see the header)."""
+    a = _decode_args(x, w, y, sw, bs, gs, A, B, idx, ranks, mask, scale, None, xq_out, sx_out)
+    _check("epilora_decode_lora_noalloc", lib().epilora_decode_lora_noalloc(ctypes.byref(a), _stream(stream)))
+
+
 def epilora_decode_lora(x, w, y, *, sw=None, bs=None, gs=None, A=None, B=None, idx=None, ranks=None, mask=None,
                         scale=1.0, ws=None, xq_out=None, sx_out=None, stream=None):
     """The fused decode path: quantization, shrink and GEMM in one launch."""
+    a = _decode_args(x, w, y, sw, bs, gs, A, B, idx, ranks, mask, scale, ws, xq_out, sx_out)
+    _check("epilora_decode_lora", lib().epilora_decode_lora(ctypes.byref(a), _stream(stream)))
+
+
+def _decode_args(x, w, y, sw, bs, gs, A, B, idx, ranks, mask, scale, ws, xq_out, sx_out):
     _need(x, torch.bfloat16, "x"); _need(y, torch.bfloat16, "y")
     _need(xq_out, torch.uint8, "xq_out"); _need(sx_out, torch.float32, "sx_out")
     a = LayerArgs()
@@ -246,4 +260,4 @@ def epilora_decode_lora(x, w, y, *, sw=None, bs=None, gs=None, A=None, B=None, i
     a.ldq_out = 0 if xq_out is None else _ld(xq_out)
     if ws is not None:
         a.ws, a.ws_bytes = _ptr(ws), ws.numel()
-    _check("epilora_decode_lora", lib().epilora_decode_lora(ctypes.byref(a), _stream(stream)))
+    return a

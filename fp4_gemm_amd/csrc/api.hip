@@ -1,6 +1,8 @@
 // The C ABI (include/epilora.h): host-side validation, workspace sizing and
 // dispatch to the kernels.  No entry point allocates memory or synchronizes
 // the stream, except the diagnostic epilora_device_error.
+#include <atomic>
+
 #include "../../include/epilora.h"
 #include "kernels.h"
 #include "layout.h"
@@ -72,6 +74,54 @@ AdapterArgs adapters_of(const epilora_layer_args* a, bool on) {
   d.L = a->L; d.r = a->r; d.scale = a->scale;
   if (!on) { d.r = 16; d.L = 0; }
   return d;
+}
+
+// Host-side checks of a fused decode call (everything except the
+// workspace); `r` receives the slot width the workspace is sized for.
+int check_decode(const epilora_layer_args* a, int32_t& r) {
+  if (a->M < 0 || a->N < 0 || a->K < 0) return EPILORA_ERR_INVALID_ARG;
+  if (a->M == 0 || a->N == 0) return EPILORA_OK;
+  if (a->M > EPILORA_DECODE_MAX_M) return EPILORA_ERR_UNSUPPORTED;
+  if (a->x == nullptr || a->y == nullptr) return EPILORA_ERR_INVALID_ARG;
+  int st = check_weights(a);
+  if (st != EPILORA_OK) return st;
+  if (a->ldx < a->K || a->ldy < a->N) return EPILORA_ERR_INVALID_ARG;
+  if (a->ldx % 16 != 0 || !aligned(a->x, 16) || !aligned(a->y, 2)) return EPILORA_ERR_UNSUPPORTED;
+  if (a->xq_out != nullptr) {
+    if (a->ldq_out < a->K) return EPILORA_ERR_INVALID_ARG;
+    if (a->ldq_out % 16 != 0 || !aligned(a->xq_out, 16)) return EPILORA_ERR_UNSUPPORTED;
+  }
+  if (a->sx_out != nullptr && !aligned(a->sx_out, 4)) return EPILORA_ERR_UNSUPPORTED;
+  r = 16;
+  if (a->idx != nullptr) {
+    st = check_adapters(a->L, a->r, a->A, true, a->B, true, a->ranks, a->idx);
+    if (st != EPILORA_OK) return st;
+    r = a->r;
+  }
+  return EPILORA_OK;
+}
+
+// ---- the fixed scratch of epilora_decode_lora_noalloc ------------------------
+// One array per GPU, for the life of the process.  In host code `scratch`
+// names a host-side stand-in, not device memory: its device address on each
+// GPU comes from hipGetSymbolAddress (with that GPU current) and only that
+// address is ever passed to kernels or fill launches.
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::atomic<void*> scratch_ptr[kMaxDevices];
+
+int scratch_of_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return EPILORA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return EPILORA_ERR_UNSUPPORTED;
+  void* p = scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {  // first call on this device: look the address up once
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return EPILORA_ERR_HIP;
+    scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return EPILORA_OK;
 }
 
 }  // namespace
@@ -213,32 +263,33 @@ int epilora_lora_expand_add(const float* z, int64_t M, int64_t N, const uint16_t
 }
 
 int epilora_decode_lora(const epilora_layer_args* a, void* stream) {
-  if (a == nullptr) return EPILORA_ERR_INVALID_ARG;
-  if (a->M < 0 || a->N < 0 || a->K < 0) return EPILORA_ERR_INVALID_ARG;
-  if (a->M == 0 || a->N == 0) return EPILORA_OK;
-  if (a->M > EPILORA_DECODE_MAX_M) return EPILORA_ERR_UNSUPPORTED;
-  if (a->x == nullptr || a->y == nullptr) return EPILORA_ERR_INVALID_ARG;
-  int st = check_weights(a);
-  if (st != EPILORA_OK) return st;
-  if (a->ldx < a->K || a->ldy < a->N) return EPILORA_ERR_INVALID_ARG;
-  if (a->ldx % 16 != 0 || !aligned(a->x, 16) || !aligned(a->y, 2)) return EPILORA_ERR_UNSUPPORTED;
-  if (a->xq_out != nullptr) {
-    if (a->ldq_out < a->K) return EPILORA_ERR_INVALID_ARG;
-    if (a->ldq_out % 16 != 0 || !aligned(a->xq_out, 16)) return EPILORA_ERR_UNSUPPORTED;
-  }
-  if (a->sx_out != nullptr && !aligned(a->sx_out, 4)) return EPILORA_ERR_UNSUPPORTED;
-  const bool lora = a->idx != nullptr;
   int32_t r = 16;
-  if (lora) {
-    st = check_adapters(a->L, a->r, a->A, true, a->B, true, a->ranks, a->idx);
-    if (st != EPILORA_OK) return st;
-    r = a->r;
-  }
-  st = check_ws(a->ws, a->ws_bytes, decode_ws(a->M, a->K, r).total);
+  if (a == nullptr) return EPILORA_ERR_INVALID_ARG;
+  const int st0 = check_decode(a, r);
+  if (st0 != EPILORA_OK || a->M == 0 || a->N == 0) return st0;
+  const int st = check_ws(a->ws, a->ws_bytes, decode_ws(a->M, a->K, r).total);
   if (st != EPILORA_OK) return st;
-  AdapterArgs ad = adapters_of(a, lora);
-  return hip_status(launch_decode_lora(a->x, a->ldx, a->M, a->N, a->K, weights_of(a), ad, a->y, a->ldy, a->xq_out,
-                                       a->sx_out, a->ldq_out, a->ws, as_stream(stream)));
+  return hip_status(launch_decode_lora(a->x, a->ldx, a->M, a->N, a->K, weights_of(a), adapters_of(a, a->idx != nullptr),
+                                       a->y, a->ldy, a->xq_out, a->sx_out, a->ldq_out, a->ws, as_stream(stream)));
+}
+
+int epilora_decode_lora_noalloc(const epilora_layer_args* a, void* stream) {
+  int32_t r = 16;
+  if (a == nullptr) return EPILORA_ERR_INVALID_ARG;
+  const int st0 = check_decode(a, r);
+  if (st0 != EPILORA_OK || a->M == 0 || a->N == 0) return st0;
+  const DecodeWs lay = decode_ws(a->M, a->K, r);
+  if (lay.total > kScratchBytes) return EPILORA_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int st = scratch_of_device(&ws);
+  if (st != EPILORA_OK) return st;
+  // The previous call on this device left its counters at zero and cleared
+  // its z words, unless it timed out; clear the whole state region (control
+  // block, counters, z) so that every call starts from zero regardless.
+  hipStream_t s = as_stream(stream);
+  if (launch_fill_u32(ws, 0u, (int64_t)(kStateBytes / 4), s) != hipSuccess) return EPILORA_ERR_HIP;
+  return hip_status(launch_decode_lora(a->x, a->ldx, a->M, a->N, a->K, weights_of(a), adapters_of(a, a->idx != nullptr),
+                                       a->y, a->ldy, a->xq_out, a->sx_out, a->ldq_out, ws, s));
 }
 
 }  // extern "C"

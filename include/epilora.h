@@ -259,6 +259,23 @@ int epilora_lora_expand_add(const float* z, int64_t M, int64_t N,
  * Needs a workspace of EPILORA_OP_DECODE. */
 int epilora_decode_lora(const epilora_layer_args* args, void* stream);
 
+/* The fused decode path for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation and kernels as epilora_decode_lora, but
+ * the workspace is a fixed 16 MiB scratch array the library holds on each GPU
+ * for the life of the process (a->ws and a->ws_bytes are ignored).  The call
+ * allocates nothing: it enqueues a fill kernel that clears the scratch's
+ * state region (so no call depends on how the previous one ended), then the
+ * decode kernel.  A call whose workspace need, epilora_workspace_bytes(
+ * EPILORA_OP_DECODE, M, N, K, r), exceeds 16 MiB returns
+ * EPILORA_ERR_WORKSPACE and launches nothing.  Every call on one GPU shares
+ * that GPU's scratch: calls that may overlap in time on one GPU (different
+ * streams, or different host threads) race and must not be issued.  The
+ * device error word lives in the scratch and is not readable by the caller:
+ * an out-of-range index still counts as -1, and a wait timeout leaves that
+ * call's outputs invalid. */
+int epilora_decode_lora_noalloc(const epilora_layer_args* args, void* stream);
+
 #ifdef __cplusplus
 }
 #endif
