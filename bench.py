@@ -1,22 +1,28 @@
 """Benchmark of the multi-tenant LoRA low-precision linear layer on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu] [--no-prefill] [--no-72b]
 
 A step is one pass of the whole hot path over one batch: the Llama-8B-shaped
 decoder layer's four projections (qkv, o, gate_up, down) at M = 1 token with
 one rank-64 tenant, each through the fused decode path (per-token FP8
 quantization, shrink, FP8 GEMM with the adapter epilogue, in one launch per
-projection).  Inputs are resident in HBM; the steps are replayed from a HIP
-graph, and 4 copies of the weights and adapters are cycled so that no step
+projection).  Inputs are resident in HBM; the steps are replayed from HIP
+graphs, and 4 copies of the weights and adapters are cycled so that no step
 finds its 218 MB of weights in the 256 MB Infinity Cache (the method's
 kernel timings flush the L2 between runs).  `value` is microseconds per
-layer (lower is better).
+layer (lower is better): the mean over exactly K timed steps; the median and
+p10 / p90 over at least 100 replays of a graph of 4 steps (one per weight
+copy), per step, are reported beside it.
 
-Also reported: the same layer without an adapter (base-only FP8 GEMM, same
-kernel), the unfused paths, per-projection times, the 2048-token prefill
-GEMMs (gate_up and down, FP8 and 4-bit weights, 16 and 32 tenant segments)
-in TFLOP/s, the roofline of the dominant kernel, and the CPU oracle timed
-on a bounded sample of the same layer.
+Also reported: the same layer without an adapter (base-only, same kernel),
+the unfused paths, per projection the control set of the method's kernel
+evaluation (the GEMM with z given, the shrink alone, the exposed shrink and
+the overlap model's prediction), a streaming-read ceiling over the same
+weight bytes, the 32-token multi-tenant decode layer (28 distinct rank-64
+tenants), the 72B-shaped PreFT decode layer at M = 1, 8, 64, the
+2048-token prefill GEMMs (gate_up and down, FP8 and 4-bit weights, 16 and 32
+tenant segments) in TFLOP/s, the roofline of the dominant kernel, and the
+CPU oracle timed on a bounded sample of the same layer.
 """
 
 import argparse
@@ -201,6 +207,32 @@ def time_graph(g, rounds, warmup):
     return e0.elapsed_time(e1) / rounds
 
 
+def pct(samples):
+    """median, p10 and p90 of a list of microsecond samples."""
+    a = np.asarray(samples, dtype=np.float64)
+    return {"median_us": round(float(np.median(a)), 2), "p10_us": round(float(np.percentile(a, 10)), 2),
+            "p90_us": round(float(np.percentile(a, 90)), 2), "samples": int(a.size)}
+
+
+def call_samples(projs, fn_names, n, warmup, copies=ROTATE):
+    """Per-call microseconds for the diagnostic figures: n replays of one
+    graph that holds a pass of fn_names over each weight copy (so that short
+    kernels are not paced by graph launches), each replay between two
+    events, divided by the copies."""
+    fns = [getattr(p, n_) for p in projs for n_ in fn_names]
+    g = graph_of(fns, copies)
+    for _ in range(warmup):
+        g.replay()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for i in range(n):
+        g.replay()
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    return [1000.0 * ev[i].elapsed_time(ev[i + 1]) / copies for i in range(n)]
+
+
 def per_step_us(projs, fn_names, steps, warmup):
     """Microseconds per step (a step = fn_names over projs, on one weight
     copy): `warmup` untimed steps, then exactly `steps` timed ones between
@@ -269,35 +301,146 @@ def decode_72b(steps, warmup):
     return out
 
 
-def cpu_baseline(layer, frac=4, min_seconds=10.0, max_reps=1000):
+def decode_multitenant(steps, warmup):
+    """The 32-token multi-tenant decode layer on Llama-8B shapes: 64 resident
+    rank-64 adapters, 32 distinct tenants of which 4 tokens carry none, so 28
+    distinct adapters are read (each A and B once); fused path, two rotated
+    copies of weights and adapters (2 x 468 MB, more than the Infinity
+    Cache)."""
+    layer = config(3)
+    log("multi-tenant decode layer M=32 ...")
+    projs = [Proj(g, copies=2) for g in layer.gemms]
+    torch.cuda.synchronize()
+    us, _ = per_step_us(projs, ["fused"], steps, warmup)
+    base_us, _ = per_step_us(projs, ["fused_base"], steps, warmup)
+    nbytes = sum(p.bytes() for p in projs)
+    wbytes = sum(p.K * p.N + 4 * p.N for p in projs)
+    out = {"fused_us": round(us, 2), "base_only_us": round(base_us, 2), "bytes": nbytes, "weight_bytes": wbytes,
+           "GBps": round(nbytes / us / 1e3, 1), "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
+           "distinct_tenants": len(projs[0].adapter_ranks()[1]),
+           "per_projection_us": {p.g.name: round(float(np.mean(call_samples([p], ["fused"], 20, 2, copies=2))), 2)
+                                 for p in projs}}
+    del projs
+    torch.cuda.empty_cache()
+    return out
+
+
+class ReadProbe:
+    """The streaming-read probe (libepilora_probe.so, a measurement kernel of
+    its own, outside the layer's library)."""
+
+    def __init__(self):
+        import ctypes
+        path = os.path.join(ROOT, "fp4_gemm_amd", "libepilora_probe.so")
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build with `python -m fp4_gemm_amd.build`")
+        self.lib = ctypes.CDLL(path)
+        f = self.lib.epilora_probe_stream_read
+        f.restype = ctypes.c_int
+        f.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        self.out = torch.zeros(4, dtype=torch.int32, device=DEV)
+
+    def read(self, t, grid):
+        st = self.lib.epilora_probe_stream_read(t.data_ptr(), t.numel() * t.element_size(), grid,
+                                                self.out.data_ptr(), torch.cuda.current_stream().cuda_stream)
+        assert st == 0, st
+
+
+def read_ceiling(projs, steps, warmup):
+    """Microseconds per layer for a plain streaming read of the layer's
+    weight bytes (each projection's weight codes, rotated copies as in the
+    timed steps), best over a few grid sizes; the practical bandwidth
+    ceiling of the weight-streaming kernels."""
+    probe = ReadProbe()
+    best = None
+    for grid in (512, 1024, 2048):
+        for p in projs:
+            p._probe = (lambda c, p=p, grid=grid: probe.read(p.w[c % p.copies][0], grid))
+        us, _ = per_step_us(projs, ["_probe"], steps, warmup)
+        if best is None or us < best[0]:
+            best = (us, grid)
+    wbytes = sum(p.w[0][0].numel() for p in projs)
+    return {"read_us": round(best[0], 2), "grid": best[1], "bytes": wbytes,
+            "GBps": round(wbytes / best[0] / 1e3, 1), "frac_of_8TBps": round(wbytes / best[0] / 1e3 / HBM_PEAK_GBS, 4)}
+
+
+def projection_controls(p, n, warmup):
+    """The method's control set for one projection (per call, medians over n
+    replays of rotated copies): the fused path and the same kernel without an
+    adapter; the base GEMM from pre-quantized x; the GEMM with its adapter
+    epilogue and z given (the shrink's output already in memory); the shrink
+    alone; the quantizer alone.  exposed_shrink = fused - z_given.  The
+    overlap model: the adapter costs t_epi + max(0, t_shrink - t_main), with
+    t_main the base GEMM, t_epi = z_given - t_main, t_shrink the shrink
+    alone."""
+    med = {}
+    for name in ("fused", "fused_base", "gemm_base", "gemm_lora", "shrink", "quant"):
+        med[name] = pct(call_samples([p], [name], n, warmup))
+    m = {k: v["median_us"] for k, v in med.items()}
+    t_main, t_epi = m["gemm_base"], m["gemm_lora"] - m["gemm_base"]
+    model_cost = t_epi + max(0.0, m["shrink"] - t_main)
+    return {
+        "fused_us": med["fused"], "fused_base_us": med["fused_base"], "gemm_base_us": med["gemm_base"],
+        "z_given_us": med["gemm_lora"], "shrink_alone_us": med["shrink"], "quant_alone_us": med["quant"],
+        "exposed_shrink_us": round(m["fused"] - m["gemm_lora"], 2),
+        "adapter_cost_us": round(m["fused"] - m["fused_base"], 2),
+        "model": {"t_main_us": t_main, "t_epi_us": round(t_epi, 2), "t_shrink_us": m["shrink"],
+                  "predicted_adapter_cost_us": round(model_cost, 2),
+                  "predicted_fused_us": round(m["fused_base"] + model_cost, 2)},
+        "bytes": p.bytes(), "GBps": round(p.bytes() / m["fused"] / 1e3, 1),
+    }
+
+
+def cpu_baseline(layer, frac=4, min_seconds=6.0, max_reps=1000):
     """The oracle on a bounded sample of the decode layer: every frac-th
     output channel of each projection (its weights quantized by the oracle
     outside the timed region), repeated until about min_seconds of CPU work
-    have been timed; the mean time of one pass, scaled by frac, is reported
-    in microseconds per layer."""
+    have been timed; the mean time of one pass, scaled by frac, in
+    microseconds per layer.  Timed with the BLAS pool at every host core and
+    at one thread.  "cold" is the oracle's call as it stands (it decodes the
+    FP8 weight codes by table on every call); "warm" subtracts the measured
+    table decode of those weights (what a pass costs with decoded weights
+    kept)."""
     import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = os.cpu_count()
+    from threadpoolctl import threadpool_info, threadpool_limits
     cases = []
     for g in layer.gemms:
         cols = np.arange(0, g.N, frac)
         wq, sw = oracle.quant_weight_fp8(g.w()[cols])
         cases.append((g.x(), g.A(), g.B()[:, cols], wq, sw))
-    timed, reps = 0.0, 0
-    while reps < max_reps and (timed < min_seconds or reps < 2):
-        t0 = time.perf_counter()
+
+    def timed(fn):
+        t_sum, reps = 0.0, 0
+        while reps < max_reps and (t_sum < min_seconds or reps < 2):
+            t0 = time.perf_counter()
+            fn()
+            t_sum += time.perf_counter() - t0
+            reps += 1
+        return t_sum / reps * frac * 1e6, reps, t_sum
+
+    def layer_pass():
         for x, A, B, wq, sw in cases:
             oracle.linear_lora(x, A, B, layer.idx, layer.scale, wq=wq, sw=sw, ranks=layer.ranks, mask=layer.mask)
-        timed += time.perf_counter() - t0
-        reps += 1
-    us = timed / reps * frac * 1e6
-    return {"value": round(us, 1), "unit": "us/layer", "cores": int(threads), "kind": "oracle",
+
+    def decode_pass():
+        for _, _, _, wq, _ in cases:
+            oracle.e4m3_decode(wq)
+
+    out = {}
+    threads_all = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    for label, limit in (("all", None), ("one", 1)):
+        with threadpool_limits(limits=limit):
+            cold, reps, t_sum = timed(layer_pass)
+            dec, _, _ = timed(decode_pass)
+        out[label] = {"cold_us": round(cold, 1), "warm_us": round(cold - dec, 1), "passes": reps,
+                      "seconds": round(t_sum, 1), "threads": threads_all if limit is None else 1}
+    return {"value": out["all"]["cold_us"], "unit": "us/layer", "cores": int(out["all"]["threads"]),
+            "kind": "oracle",
             "sample": f"Llama-8B decode layer (M=1, r=64): every {frac}th output channel of each of the 4 "
-                      f"projections (fp64 oracle incl. the FP8 decode of those weights), {reps} passes, "
-                      f"{timed:.1f} s timed, scaled x{frac}; host has {os.cpu_count()} cpus"}
+                      f"projections (fp64 oracle incl. the table decode of those FP8 weights), "
+                      f"{out['all']['passes']} passes in {out['all']['seconds']} s at {out['all']['threads']} "
+                      f"BLAS threads, scaled x{frac}; host has {os.cpu_count()} cpus",
+            "modes": out}
 
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_gate_up_traffic.txt")
@@ -362,6 +505,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-72b", action="store_true", help="skip the 72B-shaped decode layer")
+    ap.add_argument("--no-mt", action="store_true", help="skip the 32-token multi-tenant decode layer")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only the dispatches the HBM-counter runs measure (see traffic_probe)")
     args = ap.parse_args()
@@ -381,39 +525,49 @@ def main():
     projs = [Proj(g) for g in layer.gemms]
     torch.cuda.synchronize()
     fused_us, timed_steps = per_step_us(projs, ["fused"], args.steps, args.warmup)
+    # percentiles over single replays of a graph of ROTATE steps (one per
+    # weight copy), per step
+    fused_pct = pct(call_samples(projs, ["fused"], max(100, args.steps // ROTATE), args.warmup))
     base_us, _ = per_step_us(projs, ["fused_base"], args.steps, args.warmup)
-    serial_us = per_call_us(projs, ["quant", "shrink", "gemm_lora"], args.steps, args.warmup)
-    separate_us = per_call_us(projs, ["quant", "gemm_base", "shrink", "expand"], args.steps, args.warmup)
-    gemm_only_us = per_call_us(projs, ["gemm_base"], args.steps, args.warmup)
-    per_proj = {}
-    for p in projs:
-        f_us = per_call_us([p], ["fused"], args.steps, args.warmup)
-        b_us = per_call_us([p], ["fused_base"], args.steps, args.warmup)
-        per_proj[p.g.name] = {"fused_us": round(f_us, 2), "base_us": round(b_us, 2),
-                              "bytes": p.bytes(), "GBps": round(p.bytes() / f_us / 1e3, 1)}
+    base_pct = pct(call_samples(projs, ["fused_base"], max(100, args.steps // ROTATE), args.warmup))
+    reps = max(25, args.steps // ROTATE)
+    serial_us = pct(call_samples(projs, ["quant", "shrink", "gemm_lora"], reps, 2))
+    separate_us = pct(call_samples(projs, ["quant", "gemm_base", "shrink", "expand"], reps, 2))
+    gemm_only_us = pct(call_samples(projs, ["gemm_base"], reps, 2))
+    log("per-projection controls ...")
+    per_proj = {p.g.name: projection_controls(p, reps, 2) for p in projs}
+    ceiling = read_ceiling(projs, args.steps, args.warmup)
     layer_bytes = sum(p.bytes() for p in projs)
+    base_bytes = sum(p.K * p.N + 4 * p.N + 2 * p.M * (p.K + p.N) for p in projs)
     dom = max(projs, key=lambda p: p.bytes())  # gate_up: the dominant kernel
-    dom_us = per_proj[dom.g.name]["fused_us"]
+    dom_us = float(np.mean(call_samples([dom], ["fused"], reps, 2)))
     dom_gbs = dom.bytes() / dom_us / 1e3
-    log(f"decode layer: fused {fused_us:.1f} us, base {base_us:.1f} us")
+    log(f"decode layer: fused {fused_us:.1f} us, base {base_us:.1f} us, read ceiling {ceiling['read_us']} us")
+    del projs
+    torch.cuda.empty_cache()
+
+    mt = None if args.no_mt else decode_multitenant(max(20, args.steps // 2), max(4, args.warmup // 2))
 
     # ---- prefill: M = 2048, tenant segments ----
     prefill = {}
     if not args.no_prefill:
-        for wfmt, segs in (("fp8", 32), ("fp8", 16), ("fp4", 16)):
+        for wfmt, segs in (("fp8", 32), ("fp8", 16), ("fp4", 32), ("fp4", 16)):
             lay5 = config(5, segments=segs, wfmt=wfmt)
             for g in lay5.gemms:
                 log(f"prefill {wfmt} {segs} segments {g.name} ...")
                 p = Proj(g, wfmt, copies=3)
                 p.quant(0)
                 p.shrink(0)
-                gemm_ms = time_graph(graph_of([p.gemm_lora], 3), 10, 2) / 3
-                path_ms = time_graph(graph_of([p.quant, p.shrink, p.gemm_lora], 3), 5, 1) / 3
+                gemm = pct(call_samples([p], ["gemm_lora"], 10, 2, copies=3))
+                base = pct(call_samples([p], ["gemm_base"], 10, 2, copies=3))
+                path = pct(call_samples([p], ["quant", "shrink", "gemm_lora"], 5, 1, copies=3))
+                g_us, b_us, p_us = gemm["median_us"], base["median_us"], path["median_us"]
                 prefill[f"{g.name}_{wfmt}_{segs}seg"] = {
-                    "gemm_us": round(gemm_ms * 1e3, 1), "path_us": round(path_ms * 1e3, 1),
-                    "gemm_tflops": round(p.flops() / gemm_ms / 1e9, 1),
-                    "path_tflops": round(p.flops() / path_ms / 1e9, 1),
-                    "gemm_frac_fp8_peak": round(p.flops() / gemm_ms / 1e9 / FP8_PEAK_TFLOPS, 4)}
+                    "gemm_us": gemm, "base_only_gemm_us": base, "path_us": path,
+                    "gemm_tflops": round(p.flops() / g_us / 1e6, 1),
+                    "base_only_tflops": round(2 * p.M * p.N * p.K / b_us / 1e6, 1),
+                    "path_tflops": round(p.flops() / p_us / 1e6, 1),
+                    "gemm_frac_fp8_peak": round(p.flops() / g_us / 1e6 / FP8_PEAK_TFLOPS, 4)}
                 del p
                 torch.cuda.empty_cache()
 
@@ -444,18 +598,25 @@ def main():
                                "FP8 e4m3 per-channel weights, fused decode path, HIP graph replay, "
                                f"{ROTATE} rotated weight copies",
                    "M": 1, "rank": 64, "tenants": 1},
+        "step_percentiles": fused_pct,
         "hbm_frac": round(layer_bytes / fused_us / 1e3 / HBM_PEAK_GBS, 4),
+        "hbm_frac_of_read_ceiling": round((layer_bytes / fused_us) / (ceiling["bytes"] / ceiling["read_us"]), 4),
         "layer_bytes": layer_bytes,
+        "read_ceiling": ceiling,
         "base_only_us": round(base_us, 2),
+        "base_only_percentiles": base_pct,
+        "base_only_bytes": base_bytes,
+        "base_only_hbm_frac": round(base_bytes / base_us / 1e3 / HBM_PEAK_GBS, 4),
         "fused_over_base": round(fused_us / base_us, 3),
-        "gemm_only_us": round(gemm_only_us, 2),
-        "serialized_us": round(serial_us, 2),
-        "separate_kernels_us": round(separate_us, 2),
+        "gemm_only_us": gemm_only_us,
+        "serialized_us": serial_us,
+        "separate_kernels_us": separate_us,
         "per_projection": per_proj,
         "roofline": {"kernel": f"decode_kernel ({dom.g.name}, fused)", "bound": "hbm",
                      "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
-                     "algorithmic_bytes": dom.bytes(), "launch_us": dom_us},
+                     "algorithmic_bytes": dom.bytes(), "launch_us": round(dom_us, 2)},
+        "decode_multitenant_m32": mt,
         "prefill": prefill,
         "decode_72b_preft": d72,
         "cpu_baseline": cpu,

@@ -22,6 +22,10 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libepilora.so")
+# The streaming-read probe the benchmark uses as a bandwidth ceiling; a
+# library of its own, outside the layer's ABI.
+PROBE_SRC = os.path.join(HERE, "probe", "stream_read.hip")
+PROBE_OUT = os.path.join(HERE, "libepilora_probe.so")
 BUILD = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -50,21 +54,29 @@ def _compile(src, verbose):
     return obj
 
 
-def build(jobs=None, verbose=False):
-    """Compile every kernel source and link libepilora.so; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    jobs = jobs or min(len(srcs), os.cpu_count() or 4, 8)
-    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = OUT + ".tmp"
+def _link(objs, out, verbose):
+    tmp = out + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(jobs=None, verbose=False):
+    """Compile every kernel source and link libepilora.so (and the read
+    probe's libepilora_probe.so); returns the library's path."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = sources()
+    jobs = jobs or min(len(srcs) + 1, os.cpu_count() or 4, 8)
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        futs = [ex.submit(_compile, s, verbose) for s in srcs + [PROBE_SRC]]
+        objs = [f.result() for f in futs]
+    _link(objs[-1:], PROBE_OUT, verbose)
+    objs = objs[:-1]
+    _link(objs, OUT, verbose)
     return OUT
 
 
