@@ -48,4 +48,6 @@ from .linear import (  # noqa: F401
     shrink,
     expand,
     linear_lora,
+    slice_bounds,
+    linear_lora_sliced,
 )

@@ -243,3 +243,62 @@ def linear_lora(x, A, B, idx, scale, *, wq=None, sw=None, wc=None, bs=None,
     y = base.copy()
     y[act] = base[act] + lora[act]
     return dict(xq=xq, sx=sx, z=z, base=base, y=y, active=act)
+
+
+# ---------------------------------------------------------------------------
+# Multi-slice projections
+# ---------------------------------------------------------------------------
+
+
+def slice_bounds(slice_n):
+    """[(start, stop)] of consecutive output slices of widths slice_n."""
+    ends = np.cumsum(np.asarray(slice_n, dtype=np.int64))
+    starts = np.concatenate([[0], ends[:-1]])
+    return list(zip(starts.tolist(), ends.tolist()))
+
+
+def linear_lora_sliced(x, A, B, idx, scale, slice_n, *, wq=None, sw=None, wc=None, bs=None, gs=None,
+                       ranks=None, mask=None, rows=None, cols=None, weights_of_cols=False):
+    """A projection whose outputs are several consecutive slices, each with
+    its own adapter pair: attention's query / key / value (three slices of
+    unequal widths) or the MLP's gate / up (two), as in "EpiLoRA ...",
+    Evaluation, "Many tenants" and the appendix's account of the expand
+    costs (Table 15): the up-projection of slice s adds into the slice's
+    output columns only, and its down-projection is the slice's own.
+
+    A: uint16 [L][S][r][K] (slice s of adapter a: A[a][s]);
+    B: uint16 [L][N][r] (rows of slice s hold that slice's up-projection);
+    slice_n: the S slice widths (sum N).  For output column n in slice s and
+    an active token t: y[t][n] = base[t][n] + scale * sum_j
+    B[a_t][n][j] * z_s[t][j], with z_s = shrink(x, A[:, s]).  Other rows get
+    no add.  The result's z is [M][S * r], slice s in columns s*r .. s*r+r.
+    `cols` samples output columns (indices into N); with weights_of_cols the
+    weights passed are already those columns' rows, in that order."""
+    L, S, r, K = A.shape
+    bounds = slice_bounds(slice_n)
+    if len(bounds) != S or bounds[-1][1] != B.shape[1]:
+        raise ValueError("slice widths must match A's slices and B's rows")
+    xs = _pick(x, rows)
+    xq, sx = quant_act(xs)
+    wcols = None if weights_of_cols else cols
+    if wq is not None:
+        base = base_fp8(xq, sx, wq, sw, cols=wcols)
+    else:
+        base = base_fp4(xq, sx, wc, bs, gs, cols=wcols)
+    idx_s = _pick(np.asarray(idx), rows)
+    mask_s = None if mask is None else _pick(np.asarray(mask), rows)
+    colset = np.arange(B.shape[1]) if cols is None else np.asarray(cols)
+    y = base.copy()
+    z_all = np.zeros((xs.shape[0], S * r), dtype=np.float64)
+    act = None
+    for s, (n0, n1) in enumerate(bounds):
+        z = shrink(xs, A[:, s], idx_s, ranks, mask_s)
+        z_all[:, s * r:(s + 1) * r] = z
+        pos = np.nonzero((colset >= n0) & (colset < n1))[0]   # positions in the output
+        if pos.size == 0:
+            continue
+        lora, act = expand(z, B, idx_s, scale, ranks, mask_s, cols=colset[pos])
+        y[np.ix_(act, pos)] = base[np.ix_(act, pos)] + lora[act]
+    if act is None:
+        act = active_rows(idx_s, L, r, ranks, mask_s)[0]
+    return dict(xq=xq, sx=sx, z=z_all, base=base, y=y, active=act)

@@ -344,3 +344,123 @@ def test_workload_layer_through_oracle():
     wq, sw = oracle.quant_weight_fp8(g.w())
     out = oracle.linear_lora(g.x(), g.A(), g.B(), lay.idx, lay.scale, wq=wq, sw=sw)
     assert out["y"].shape == (3, 32) and out["active"].tolist() == [True, False, True]
+
+
+# --- multi-slice projections ----------------------------------------------------------
+
+def _sliced_inputs(rng, M=7, K=48, slice_n=(24, 8, 8), L=3, r=6):
+    N = sum(slice_n)
+    S = len(slice_n)
+    x = rand_bf16(rng, (M, K), 1.0)
+    w = rand_bf16(rng, (N, K), 0.02)
+    A = rand_bf16(rng, (L, S, r, K), 1.0 / np.sqrt(K))
+    B = rand_bf16(rng, (L, N, r), 0.01)
+    return x, w, A, B
+
+
+def test_sliced_equals_block_diagonal_adapter():
+    """A multi-slice projection is one adapter of rank S*r whose A stacks the
+    slices' A and whose B is block diagonal (slice s's rows use only columns
+    s*r .. s*r+r): the unsliced layer on that merged adapter, computed
+    through a dense merged update, gives the same outputs."""
+    rng = np.random.default_rng(40)
+    slice_n = (24, 8, 8)
+    x, w, A, B = _sliced_inputs(rng, slice_n=slice_n)
+    L, S, r, K = A.shape
+    wq, sw = oracle.quant_weight_fp8(w)
+    idx = np.array([0, 2, -1, 1, 2, 0, 1])
+    ranks = np.array([6, 4, 0])
+    mask = np.array([1, 1, 1, 1, 0, 1, 1], np.uint8)
+    for a, rk in enumerate(ranks):   # padding past each rank is zero in the data
+        A[a, :, rk:] = 0
+        B[a, :, rk:] = 0
+    out = oracle.linear_lora_sliced(x, A, B, idx, 2.0, slice_n, wq=wq, sw=sw, ranks=ranks, mask=mask)
+    Abig = A.reshape(L, S * r, K)
+    Bbig = np.zeros((L, B.shape[1], S * r), np.uint16)
+    for s, (n0, n1) in enumerate(oracle.slice_bounds(slice_n)):
+        Bbig[:, n0:n1, s * r:(s + 1) * r] = B[:, n0:n1]
+    ranks_big = np.where(ranks > 0, S * r, 0)
+    ref = oracle.linear_lora(x, Abig, Bbig, idx, 2.0, wq=wq, sw=sw, ranks=ranks_big, mask=mask)
+    assert np.array_equal(out["active"], ref["active"])
+    assert np.allclose(out["y"], ref["y"], rtol=1e-12, atol=1e-15)
+    assert np.allclose(out["z"], ref["z"], rtol=1e-12, atol=1e-15)
+    # and through the dense merged update B_big A_big of each active token
+    xf = t_bf16(x)
+    for t in np.nonzero(out["active"])[0]:
+        dW = t_bf16(Bbig[idx[t]]) @ t_bf16(Abig[idx[t]])
+        assert np.allclose(out["y"][t] - out["base"][t], 2.0 * (dW @ xf[t]).numpy(), rtol=1e-9, atol=1e-12)
+    for t in np.nonzero(~out["active"])[0]:
+        assert np.array_equal(out["y"][t], out["base"][t])
+
+
+def test_one_slice_is_the_plain_layer():
+    rng = np.random.default_rng(41)
+    x, w, A, B = _sliced_inputs(rng, slice_n=(40,))
+    wq, sw = oracle.quant_weight_fp8(w)
+    idx = np.array([0, 1, 2, -1, 2, 1, 0])
+    a = oracle.linear_lora_sliced(x, A, B, idx, 2.0, (40,), wq=wq, sw=sw)
+    b = oracle.linear_lora(x, A[:, 0], B, idx, 2.0, wq=wq, sw=sw)
+    for k in ("y", "z", "base", "xq", "sx", "active"):
+        assert np.array_equal(a[k], b[k]), k
+
+
+def test_slices_are_independent():
+    """Zeroing slice s's down-projection leaves exactly that slice's outputs
+    at the base value and changes no other slice's outputs."""
+    rng = np.random.default_rng(42)
+    slice_n = (16, 8, 16)
+    x, w, A, B = _sliced_inputs(rng, slice_n=slice_n)
+    wq, sw = oracle.quant_weight_fp8(w)
+    idx = np.array([0, 1, 2, 0, 1, 2, 0])
+    full = oracle.linear_lora_sliced(x, A, B, idx, 2.0, slice_n, wq=wq, sw=sw)
+    bounds = oracle.slice_bounds(slice_n)
+    for s, (n0, n1) in enumerate(bounds):
+        A0 = A.copy()
+        A0[:, s] = 0
+        out = oracle.linear_lora_sliced(x, A0, B, idx, 2.0, slice_n, wq=wq, sw=sw)
+        assert np.array_equal(out["y"][:, n0:n1], full["base"][:, n0:n1])
+        other = np.r_[0:n0, n1:sum(slice_n)]
+        assert np.array_equal(out["y"][:, other], full["y"][:, other])
+        assert np.abs(full["y"][:, n0:n1] - full["base"][:, n0:n1]).max() > 0
+
+
+def test_sliced_sampled_columns():
+    rng = np.random.default_rng(43)
+    slice_n = (24, 8, 8)
+    x, w, A, B = _sliced_inputs(rng, slice_n=slice_n)
+    wq, sw = oracle.quant_weight_fp8(w)
+    idx = np.array([0, 2, -1, 1, 2, 0, 1])
+    full = oracle.linear_lora_sliced(x, A, B, idx, 2.0, slice_n, wq=wq, sw=sw)
+    cols = np.array([1, 23, 24, 31, 32, 39])
+    rows = np.array([0, 3, 6])
+    part = oracle.linear_lora_sliced(x, A, B, idx, 2.0, slice_n, wq=wq[cols], sw=sw[cols], rows=rows, cols=cols,
+                                     weights_of_cols=True)
+    assert np.array_equal(part["y"], full["y"][np.ix_(rows, cols)])
+
+
+def test_sliced_brute_force():
+    """M=2, K=4, N=8 in slices (4, 2, 2), r=2: Python loops straight from the
+    definition (fp64), every index and mask combination."""
+    rng = np.random.default_rng(44)
+    slice_n = (4, 2, 2)
+    x, w, A, B = _sliced_inputs(rng, M=2, K=4, slice_n=slice_n, L=2, r=2)
+    wq, sw = oracle.quant_weight_fp8(w)
+    xf = t_bf16(x).numpy()
+    Af, Bf = t_bf16(A).numpy(), t_bf16(B).numpy()
+    for i0, i1, m0, m1 in itertools.product([-1, 0, 1], [-1, 0, 1], [0, 1], [0, 1]):
+        idx = np.array([i0, i1])
+        mask = np.array([m0, m1], np.uint8)
+        out = oracle.linear_lora_sliced(x, A, B, idx, 2.0, slice_n, wq=wq, sw=sw, mask=mask)
+        for t in range(2):
+            for n in range(8):
+                s = 0 if n < 4 else (1 if n < 6 else 2)
+                want = out["base"][t][n]
+                if idx[t] >= 0 and mask[t]:
+                    add = 0.0
+                    for j in range(2):
+                        zt = 0.0
+                        for k in range(4):
+                            zt += Af[idx[t], s, j, k] * xf[t, k]
+                        add += Bf[idx[t], n, j] * zt
+                    want = want + 2.0 * add
+                assert abs(out["y"][t][n] - want) <= 1e-12 * max(1.0, abs(want))

@@ -7,8 +7,9 @@ builds the integer metadata (tenant indices, masks, ranks).
 
 Shapes follow the layers the method is measured on ("EpiLoRA: Fusing Many
 LoRA Adapters into Low-Precision GEMMs for Serving and RL", Evaluation,
-Setup: Llama-3.1-8B and Qwen2.5-72B with random adapters of rank 16-128,
-since speed depends only on the adapters' shapes) and the prefill-only
+Setup: Llama-3.1-8B and Qwen2.5-72B layer shapes; the adapters there are
+random draws of ranks 16 to 128, because their shapes alone set the
+kernels' speed) and the prefill-only
 serving case ("PreFT: Prefill-only finetuning for efficient inference",
 abstract: 512 adapters on a 70B-class model).
 
@@ -22,6 +23,8 @@ no token references need not be drawn at all.
 from .configs import (  # noqa: F401
     GEMMS_8B,
     GEMMS_72B,
+    SLICES_8B,
+    SLICES_72B,
     GemmCase,
     Layer,
     bf16_bits,
