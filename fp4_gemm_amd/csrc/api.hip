@@ -2,6 +2,7 @@
 // dispatch to the kernels.  No entry point allocates memory or synchronizes
 // the stream, except the diagnostic epilora_device_error.
 #include <atomic>
+#include <climits>
 
 #include "../../include/epilora.h"
 #include "kernels.h"
@@ -67,14 +68,43 @@ WeightArgs weights_of(const epilora_layer_args* a) {
   return w;
 }
 
+// Output slices with their own adapter pairs: nslices in [0, kMaxSlices]
+// (0 and 1 mean one slice), widths positive and summing to N, each a
+// multiple of `unit` (the output tile the kernels keep inside one slice).
+int check_slices(int32_t nslices, const int64_t* slice_n, int64_t N, int64_t unit) {
+  if (nslices < 0 || nslices > kMaxSlices) return EPILORA_ERR_INVALID_ARG;
+  if (nslices <= 1) return EPILORA_OK;
+  if (slice_n == nullptr) return EPILORA_ERR_INVALID_ARG;
+  int64_t sum = 0;
+  for (int i = 0; i < nslices; ++i) {
+    if (slice_n[i] <= 0) return EPILORA_ERR_INVALID_ARG;
+    if (slice_n[i] % unit != 0) return EPILORA_ERR_UNSUPPORTED;
+    sum += slice_n[i];
+  }
+  return sum == N ? EPILORA_OK : EPILORA_ERR_INVALID_ARG;
+}
+
+void set_slices(AdapterArgs& d, int32_t nslices, const int64_t* slice_n) {
+  d.S = nslices > 1 ? nslices : 1;
+  d.zld = d.S * d.r;
+  int64_t end = 0;
+  for (int i = 0; i < kMaxSlices; ++i) {
+    end += (i < d.S && d.S > 1) ? slice_n[i] : 0;
+    d.slice_end[i] = i < d.S - 1 ? end : INT64_MAX;
+  }
+}
+
 AdapterArgs adapters_of(const epilora_layer_args* a, bool on) {
   AdapterArgs d;
   d.A = a->A; d.B = a->B; d.ranks = a->ranks; d.mask = a->mask;
   d.idx = on ? a->idx : nullptr;
   d.L = a->L; d.r = a->r; d.scale = a->scale;
   if (!on) { d.r = 16; d.L = 0; }
+  set_slices(d, on ? a->nslices : 1, a->slice_n);
   return d;
 }
+
+int32_t slices_of(const epilora_layer_args* a) { return a->nslices > 1 ? a->nslices : 1; }
 
 // Host-side checks of a fused decode call (everything except the
 // workspace); `r` receives the slot width the workspace is sized for.
@@ -96,9 +126,16 @@ int check_decode(const epilora_layer_args* a, int32_t& r) {
   if (a->idx != nullptr) {
     st = check_adapters(a->L, a->r, a->A, true, a->B, true, a->ranks, a->idx);
     if (st != EPILORA_OK) return st;
+    st = check_slices(a->nslices, a->slice_n, a->N, 16);
+    if (st != EPILORA_OK) return st;
     r = a->r;
   }
   return EPILORA_OK;
+}
+
+// Workspace bytes of a fused decode call that passed check_decode.
+size_t decode_need(const epilora_layer_args* a, int32_t r) {
+  return decode_ws(a->M, a->K, r, a->idx != nullptr ? slices_of(a) : 1).total;
 }
 
 // ---- the fixed scratch of epilora_decode_lora_noalloc ------------------------
@@ -203,23 +240,32 @@ int epilora_quant_weight_fp4(const uint16_t* w, int64_t N, int64_t K, uint8_t* w
   return hip_status(launch_quant_weight_fp4(w, N, K, wc, bs, gs, ws, as_stream(stream)));
 }
 
-int epilora_lora_shrink(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* A, int32_t L,
-                        int32_t r, const int32_t* ranks, const int32_t* idx, const uint8_t* mask, float* z,
-                        void* ws, size_t ws_bytes, void* stream) {
+int epilora_lora_shrink_sliced(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* A, int32_t L,
+                               int32_t nslices, int32_t r, const int32_t* ranks, const int32_t* idx,
+                               const uint8_t* mask, float* z, void* ws, size_t ws_bytes, void* stream) {
   if (M < 0 || K < 0) return EPILORA_ERR_INVALID_ARG;
+  if (nslices < 1 || nslices > kMaxSlices) return EPILORA_ERR_INVALID_ARG;
   if (M == 0) return EPILORA_OK;
   if (x == nullptr || z == nullptr) return EPILORA_ERR_INVALID_ARG;
   int st = check_adapters(L, r, A, true, nullptr, false, ranks, idx);
   if (st != EPILORA_OK) return st;
   if (ldx < K) return EPILORA_ERR_INVALID_ARG;
   if (K % 16 != 0 || ldx % 16 != 0 || !aligned(x, 16) || !aligned(z, 16)) return EPILORA_ERR_UNSUPPORTED;
-  if (cdiv(M, kShrinkTokens) > kMaxShrinkTiles) return EPILORA_ERR_UNSUPPORTED;
-  st = check_ws(ws, ws_bytes, shrink_ws(kStateBytes, M, K, r).total);
+  if (cdiv(M, kShrinkTokens) * nslices > kMaxShrinkTiles) return EPILORA_ERR_UNSUPPORTED;
+  st = check_ws(ws, ws_bytes, shrink_ws(kStateBytes, M, K, r, nslices).total);
   if (st != EPILORA_OK) return st;
   AdapterArgs ad;
   ad.A = A; ad.B = nullptr; ad.ranks = ranks; ad.idx = idx; ad.mask = mask;
   ad.L = L; ad.r = r; ad.scale = 1.0f;
+  ad.S = nslices; ad.zld = nslices * r;
+  for (int i = 0; i < kMaxSlices; ++i) ad.slice_end[i] = INT64_MAX;
   return hip_status(launch_shrink(x, M, K, ldx, ad, z, ws, as_stream(stream)));
+}
+
+int epilora_lora_shrink(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* A, int32_t L,
+                        int32_t r, const int32_t* ranks, const int32_t* idx, const uint8_t* mask, float* z,
+                        void* ws, size_t ws_bytes, void* stream) {
+  return epilora_lora_shrink_sliced(x, M, K, ldx, A, L, 1, r, ranks, idx, mask, z, ws, ws_bytes, stream);
 }
 
 int epilora_gemm_lora(const epilora_layer_args* a, void* stream) {
@@ -236,6 +282,9 @@ int epilora_gemm_lora(const epilora_layer_args* a, void* stream) {
   if (lora) {
     st = check_adapters(a->L, a->r, a->A, false, a->B, true, a->ranks, a->idx);
     if (st != EPILORA_OK) return st;
+    // output tiles stay inside one slice: 16 rows (M <= 64), 128 (prefill)
+    st = check_slices(a->nslices, a->slice_n, a->N, a->M <= EPILORA_DECODE_MAX_M ? 16 : 128);
+    if (st != EPILORA_OK) return st;
     if (!aligned(a->z, 16)) return EPILORA_ERR_UNSUPPORTED;
     st = check_ws(a->ws, a->ws_bytes, kCtrlBytes);
     if (st != EPILORA_OK) return st;
@@ -244,13 +293,16 @@ int epilora_gemm_lora(const epilora_layer_args* a, void* stream) {
                                      a->z, a->y, a->ldy, a->ws, as_stream(stream)));
 }
 
-int epilora_lora_expand_add(const float* z, int64_t M, int64_t N, const uint16_t* B, int32_t L, int32_t r,
-                            const int32_t* ranks, const int32_t* idx, const uint8_t* mask, float scale, uint16_t* y,
-                            int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
+int epilora_lora_expand_add_sliced(const float* z, int64_t M, int64_t N, const uint16_t* B, int32_t L, int32_t r,
+                                   int32_t nslices, const int64_t* slice_n, const int32_t* ranks,
+                                   const int32_t* idx, const uint8_t* mask, float scale, uint16_t* y, int64_t ldy,
+                                   void* ws, size_t ws_bytes, void* stream) {
   if (M < 0 || N < 0) return EPILORA_ERR_INVALID_ARG;
+  int st = check_slices(nslices, slice_n, N, 1);
+  if (st != EPILORA_OK) return st;
   if (M == 0 || N == 0) return EPILORA_OK;
   if (z == nullptr || y == nullptr) return EPILORA_ERR_INVALID_ARG;
-  int st = check_adapters(L, r, nullptr, false, B, true, ranks, idx);
+  st = check_adapters(L, r, nullptr, false, B, true, ranks, idx);
   if (st != EPILORA_OK) return st;
   if (ldy < N) return EPILORA_ERR_INVALID_ARG;
   if (!aligned(z, 16) || !aligned(y, 2)) return EPILORA_ERR_UNSUPPORTED;
@@ -259,7 +311,15 @@ int epilora_lora_expand_add(const float* z, int64_t M, int64_t N, const uint16_t
   AdapterArgs ad;
   ad.A = nullptr; ad.B = B; ad.ranks = ranks; ad.idx = idx; ad.mask = mask;
   ad.L = L; ad.r = r; ad.scale = scale;
+  set_slices(ad, nslices, slice_n);
   return hip_status(launch_expand_add(z, M, N, ad, y, ldy, ws, as_stream(stream)));
+}
+
+int epilora_lora_expand_add(const float* z, int64_t M, int64_t N, const uint16_t* B, int32_t L, int32_t r,
+                            const int32_t* ranks, const int32_t* idx, const uint8_t* mask, float scale, uint16_t* y,
+                            int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
+  return epilora_lora_expand_add_sliced(z, M, N, B, L, r, 1, nullptr, ranks, idx, mask, scale, y, ldy, ws, ws_bytes,
+                                        stream);
 }
 
 int epilora_decode_lora(const epilora_layer_args* a, void* stream) {
@@ -267,7 +327,7 @@ int epilora_decode_lora(const epilora_layer_args* a, void* stream) {
   if (a == nullptr) return EPILORA_ERR_INVALID_ARG;
   const int st0 = check_decode(a, r);
   if (st0 != EPILORA_OK || a->M == 0 || a->N == 0) return st0;
-  const int st = check_ws(a->ws, a->ws_bytes, decode_ws(a->M, a->K, r).total);
+  const int st = check_ws(a->ws, a->ws_bytes, decode_need(a, r));
   if (st != EPILORA_OK) return st;
   return hip_status(launch_decode_lora(a->x, a->ldx, a->M, a->N, a->K, weights_of(a), adapters_of(a, a->idx != nullptr),
                                        a->y, a->ldy, a->xq_out, a->sx_out, a->ldq_out, a->ws, as_stream(stream)));
@@ -278,8 +338,7 @@ int epilora_decode_lora_noalloc(const epilora_layer_args* a, void* stream) {
   if (a == nullptr) return EPILORA_ERR_INVALID_ARG;
   const int st0 = check_decode(a, r);
   if (st0 != EPILORA_OK || a->M == 0 || a->N == 0) return st0;
-  const DecodeWs lay = decode_ws(a->M, a->K, r);
-  if (lay.total > kScratchBytes) return EPILORA_ERR_WORKSPACE;
+  if (decode_need(a, r) > kScratchBytes) return EPILORA_ERR_WORKSPACE;
   void* ws = nullptr;
   const int st = scratch_of_device(&ws);
   if (st != EPILORA_OK) return st;

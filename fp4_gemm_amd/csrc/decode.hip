@@ -11,9 +11,10 @@
 //                              quantized-rows flag (nq = 0 when every GEMM
 //                              workgroup quantizes the few rows into its own
 //                              LDS and the caller keeps no copy);
-//   the next tiles*splits      compute the shrink (bf16 x, fp32 partials,
+//   the next tiles*splits*S    compute the shrink (bf16 x, fp32 partials,
 //                              the last split of a tile adds them in a fixed
-//                              order) and store z in place, each word as its
+//                              order; one set per output slice with its own
+//                              adapter pair) and store z in place, each word as its
 //                              bitwise complement into a region that reads
 //                              zero until then;
 //   the rest                   own 16-row weight tiles: request their first
@@ -68,12 +69,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((XLDS &
   }
   if (bid < p.nq + p.ns) {  // ---- shrink
     const int sb = bid - p.nq;
-    const int tile = sb % p.tiles, split = sb / p.tiles;
+    const int tile = sb % p.tiles, rest = sb / p.tiles;
+    const int split = rest % p.s.splits, slice = rest / p.s.splits;
     int s_begin, s_end;
     shrink_range(p.s, split, s_begin, s_end);
     float* red = reinterpret_cast<float*>(smem);
-    const uint64_t active = shrink_tile<NW>(p.s, (int64_t)tile * kShrinkTokens, s_begin, s_end, red, split == 0);
-    shrink_finish<NW>(p.s, tile, split, red, active);
+    const uint64_t active =
+        shrink_tile<NW>(p.s, (int64_t)tile * kShrinkTokens, slice, s_begin, s_end, red, split == 0 && slice == 0);
+    shrink_finish<NW>(p.s, tile, slice, split, red, active);
     return;
   }
 
@@ -108,7 +111,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((XLDS &
   }
   __syncthreads();
   if (*last != 0 && p.ns > 0) {
-    const int n = (int)(g.M * p.s.ad.r);
+    const int n = (int)(g.M * p.s.ad.zld);
     const auto zr = make_rsrc(g.z, (uint32_t)(n * 4));
     for (int e = 4 * threadIdx.x; e < n; e += 4 * NW * 64) buf_store16<kCoherent>(zr, 4u * e, make_uint4(0u, 0u, 0u, 0u));
   }
@@ -173,7 +176,7 @@ hipError_t launch_decode_lora(const uint16_t* x, int64_t ldx, int64_t M, int64_t
                               uint8_t* xq_out, float* sx_out, int64_t ldq_out, void* ws, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   char* wsb = reinterpret_cast<char*>(ws);
-  const DecodeWs lay = decode_ws(M, K, ad.r);
+  const DecodeWs lay = decode_ws(M, K, ad.r, ad.S);
   int* ctrl = reinterpret_cast<int*>(ws);
   DecodeParams p{};
   SkinnyJob& J = p.job;
@@ -202,7 +205,7 @@ hipError_t launch_decode_lora(const uint16_t* x, int64_t ldx, int64_t M, int64_t
   s.partials = reinterpret_cast<float*>(wsb + lay.shrink.partials);
   s.splits = shrink_splits(M, K, ad.r);
   p.tiles = (int)cdiv(M, kShrinkTokens);
-  p.ns = adapters ? p.tiles * s.splits : 0;
+  p.ns = adapters ? p.tiles * s.splits * ad.S : 0;
   const bool want_xq = xq_out != nullptr || sx_out != nullptr;
   if (wt.fmt == EPILORA_W_FP8) dispatch_decode<EPILORA_W_FP8>(p, want_xq, stream);
   else dispatch_decode<EPILORA_W_FP4>(p, want_xq, stream);

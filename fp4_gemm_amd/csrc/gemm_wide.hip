@@ -19,7 +19,9 @@
 // XCD runs together share a few weight tiles in that XCD's L2.
 //
 // Epilogue: the accumulators are scaled in place, (acc * sx_t) * sw_n (or
-// gs * 8).  With adapters, z for the tile's tokens is staged in LDS as bf16
+// gs * 8).  With adapters, z for the tile's tokens (the columns of the output
+// slice the tile lies in, for projections with per-slice adapters) is staged
+// in LDS as bf16
 // and the distinct adapters of the tile's tokens are taken in turn: every
 // 16-token block holding one of the adapter's tokens multiplies z (other
 // tokens zero) by the adapter's B rows on bf16 MFMA; only the adapter's own
@@ -261,6 +263,9 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(BM
   // (128 ranks), 16-byte chunks swizzled by (token % 16).
   if (p.z != nullptr) {
     const int r = p.ad.r;
+    // The tile's outputs lie inside one output slice (the host requires
+    // slice widths that are multiples of the tile width): its z columns.
+    const int zsl = slice_of(p.ad, n0);
     constexpr int ZIT = BM * 16 / kWideThreads;  // bf16 chunks (8 ranks) per thread
     constexpr int ZB = ZIT;                      // chunks in flight: all
     float4 zf[ZB][2];
@@ -270,7 +275,7 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(BM
         const int e = tid + (i0 + i) * kWideThreads;
         const int t = e >> 4, cb = e & 15;
         const bool ok = m0 + t < p.M && 8 * cb < r;
-        const float4* src = reinterpret_cast<const float4*>(p.z + (m0 + t) * r + 8 * cb);
+        const float4* src = reinterpret_cast<const float4*>(p.z + (m0 + t) * p.ad.zld + zsl * r + 8 * cb);
         zf[i][0] = ok ? src[0] : make_float4(0.f, 0.f, 0.f, 0.f);
         zf[i][1] = ok ? src[1] : make_float4(0.f, 0.f, 0.f, 0.f);
       }

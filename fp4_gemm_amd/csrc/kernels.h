@@ -8,16 +8,33 @@
 
 namespace epilora {
 
-// Adapter metadata as the kernels see it.
+constexpr int kMaxSlices = 4;
+
+// Adapter metadata as the kernels see it.  A projection's outputs may be S
+// consecutive slices, each with its own adapter pair: A holds the slices'
+// down-projections side by side ([L][S][r][K]), B the rows of each slice's
+// up-projection in place ([L][N][r]), z the slices' results side by side
+// ([M][S r]).  S = 1 is the plain layer.
 struct AdapterArgs {
-  const uint16_t* A;     // [L][r][K]
+  const uint16_t* A;     // [L][S][r][K]
   const uint16_t* B;     // [L][N][r]
-  const int32_t* ranks;  // [L] or null
+  const int32_t* ranks;  // [L] or null (one rank for every slice of an adapter)
   const int32_t* idx;    // [M] or null (no adapters)
   const uint8_t* mask;   // [M] or null
   int32_t L, r;
   float scale;
+  int32_t S;                     // slices, 1..kMaxSlices
+  int32_t zld;                   // z row stride: S * r
+  int64_t slice_end[kMaxSlices]; // end (exclusive) of each slice's outputs
 };
+
+// The slice output n falls in.
+__host__ __device__ inline int slice_of(const AdapterArgs& ad, int64_t n) {
+  int s = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxSlices - 1; ++i) s += (i < ad.S - 1 && n >= ad.slice_end[i]) ? 1 : 0;
+  return s;
+}
 
 // Base-weight operand.
 struct WeightArgs {

@@ -36,7 +36,7 @@ constexpr size_t kDoneOffset = kCtrlBytes;
 constexpr int64_t kMaxShrinkTiles = 4096;  // the shrink takes M <= 65536 per call
 constexpr size_t kTileCounterOffset = kDoneOffset + (size_t)kDoneGroups * kDoneStride * 4;
 constexpr size_t kZOffset = align256(kTileCounterOffset + 4 * (size_t)kMaxShrinkTiles);
-constexpr size_t kZBytes = 64 * 128 * 4;
+constexpr size_t kZBytes = 64 * 512 * 4;  // M <= 64 tokens, up to 4 slices of rank 128
 constexpr size_t kStateBytes = align256(kZOffset + kZBytes);
 
 // ---- shrink -----------------------------------------------------------------
@@ -84,12 +84,14 @@ struct ShrinkWs {
 };
 
 // `base`: where the shrink's data region may start (at least kStateBytes).
-inline ShrinkWs shrink_ws(size_t base, int64_t M, int64_t K, int32_t r) {
+// r is the slot width of one slice; S slices each keep their own partials.
+// The tile counters ([tiles][S] words) hold at most kMaxShrinkTiles.
+inline ShrinkWs shrink_ws(size_t base, int64_t M, int64_t K, int32_t r, int32_t S = 1) {
   ShrinkWs w;
   const int s = shrink_splits(M, K, r);
   w.counters = kTileCounterOffset;
   w.partials = align256(base);
-  w.total = align256(w.partials + (s > 1 ? (size_t)s * M * r * 4 : 0));
+  w.total = align256(w.partials + (s > 1 ? (size_t)s * M * r * 4 * S : 0));
   return w;
 }
 
@@ -102,12 +104,12 @@ struct DecodeWs {
   size_t total;
 };
 
-inline DecodeWs decode_ws(int64_t M, int64_t K, int32_t r) {
+inline DecodeWs decode_ws(int64_t M, int64_t K, int32_t r, int32_t S = 1) {
   DecodeWs w;
   w.xq = kStateBytes;
   w.sx = align256(w.xq + (size_t)M * K);
   w.z = align256(w.sx + 4 * (size_t)M);
-  w.shrink = shrink_ws(align256(w.z + 4 * (size_t)M * r), M, K, r);
+  w.shrink = shrink_ws(align256(w.z + 4 * (size_t)M * r * S), M, K, r, S);
   w.total = w.shrink.total;
   return w;
 }

@@ -10,8 +10,10 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) 
   extern __shared__ float red[];  // [4 waves][16 tokens][r]
   int s_begin, s_end;
   shrink_range(p, blockIdx.y, s_begin, s_end);
-  const uint64_t active = shrink_tile<4>(p, (int64_t)blockIdx.x * kShrinkTokens, s_begin, s_end, red, blockIdx.y == 0);
-  shrink_finish<4>(p, blockIdx.x, blockIdx.y, red, active);
+  const int slice = blockIdx.z;
+  const uint64_t active = shrink_tile<4>(p, (int64_t)blockIdx.x * kShrinkTokens, slice, s_begin, s_end, red,
+                                         blockIdx.y == 0 && slice == 0);
+  shrink_finish<4>(p, blockIdx.x, slice, blockIdx.y, red, active);
 }
 
 // ---------------------------------------------------------------------------
@@ -38,12 +40,12 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_wide_kernel(ShrinkParam
   const int col = lane & 15, grp = lane >> 4;
   const int r = p.ad.r;
   const int64_t K = p.K;
-  const int tile = blockIdx.x, split = blockIdx.y;
+  const int tile = blockIdx.x, split = blockIdx.y, slice = blockIdx.z;
   const int64_t t0 = (int64_t)tile * kShrinkWideTokens;
   int s_begin, s_end;
   shrink_range(p, split, s_begin, s_end);
   int rank_l;  // lane l resolves token t0 + l (the same in every wave)
-  const int a_l = resolve_token(t0 + lane, p.M, p.ad, p.ctrl + kCtrlError, split == 0 && wave == 0, rank_l);
+  const int a_l = resolve_token(t0 + lane, p.M, p.ad, p.ctrl + kCtrlError, split == 0 && slice == 0 && wave == 0, rank_l);
 
   f32x4 acc[kMaxJB];
 #pragma unroll
@@ -78,7 +80,7 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_wide_kernel(ShrinkParam
     const int jbn = (rank + 15) >> 4;
     const bool mine = ((members >> (16 * wave)) & 0xFFFFull) != 0;
     const bool member = (members >> (16 * wave + col)) & 1;
-    const uint16_t* Aa = p.ad.A + (int64_t)a * r * K;
+    const uint16_t* Aa = p.ad.A + ((int64_t)a * p.ad.S + slice) * r * K;
     const uint16_t* xr = p.x + (t0 + 16 * wave + col) * p.ldx;
     if (s_begin < s_end) a_load(Aa, rank, s_begin);
     for (int s = s_begin; s < s_end; ++s) {
@@ -112,13 +114,13 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_wide_kernel(ShrinkParam
       *reinterpret_cast<float4*>(&red[(16 * wave + col) * r + jb * 16 + 4 * grp]) =
           make_float4(acc[jb][0], acc[jb][1], acc[jb][2], acc[jb][3]);
   __syncthreads();
-  shrink_finish<4, kShrinkWideTokens>(p, tile, split, red, __ballot(a_l >= 0));
+  shrink_finish<4, kShrinkWideTokens>(p, tile, slice, split, red, __ballot(a_l >= 0));
 }
 
 hipError_t launch_shrink(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const AdapterArgs& ad,
                          float* z, void* ws, hipStream_t stream) {
   if (M == 0) return hipSuccess;
-  const ShrinkWs lay = shrink_ws(kStateBytes, M, K, ad.r);
+  const ShrinkWs lay = shrink_ws(kStateBytes, M, K, ad.r, ad.S);
   ShrinkParams p;
   p.x = x; p.M = M; p.K = K; p.ldx = ldx; p.ad = ad; p.z = z;
   p.ctrl = reinterpret_cast<int*>(ws);
@@ -127,11 +129,11 @@ hipError_t launch_shrink(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, c
   p.splits = shrink_splits(M, K, ad.r);
   p.zflip = 0u;
   if (M > kShrinkWideM) {
-    const dim3 grid((unsigned)cdiv(M, kShrinkWideTokens), (unsigned)p.splits);
+    const dim3 grid((unsigned)cdiv(M, kShrinkWideTokens), (unsigned)p.splits, (unsigned)ad.S);
     hipLaunchKernelGGL(shrink_wide_kernel, grid, dim3(kShrinkThreads), 0, stream, p);
     return hipGetLastError();
   }
-  const dim3 grid((unsigned)cdiv(M, kShrinkTokens), (unsigned)p.splits);
+  const dim3 grid((unsigned)cdiv(M, kShrinkTokens), (unsigned)p.splits, (unsigned)ad.S);
   const size_t lds = (size_t)kShrinkWaves * 16 * ad.r * sizeof(float);
   hipLaunchKernelGGL(shrink_kernel, grid, dim3(kShrinkThreads), lds, stream, p);
   return hipGetLastError();
@@ -154,7 +156,7 @@ __global__ __launch_bounds__(256) void expand_add_kernel(const float* __restrict
   if (n >= N) return;
   const int r = ad.r;
   const uint16_t* br = ad.B + ((int64_t)a * N + n) * r;
-  const float* zr = z + t * r;
+  const float* zr = z + t * ad.zld + slice_of(ad, n) * r;
   float acc = 0.f;
   int j = 0;
   for (; j + 8 <= rank; j += 8) {

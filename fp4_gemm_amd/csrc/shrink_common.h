@@ -35,7 +35,7 @@ struct ShrinkParams {
   const uint16_t* x;
   int64_t M, K, ldx;
   AdapterArgs ad;
-  float* z;
+  float* z;  // [M][ad.zld]
   int* ctrl;
   int* counters;
   float* partials;
@@ -49,9 +49,10 @@ __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<
 // result in `red` (LDS of kShrinkWaves * 16 * r floats) and returns the
 // tile's active tokens as a bit mask (bit i: token t0 + i).  Every thread of
 // the block must call it.
+// `slice`: which of the projection's output slices (its own A) this is.
 template <int NW>
-__device__ __forceinline__ uint64_t shrink_tile(const ShrinkParams& p, int64_t t0, int s_begin, int s_end, float* red,
-                                            bool report) {
+__device__ __forceinline__ uint64_t shrink_tile(const ShrinkParams& p, int64_t t0, int slice, int s_begin, int s_end,
+                                                float* red, bool report) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int r = p.ad.r;
@@ -78,7 +79,7 @@ __device__ __forceinline__ uint64_t shrink_tile(const ShrinkParams& p, int64_t t
     pending &= ~members;
     const bool member = (members >> col) & 1;
     const int jbn = (rank + 15) >> 4;
-    const uint16_t* Aa = p.ad.A + (int64_t)a * r * K;
+    const uint16_t* Aa = p.ad.A + ((int64_t)a * p.ad.S + slice) * r * K;
     const uint16_t* xr = p.x + (t0 + col) * p.ldx;
     for (int s = s_begin + ws; s < s_end; s += WS) {
       const int64_t k = (int64_t)s * kShrinkStep + grp * 32;
@@ -186,14 +187,21 @@ __device__ __forceinline__ void combine_partials(const float* partials, int spli
   __syncthreads();
 }
 
+// The split partials of one slice: [splits][M][r] fp32, one such block per
+// slice.
+__device__ __forceinline__ float* slice_partials(const ShrinkParams& p, int slice) {
+  return p.partials + (int64_t)slice * p.splits * p.M * p.ad.r;
+}
+
 // Store this workgroup's [rows][r] sums (in LDS `red`) as its split's
 // partial with device-coherent stores; returns once they have completed.
 template <int NW, int TT = kShrinkTokens>
-__device__ __forceinline__ void shrink_store_partial(const ShrinkParams& p, int tile, int split, const float* red) {
+__device__ __forceinline__ void shrink_store_partial(const ShrinkParams& p, int tile, int slice, int split,
+                                                     const float* red) {
   const int64_t t0 = (int64_t)tile * TT;
   const int r = p.ad.r;
   const int64_t rows = p.M - t0 < TT ? p.M - t0 : TT;
-  const auto pr = make_rsrc(p.partials + ((int64_t)split * p.M + t0) * r, (uint32_t)(rows * r * 4));
+  const auto pr = make_rsrc(slice_partials(p, slice) + ((int64_t)split * p.M + t0) * r, (uint32_t)(rows * r * 4));
   for (int e = 4 * threadIdx.x; e < rows * r; e += 4 * NW * kWave)
     buf_store16<kCoherent>(pr, 4 * e, *reinterpret_cast<const uint4*>(&red[e]));
   wait_all_memory();
@@ -213,37 +221,39 @@ __device__ __forceinline__ void shrink_store_partial(const ShrinkParams& p, int 
 // region by the last one is ordered after all of them.  A store to a row no
 // consumer polls could otherwise land after that clear and survive, as a
 // stale nonzero word, into the next call on the same workspace.
+// `slice`: the tile's z goes to columns slice * r .. + r of the [M][S r] z.
 template <int NW, int TT = kShrinkTokens>
-__device__ __forceinline__ bool shrink_finish(const ShrinkParams& p, int tile, int split, float* red,
+__device__ __forceinline__ bool shrink_finish(const ShrinkParams& p, int tile, int slice, int split, float* red,
                                               uint64_t active) {
   __shared__ int last;
   const int64_t t0 = (int64_t)tile * TT;
-  const int r = p.ad.r;
+  const int r = p.ad.r, zld = p.ad.zld;
   const int64_t rows = p.M - t0 < TT ? p.M - t0 : TT;
-  const uint32_t tile_bytes = (uint32_t)(rows * r * 4);
-  const auto zr = make_rsrc(p.z + t0 * r, tile_bytes);
+  const auto zr = make_rsrc(p.z + t0 * zld + slice * r, (uint32_t)(((rows - 1) * zld + r) * 4));
+  auto zoff = [&](int e) { return (uint32_t)(((e / r) * zld + e % r) * 4); };  // e: a word of the tile, row-major
   const uint32_t f = p.zflip;
-  auto keep = [&](int e) { return f == 0u || ((active >> (e / r)) & 1ull) != 0; };  // e: a word of the tile
+  auto keep = [&](int e) { return f == 0u || ((active >> (e / r)) & 1ull) != 0; };
   if (p.splits == 1) {
     for (int e = 4 * threadIdx.x; e < rows * r; e += 4 * NW * kWave) {
       const uint4 v = *reinterpret_cast<const uint4*>(&red[e]);
-      if (keep(e)) buf_store16<kCoherent>(zr, 4 * e, make_uint4(v.x ^ f, v.y ^ f, v.z ^ f, v.w ^ f));
+      if (keep(e)) buf_store16<kCoherent>(zr, zoff(e), make_uint4(v.x ^ f, v.y ^ f, v.z ^ f, v.w ^ f));
     }
     wait_all_memory();
     __syncthreads();
     return true;
   }
-  shrink_store_partial<NW, TT>(p, tile, split, red);
-  if (threadIdx.x == 0) last = atomic_add_relaxed(&p.counters[tile], 1) == p.splits - 1;
+  shrink_store_partial<NW, TT>(p, tile, slice, split, red);
+  int* counter = &p.counters[tile * p.ad.S + slice];
+  if (threadIdx.x == 0) last = atomic_add_relaxed(counter, 1) == p.splits - 1;
   __syncthreads();
   if (!last) return false;
   // `red` is free again and holds the chunk sums.
-  combine_partials<NW * kWave>(p.partials, p.splits, p.M, t0, rows, r, red, [&](int q, const float4& v) {
+  combine_partials<NW * kWave>(slice_partials(p, slice), p.splits, p.M, t0, rows, r, red, [&](int q, const float4& v) {
     if (keep(4 * q))
-      buf_store16<kCoherent>(zr, 16u * q, make_uint4(__float_as_uint(v.x) ^ f, __float_as_uint(v.y) ^ f,
-                                                     __float_as_uint(v.z) ^ f, __float_as_uint(v.w) ^ f));
+      buf_store16<kCoherent>(zr, zoff(4 * q), make_uint4(__float_as_uint(v.x) ^ f, __float_as_uint(v.y) ^ f,
+                                                         __float_as_uint(v.z) ^ f, __float_as_uint(v.w) ^ f));
   });
-  if (threadIdx.x == 0) store_relaxed(&p.counters[tile], 0);
+  if (threadIdx.x == 0) store_relaxed(counter, 0);
   wait_all_memory();
   __syncthreads();
   return true;

@@ -252,6 +252,7 @@ struct Skinny {
   uint32_t kofs, xbase[MB];
   __amdgpu_buffer_rsrc_t xr;
   bool adapters;
+  int zslice;    // unfused: the slice whose z is staged in LDS
   float gscale;  // 4-bit weights: gs * 8
 
   __device__ __forceinline__ Skinny(const SkinnyJob& j, char* lds, int gidx) : J(j), p(j.g), g(gidx) {
@@ -506,10 +507,10 @@ struct Skinny {
   // wall-clock limit.  Returns false on a timeout (or when the host has set
   // the workspace's force-timeout word, read with the first poll).  Ends with
   // a barrier.
-  __device__ __forceinline__ bool poll_z() const {
+  __device__ __forceinline__ bool poll_z(int slice) const {
     const int r = p.ad.r;
     const int n = (int)p.M * r;
-    const auto zr = make_rsrc(p.z, (uint32_t)(n * 4));
+    const auto zr = make_rsrc(p.z + slice * r, (uint32_t)(((p.M - 1) * p.ad.zld + r) * 4));
     int* err = p.ctrl + kCtrlError;
     const int64_t start = wall_clock64();
     for (;;) {
@@ -519,7 +520,7 @@ struct Skinny {
         if (tok[e / r].a < 0) {
           zs[e] = 0.f;
         } else {
-          const uint32_t w = buf_load4<kCoherent>(zr, 4u * e);
+          const uint32_t w = buf_load4<kCoherent>(zr, 4u * ((e / r) * p.ad.zld + e % r));
           if (w == 0u) missing = 1;
           else zs[e] = __uint_as_float(~w);
         }
@@ -544,13 +545,15 @@ struct Skinny {
     }
   }
 
-  // z (M x r fp32) into LDS, rows of inactive tokens as zero.  Ends with a
-  // barrier.
-  __device__ __forceinline__ void stage_z() const {
+  // One slice's z (M x r fp32, columns slice * r .. + r of the [M][S r] z)
+  // into LDS, rows of inactive tokens as zero.  Starts and ends with a
+  // barrier (the previous slice's values may still be read).
+  __device__ __forceinline__ void stage_z(int slice) const {
     const int r = p.ad.r;
-    const auto zr = make_rsrc(p.z, (uint32_t)(p.M * r * 4));
+    const auto zr = make_rsrc(p.z + slice * r, (uint32_t)(((p.M - 1) * p.ad.zld + r) * 4));
+    __syncthreads();
     for (int e = threadIdx.x; e < p.M * r; e += NW * kWave)
-      zs[e] = tok[e / r].a >= 0 ? __uint_as_float(buf_load4<XPOL>(zr, 4u * e)) : 0.f;
+      zs[e] = tok[e / r].a >= 0 ? __uint_as_float(buf_load4<XPOL>(zr, 4u * ((e / r) * p.ad.zld + e % r))) : 0.f;
     __syncthreads();
   }
 
@@ -584,6 +587,13 @@ struct Skinny {
       return;
     }
     reduce_tile(acc, red);
+    if (adapters && p.ad.S > 1) {  // a tile lies inside one slice; the slices come in order
+      const int sl = slice_of(p.ad, n0_of(j));
+      if (sl != zslice) {
+        stage_z(sl);
+        zslice = sl;
+      }
+    }
     outputs(n0_of(j), red, true, pre, pws);
     if (j + 1 < total) {
       pre = b_chunk(n0_of(j + 1), threadIdx.x >> 4);
@@ -601,11 +611,22 @@ struct Skinny {
 #pragma unroll
     for (int s = 0; s < S; ++s)
       if (s < mine) pb[s] = b_chunk(n0_of(s * nb), threadIdx.x >> 4);
-    if (adapters) ok = poll_z();
-    if (!ok) return;
+    // The tiles come in output order: for each slice they span (one unless
+    // the projection has several), poll that slice's z into LDS, then write
+    // the outputs of the tiles inside it.
+    const int sl0 = mine > 0 ? slice_of(p.ad, n0_of(0)) : 0;
+    const int sl1 = mine > 0 ? slice_of(p.ad, n0_of((mine - 1) * nb)) : 0;
+    for (int sl = sl0; sl <= sl1; ++sl) {
+      if (adapters) {
+        if (sl > sl0) __syncthreads();  // the previous slice's z is no longer read
+        ok = poll_z(sl);
+        if (!ok) return;
+      }
 #pragma unroll
-    for (int s = 0; s < S; ++s)
-      if (s < mine) outputs(n0_of(s * nb), stash + s * T * 16, true, pb[s], pw[s]);
+      for (int s = 0; s < S; ++s)
+        if (s < mine && (sl0 == sl1 || slice_of(p.ad, n0_of(s * nb)) == sl))
+          outputs(n0_of(s * nb), stash + s * T * 16, true, pb[s], pw[s]);
+    }
   }
 
   // ---- the whole job --------------------------------------------------------
@@ -637,7 +658,10 @@ struct Skinny {
     }
     if (!FUSED) {
       for (int t = threadIdx.x; t < M; t += NT) sxs[t] = p.sx[t];
-      if (adapters) stage_z();
+      if (adapters) {
+        zslice = total > 0 ? slice_of(p.ad, n0_of(0)) : 0;
+        stage_z(zslice);
+      }
     }
     __syncthreads();
 

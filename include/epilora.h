@@ -138,6 +138,19 @@ typedef struct epilora_layer_args {
   /* Scratch. */
   void* ws;
   size_t ws_bytes;
+  /* Projections whose N outputs are several consecutive slices, each with
+     its own adapter pair (attention's query / key / value, the MLP's gate /
+     up: "EpiLoRA ...", Evaluation, the many-tenant results and the
+     appendix's comparison of expand costs, Tables 14 and 15): nslices in
+     0..4 (0 or 1: one slice, the plain layer), slice_n[s] the width of
+     slice s (sum N).  Then A is [L][nslices][r][K] (slice s's
+     down-projection of adapter a at A[a][s]), B stays [L][N][r] (the rows of
+     slice s hold its up-projection) and z is [M][nslices * r] (slice s in
+     columns s*r .. s*r+r).  Output n of slice s adds s * B[a][n] . z_s.
+     Widths must be multiples of 16 (M <= 64) or 128 (M > 64), else
+     EPILORA_ERR_UNSUPPORTED. */
+  int32_t nslices;
+  int64_t slice_n[4];
 } epilora_layer_args;
 
 /* Library version (EPILORA_VERSION of the build). */
@@ -146,8 +159,10 @@ int epilora_version(void);
 /* Static text for a status code. */
 const char* epilora_strerror(int status);
 
-/* Bytes of workspace `op` needs for a call of the given sizes (r = slot
- * width); each call checks its own need against ws_bytes.  One workspace may
+/* Bytes of workspace `op` needs for a call of the given sizes (r = the row
+ * width of z: the slot width, times the number of output slices for a
+ * projection with per-slice adapters); each call checks its own need
+ * against ws_bytes.  One workspace may
  * serve every call on one stream in turn (the pages' plugin shares its
  * scratch buffers across layers: "The vLLM plugin", Memory); calls that
  * overlap in time must not share one. */
@@ -214,6 +229,20 @@ int epilora_lora_shrink(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                         const uint8_t* mask, float* z, void* ws,
                         size_t ws_bytes, void* stream);
 
+/* The shrink of a projection with per-slice adapters (see
+ * epilora_layer_args.nslices): A is [L][nslices][r][K], z is
+ * [M][nslices * r]; slice s's z_s[t] = A[idx[t]][s] x[t] goes to columns
+ * s*r .. s*r+r, under the same activity rule, rank and determinism as
+ * epilora_lora_shrink (which is this call with nslices = 1).  nslices in
+ * 1..4; cdiv(M, 16) * nslices <= 4096.  Needs a workspace of
+ * EPILORA_OP_SHRINK with r = nslices * r. */
+int epilora_lora_shrink_sliced(const uint16_t* x, int64_t M, int64_t K,
+                               int64_t ldx, const uint16_t* A, int32_t L,
+                               int32_t nslices, int32_t r,
+                               const int32_t* ranks, const int32_t* idx,
+                               const uint8_t* mask, float* z, void* ws,
+                               size_t ws_bytes, void* stream);
+
 /* The low-precision GEMM with the multi-adapter epilogue
  * ("Multi-adapter kernels", K2; "Kernel details", one output tile of K2).
  * base[t][n] = (acc[t][n] * sx[t]) * sw[n] for FP8 weights, where
@@ -239,6 +268,17 @@ int epilora_lora_expand_add(const float* z, int64_t M, int64_t N,
                             const uint8_t* mask, float scale, uint16_t* y,
                             int64_t ldy, void* ws, size_t ws_bytes,
                             void* stream);
+
+/* The separate up-projection of a projection with per-slice adapters: z is
+ * [M][nslices * r] and output n of slice s uses z_s (slice widths slice_n,
+ * a host array of nslices entries summing to N). */
+int epilora_lora_expand_add_sliced(const float* z, int64_t M, int64_t N,
+                                   const uint16_t* B, int32_t L, int32_t r,
+                                   int32_t nslices, const int64_t* slice_n,
+                                   const int32_t* ranks, const int32_t* idx,
+                                   const uint8_t* mask, float scale,
+                                   uint16_t* y, int64_t ldy, void* ws,
+                                   size_t ws_bytes, void* stream);
 
 /* The fused small-batch (decode) path ("Multi-adapter kernels", The decode
  * path): quantization, shrink and the GEMM with its epilogue in ONE launch.

@@ -75,7 +75,9 @@ class DeviceGemm:
             ep.epilora_quant_weight_fp4(w, self.wq, self.bs, self.gs, ws)
             self.wkw = dict(bs=self.bs, gs=self.gs)
         del w
-        self.A_np = g.A()
+        self.slices = g.slices
+        self.S = len(g.slices) if g.slices else 1
+        self.A_np = g.A_sliced() if g.slices else g.A()
         self.B_np = g.B()
         self.A = to_dev(self.A_np)
         self.B = to_dev(self.B_np)
@@ -93,8 +95,8 @@ class DeviceGemm:
         return xq, sx
 
     def shrink(self, ws=None):
-        ws = ws if ws is not None else ep.new_workspace(ep.OP_SHRINK, self.M, self.N, self.K, self.r)
-        z = torch.empty(self.M, self.r, dtype=torch.float32, device=DEV)
+        ws = ws if ws is not None else ep.new_workspace(ep.OP_SHRINK, self.M, self.N, self.K, self.r * self.S)
+        z = torch.empty(self.M, self.r * self.S, dtype=torch.float32, device=DEV)
         ep.epilora_lora_shrink(self.x, self.A, self.idx, z, ws, ranks=self.ranks, mask=self.mask)
         return z, ws
 
@@ -105,7 +107,7 @@ class DeviceGemm:
         else:
             ws = ws if ws is not None else ep.new_workspace(ep.OP_GEMM, self.M, self.N, self.K, self.r)
             ep.epilora_gemm_lora(xq, sx, self.wq, y, z=z, B=self.B, idx=self.idx, ranks=self.ranks,
-                                 mask=self.mask, scale=self.scale, ws=ws, **self.wkw)
+                                 mask=self.mask, scale=self.scale, ws=ws, slices=self.slices, **self.wkw)
         return y
 
     def separate(self):
@@ -115,12 +117,13 @@ class DeviceGemm:
         return dict(xq=xq, sx=sx, z=z, y=y, ws=ws)
 
     def decode(self, ws=None, keep_xq=True):
-        ws = ws if ws is not None else ep.new_workspace(ep.OP_DECODE, self.M, self.N, self.K, self.r)
+        ws = ws if ws is not None else ep.new_workspace(ep.OP_DECODE, self.M, self.N, self.K, self.r * self.S)
         y = torch.empty(self.M, self.N, dtype=torch.bfloat16, device=DEV)
         xq = torch.empty(self.M, self.K, dtype=torch.uint8, device=DEV) if keep_xq else None
         sx = torch.empty(self.M, dtype=torch.float32, device=DEV) if keep_xq else None
         ep.epilora_decode_lora(self.x, self.wq, y, A=self.A, B=self.B, idx=self.idx, ranks=self.ranks,
-                               mask=self.mask, scale=self.scale, ws=ws, xq_out=xq, sx_out=sx, **self.wkw)
+                               mask=self.mask, scale=self.scale, ws=ws, xq_out=xq, sx_out=sx,
+                               slices=self.slices, **self.wkw)
         return dict(xq=xq, sx=sx, y=y, ws=ws)
 
     # -- the oracle on the same inputs ----------------------------------------
@@ -136,7 +139,12 @@ class DeviceGemm:
         else:
             wc, bs, gs = oracle.quant_weight_fp4(self.w_np, rows=cols)
             wkw = dict(wc=wc, bs=bs, gs=gs)
-        out = oracle.linear_lora(self.x_np, self.A_np, B, lay.idx, lay.scale, ranks=lay.ranks,
-                                 mask=lay.mask, rows=rows, **wkw)
+        if self.slices:
+            out = oracle.linear_lora_sliced(self.x_np, self.A_np, self.B_np, lay.idx, lay.scale, self.slices,
+                                            ranks=lay.ranks, mask=lay.mask, rows=rows, cols=cols,
+                                            weights_of_cols=cols is not None, **wkw)
+        else:
+            out = oracle.linear_lora(self.x_np, self.A_np, B, lay.idx, lay.scale, ranks=lay.ranks,
+                                     mask=lay.mask, rows=rows, **wkw)
         out["w"] = wkw
         return out

@@ -32,7 +32,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 16
     for n in names:
         assert hasattr(L, n), n
         assert n in ep.SIGNATURES, n
@@ -49,7 +49,8 @@ def test_version_and_strerror(L):
 def test_layer_args_layout_matches_header():
     # 3 sizes, x+ldx, xq+sx+ldq, wfmt(+pad), 4 weight ptrs, L+r, 6 ptrs, scale(+pad),
     # y+ldy, xq_out+sx_out+ldq_out, ws+ws_bytes
-    assert ctypes.sizeof(ep.LayerArgs) == 8 * 3 + 16 + 24 + 8 + 32 + 8 + 48 + 8 + 16 + 24 + 16
+    assert ctypes.sizeof(ep.LayerArgs) == 8 * 3 + 16 + 24 + 8 + 32 + 8 + 48 + 8 + 16 + 24 + 16 + 8 + 32
+    assert ep.LayerArgs.slice_n.offset == 8 * 3 + 16 + 24 + 8 + 32 + 8 + 48 + 8 + 16 + 24 + 16 + 8
     assert ep.LayerArgs.scale.offset == 8 * 3 + 16 + 24 + 8 + 32 + 8 + 48
 
 
@@ -133,6 +134,35 @@ def test_gemm_lora_validation(L):
     assert g(z=P, ws=None) == ep.ERR_WORKSPACE
     assert g(z=P, r=24) == ep.ERR_UNSUPPORTED
     assert g(M=0) == ep.OK and g(N=0) == ep.OK
+
+
+def _sl(*w):
+    arr = (ctypes.c_int64 * 4)()
+    for i, v in enumerate(w):
+        arr[i] = v
+    return arr
+
+
+def test_slice_validation(L):
+    g = lambda **kw: L.epilora_gemm_lora(ctypes.byref(_layer(z=P, **kw)), None)
+    assert g(nslices=5, slice_n=_sl(128, 128, 128, 128)) == ep.ERR_INVALID_ARG      # at most 4 slices
+    assert g(nslices=2, slice_n=_sl(256, 128)) == ep.ERR_INVALID_ARG                # widths do not sum to N
+    assert g(nslices=2, slice_n=_sl(512, 0)) == ep.ERR_INVALID_ARG                  # empty slice
+    assert g(nslices=2, slice_n=_sl(248, 264)) == ep.ERR_UNSUPPORTED                # not whole 16-row tiles
+    assert g(M=100, nslices=2, slice_n=_sl(256 + 64, 192)) == ep.ERR_UNSUPPORTED    # prefill: 128-wide tiles
+    d = lambda **kw: L.epilora_decode_lora(ctypes.byref(_layer(**kw)), None)
+    assert d(nslices=3, slice_n=_sl(256, 128, 112)) == ep.ERR_INVALID_ARG
+    assert d(nslices=3, slice_n=_sl(256, 136, 120)) == ep.ERR_UNSUPPORTED
+    sh = L.epilora_lora_shrink_sliced
+    assert sh(P, 4, 256, 256, P, 4, 0, 16, None, P, None, P, P, 1 << 20, None) == ep.ERR_INVALID_ARG
+    assert sh(P, 4, 256, 256, P, 4, 5, 16, None, P, None, P, P, 1 << 20, None) == ep.ERR_INVALID_ARG
+    assert sh(P, 65536, 256, 256, P, 4, 3, 16, None, P, None, P, P, 1 << 40, None) == ep.ERR_UNSUPPORTED
+    e = L.epilora_lora_expand_add_sliced
+    assert e(P, 4, 512, P, 4, 16, 2, _sl(500, 10), None, P, None, 2.0, P2, 512, P, 256, None) == ep.ERR_INVALID_ARG
+    # the workspace need grows with the slices
+    w1 = L.epilora_workspace_bytes(ep.OP_DECODE, 8, 6144, 4096, 64)
+    w3 = L.epilora_workspace_bytes(ep.OP_DECODE, 8, 6144, 4096, 3 * 64)
+    assert w3 > w1
 
 
 def test_decode_validation(L):

@@ -133,3 +133,32 @@ def test_config5_prefill(wfmt, segments, name):
         rms = np.sqrt(np.mean(exact ** 2))
         say(f"  4-bit fold vs exact NVFP4 (base term): max|d|/rms {dev.max() / rms:.3e}  "
             f"mean rel {dev.sum() / np.abs(exact).sum():.3e}")
+
+
+@pytest.mark.parametrize("name", ["qkv", "gate_up"])
+def test_config2_sliced_adapters(name):
+    # the Llama-8B decode projections with one adapter pair per output slice
+    say(f"config 2 sliced {name}")
+    d = DeviceGemm(config(2, sliced=True).gemm(name))
+    fused = d.decode()
+    check(d, fused, seed=23, what=f"cfg2 sliced {name} fused")
+    sep = d.separate()
+    assert torch.equal(sep["y"], fused["y"])
+
+
+def test_config3_sliced_qkv():
+    say("config 3 sliced qkv")
+    d = DeviceGemm(config(3, sliced=True).gemm("qkv"))
+    fused = d.decode()
+    check(d, fused, seed=33, what="cfg3 sliced qkv fused")
+
+
+@pytest.mark.parametrize("wfmt", ["fp8", "fp4"])
+def test_config5_sliced_gate_up(wfmt):
+    say(f"config 5 sliced gate_up {wfmt}")
+    lay = config(5, segments=32, wfmt=wfmt, sliced=True)
+    d = DeviceGemm(lay.gemm("gate_up"), wfmt)
+    out = d.separate()
+    starts = np.flatnonzero(np.r_[True, lay.idx[1:] != lay.idx[:-1]])
+    rows = np.unique(np.concatenate([sample(d.M, 64, 55), starts]))
+    check(d, out, rows=rows, seed=56, what=f"cfg5 sliced gate_up {wfmt}")

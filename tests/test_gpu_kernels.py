@@ -401,3 +401,53 @@ def test_decode_graph_replays_are_deterministic():
         for j, (y, y0) in enumerate(zip(ys, ref)):
             assert torch.equal(y, y0), f"replay {i}, projection {j}"
     assert ep.epilora_device_error(ws) == 0
+
+
+# --- projections with per-slice adapters (qkv: 3 slices, gate_up: 2) ---------------------
+
+SLICE_CASES = [
+    # M, K, slice widths, L, r, idx kind, mask, ranks, wfmt
+    (1, 4096, (4096, 1024, 1024), 1, 64, "zero", False, False, "fp8"),
+    (5, 512, (256, 64, 64), 4, 16, "mixed", True, True, "fp8"),
+    (24, 1024, (512, 512), 6, 32, "mixed", False, True, "fp4"),
+    (64, 512, (160, 48, 48, 80), 9, 16, "mixed", True, False, "fp8"),
+    (300, 512, (512, 128, 128), 6, 64, "sorted", True, True, "fp8"),
+    (1100, 256, (6144, 6144), 4, 128, "sorted", False, False, "fp8"),
+    (200, 1024, (384, 128, 256), 5, 32, "mixed", False, True, "fp4"),
+]
+
+
+@pytest.mark.parametrize("M,K,slices,L,r,kind,use_mask,use_ranks,wfmt", SLICE_CASES)
+def test_sliced_vs_oracle(M, K, slices, L, r, kind, use_mask, use_ranks, wfmt):
+    N = sum(slices)
+    say(f"sliced M={M} K={K} slices={slices} L={L} r={r} {kind} {wfmt}")
+    rng = np.random.default_rng(8000 + M + K + N)
+    idx = _idx(kind, M, L, rng)
+    mask = rng.integers(0, 2, M).astype(np.uint8) if use_mask else None
+    ranks = rng.choice([0, 16, r // 2, r], size=L).astype(np.int32) if use_ranks else None
+    lay = custom_layer("sl", 800 + M + N, M, K, N, L, r, idx, mask=mask, ranks=ranks, wfmt=wfmt, slices=slices)
+    d = DeviceGemm(lay.gemms[0], wfmt)
+    sep = d.separate()
+    ref = d.oracle()
+    assert np.array_equal(to_np(sep["xq"]), ref["xq"])
+    # the shrink: every slice's z against the oracle's, zero rows elsewhere
+    zg = to_np(sep["z"]).astype(np.float64)
+    scale = max(np.sqrt(np.mean(ref["z"] ** 2)), 1e-30)
+    assert np.abs(zg - ref["z"]).max() <= 1e-4 * scale
+    assert not zg[~ref["active"]].any()
+    compare(to_np(sep["y"]), ref["y"], f"sliced gemm M={M}")
+    base = to_np(d.gemm(sep["xq"], sep["sx"]))
+    assert np.array_equal(to_np(sep["y"])[~ref["active"]], base[~ref["active"]])
+    if M <= ep.DECODE_MAX_M:
+        fused = d.decode()
+        assert torch.equal(fused["y"], sep["y"])
+        assert ep.epilora_device_error(fused["ws"]) == 0
+    # the separate up-projection: base GEMM, then the sliced expand-add
+    y = d.gemm(sep["xq"], sep["sx"])
+    ep.epilora_lora_expand_add(sep["z"], d.B, d.idx, d.scale, y, sep["ws"], ranks=d.ranks, mask=d.mask,
+                               slices=slices)
+    yg = bf16_np_to_f64(to_np(y))
+    rms = np.sqrt(np.mean(ref["y"] ** 2))
+    bound = 2.0 ** -8 * (np.abs(ref["base"]) + np.abs(ref["y"])) * 1.001 + 1e-4 * rms
+    assert np.all(np.abs(yg - ref["y"]) <= bound)
+    assert ep.epilora_device_error(sep["ws"]) == 0
