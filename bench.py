@@ -65,6 +65,8 @@ class Proj:
     def __init__(self, g, wfmt="fp8", copies=ROTATE):
         lay = g.layer
         self.g, self.M, self.K, self.N, self.r = g, g.M, g.K, g.N, lay.r
+        self.slices = g.slices
+        self.S = len(g.slices) if g.slices else 1
         self.wfmt = wfmt
         self.x = dev(g.x())
         w = dev(g.w())
@@ -82,7 +84,7 @@ class Proj:
             self.w = [(wc, dict(bs=bs, gs=gs))] + [(wc.clone(), dict(bs=bs.clone(), gs=gs.clone()))
                                                    for _ in range(copies - 1)]
         del w
-        A, B = dev(g.A()), dev(g.B())
+        A, B = dev(g.A_sliced() if self.slices else g.A()), dev(g.B())
         self.A = [A] + [A.clone() for _ in range(copies - 1)]
         self.B = [B] + [B.clone() for _ in range(copies - 1)]
         self.idx = dev(lay.idx.astype(np.int32))
@@ -92,9 +94,9 @@ class Proj:
         self.y = torch.empty(self.M, self.N, dtype=torch.bfloat16, device=DEV)
         self.xq = torch.empty(self.M, self.K, dtype=torch.uint8, device=DEV)
         self.sx = torch.empty(self.M, dtype=torch.float32, device=DEV)
-        self.z = torch.empty(self.M, self.r, dtype=torch.float32, device=DEV)
-        self.ws_dec = ep.new_workspace(ep.OP_DECODE, self.M, self.N, self.K, self.r)
-        self.ws_shr = ep.new_workspace(ep.OP_SHRINK, self.M, self.N, self.K, self.r)
+        self.z = torch.empty(self.M, self.r * self.S, dtype=torch.float32, device=DEV)
+        self.ws_dec = ep.new_workspace(ep.OP_DECODE, self.M, self.N, self.K, self.r * self.S)
+        self.ws_shr = ep.new_workspace(ep.OP_SHRINK, self.M, self.N, self.K, self.r * self.S)
         self.copies = copies
 
     def with_batch(self, g):
@@ -111,14 +113,15 @@ class Proj:
         q.y = torch.empty(q.M, q.N, dtype=torch.bfloat16, device=DEV)
         q.xq = torch.empty(q.M, q.K, dtype=torch.uint8, device=DEV)
         q.sx = torch.empty(q.M, dtype=torch.float32, device=DEV)
-        q.z = torch.empty(q.M, q.r, dtype=torch.float32, device=DEV)
-        q.ws_dec = ep.new_workspace(ep.OP_DECODE, q.M, q.N, q.K, q.r)
-        q.ws_shr = ep.new_workspace(ep.OP_SHRINK, q.M, q.N, q.K, q.r)
+        q.z = torch.empty(q.M, q.r * q.S, dtype=torch.float32, device=DEV)
+        q.ws_dec = ep.new_workspace(ep.OP_DECODE, q.M, q.N, q.K, q.r * q.S)
+        q.ws_shr = ep.new_workspace(ep.OP_SHRINK, q.M, q.N, q.K, q.r * q.S)
         return q
 
     def adapters(self, c):
         c %= self.copies
-        return dict(B=self.B[c], idx=self.idx, ranks=self.ranks, mask=self.mask, scale=self.scale)
+        return dict(B=self.B[c], idx=self.idx, ranks=self.ranks, mask=self.mask, scale=self.scale,
+                    slices=self.slices)
 
     # paths ------------------------------------------------------------------
     def fused(self, c):
@@ -147,7 +150,7 @@ class Proj:
 
     def expand(self, c):
         ep.epilora_lora_expand_add(self.z, self.B[c % self.copies], self.idx, self.scale, self.y, self.ws_shr,
-                                   ranks=self.ranks, mask=self.mask)
+                                   ranks=self.ranks, mask=self.mask, slices=self.slices)
 
     # algorithmic counts -------------------------------------------------------
     def adapter_ranks(self):
@@ -164,12 +167,12 @@ class Proj:
             wb = self.K * self.N + 4 * self.N
         else:
             wb = self.K * self.N // 2 + self.K * self.N // 16 + 4
-        ab = sum(2 * rk(a) * (self.K + self.N) for a in distinct)
+        ab = sum(2 * rk(a) * (self.S * self.K + self.N) for a in distinct)
         return wb + ab + 2 * self.M * self.K + 2 * self.M * self.N
 
     def flops(self):
         act, _, rk = self.adapter_ranks()
-        return 2 * self.M * self.N * self.K + sum(2 * rk(a) * (self.K + self.N) for a in act)
+        return 2 * self.M * self.N * self.K + sum(2 * rk(a) * (self.S * self.K + self.N) for a in act)
 
 
 def graph_of(fns, copies, only=None):
@@ -322,6 +325,47 @@ def decode_multitenant(steps, warmup):
                                  for p in projs}}
     del projs
     torch.cuda.empty_cache()
+    return out
+
+
+def sliced_rows(steps, warmup, prefill):
+    """Projections with one adapter pair per output slice (qkv: 3 slices,
+    gate_up: 2): the Llama-8B decode layer at M = 1 with a rank-64 tenant
+    (fused path), its qkv and gate_up alone, and the 2048-token prefill
+    gate_up with 32 tenant segments (quant + shrink + GEMM; FP8)."""
+    out = {}
+    layer = config(2, sliced=True)
+    log("sliced decode layer ...")
+    projs = [Proj(g) for g in layer.gemms]
+    torch.cuda.synchronize()
+    us, _ = per_step_us(projs, ["fused"], steps, warmup)
+    nbytes = sum(p.bytes() for p in projs)
+    out["decode_layer_m1"] = {"fused_us": round(us, 2), "bytes": nbytes, "GBps": round(nbytes / us / 1e3, 1),
+                              "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+    for p in projs:
+        if p.slices:
+            f = pct(call_samples([p], ["fused"], 25, 2))
+            out[f"{p.g.name}_m1"] = {"slices": list(p.slices), "fused_us": f,
+                                     "GBps": round(p.bytes() / f["median_us"] / 1e3, 1)}
+    del projs
+    torch.cuda.empty_cache()
+    if prefill:
+        lay5 = config(5, segments=32, sliced=True)
+        g = lay5.gemm("gate_up")
+        log("sliced prefill gate_up ...")
+        p = Proj(g, "fp8", copies=3)
+        p.quant(0)
+        p.shrink(0)
+        gemm = pct(call_samples([p], ["gemm_lora"], 10, 2, copies=3))
+        path = pct(call_samples([p], ["quant", "shrink", "gemm_lora"], 5, 1, copies=3))
+        expand = pct(call_samples([p], ["expand"], 10, 2, copies=3))
+        out["prefill_gate_up_fp8_32seg"] = {
+            "slices": list(p.slices), "gemm_us": gemm, "path_us": path, "separate_expand_us": expand,
+            "gemm_tflops": round(p.flops() / gemm["median_us"] / 1e6, 1),
+            "gemm_frac_fp8_peak": round(p.flops() / gemm["median_us"] / 1e6 / FP8_PEAK_TFLOPS, 4),
+            "expand_ns_per_output_column": round(expand["median_us"] * 1e3 / g.N, 3)}
+        del p
+        torch.cuda.empty_cache()
     return out
 
 
@@ -547,6 +591,7 @@ def main():
     torch.cuda.empty_cache()
 
     mt = None if args.no_mt else decode_multitenant(max(20, args.steps // 2), max(4, args.warmup // 2))
+    sliced = sliced_rows(max(20, args.steps // 2), max(4, args.warmup // 2), not args.no_prefill)
 
     # ---- prefill: M = 2048, tenant segments ----
     prefill = {}
@@ -617,6 +662,7 @@ def main():
                      "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": recorded_traffic(),
                      "algorithmic_bytes": dom.bytes(), "launch_us": round(dom_us, 2)},
         "decode_multitenant_m32": mt,
+        "sliced_adapters": sliced,
         "prefill": prefill,
         "decode_72b_preft": d72,
         "cpu_baseline": cpu,

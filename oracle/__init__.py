@@ -45,6 +45,8 @@ from .linear import (  # noqa: F401
     base_fp8,
     base_fp4,
     active_rows,
+    quant_adapter_fp8,
+    adapter_values,
     shrink,
     expand,
     linear_lora,

@@ -194,34 +194,63 @@ def active_rows(idx, L, r, ranks=None, mask=None):
     return act, a, np.where(act, rk, 0)
 
 
-def shrink(x, A, idx, ranks=None, mask=None):
+def quant_adapter_fp8(m):
+    """Adapters stored in FP8 ("EpiLoRA ...", Design, "Multi-adapter
+    kernels": adapters may be stored in FP8 and dequantized in registers,
+    halving the adapter bytes): E4M3 codes with one fp32 scale per row of
+    the matrix's last axis, by the same per-row rule as the weights
+    (scale = amax / 448, code = E4M3(v / scale)).  A [L][(S)][r][K] gets one
+    scale per rank row, B [L][N][r] one per output row.  m: bf16 bits ->
+    (codes uint8 of m's shape, scales float32 of m's shape minus the last
+    axis)."""
+    m = np.asarray(m)
+    codes, sc = quant_rows_e4m3(bf16_to_f32(m.reshape(-1, m.shape[-1])))
+    return codes.reshape(m.shape), sc.reshape(m.shape[:-1])
+
+
+def adapter_values(codes, row_scale=None):
+    """An adapter matrix's values in fp64: bf16 bit patterns (row_scale
+    None), or FP8 E4M3 codes times their row's fp32 scale (the last axis is
+    the row)."""
+    if row_scale is None:
+        return bf16_to_f32(codes).astype(np.float64)
+    return e4m3_decode(codes) * np.asarray(row_scale, np.float32).astype(np.float64)[..., None]
+
+
+def shrink(x, A, idx, ranks=None, mask=None, a_scale=None):
     """z[t][j] = sum_k A[a_t][j][k] * x[t][k] over the bf16 values, for
-    active tokens and j < rank(a_t); zero elsewhere.  float64 [M][r]."""
+    active tokens and j < rank(a_t); zero elsewhere.  float64 [M][r].
+    With a_scale ([L][r]), A holds FP8 codes and row j of adapter a is
+    e4m3(A[a][j]) * a_scale[a][j]."""
     L, r, _ = A.shape
     act, a, rk = active_rows(idx, L, r, ranks, mask)
     xf = bf16_to_f32(x).astype(np.float64)
     z = np.zeros((xf.shape[0], r), dtype=np.float64)
     for t in np.nonzero(act)[0]:
-        Af = bf16_to_f32(A[a[t], : rk[t]]).astype(np.float64)
+        sc = None if a_scale is None else a_scale[a[t], : rk[t]]
+        Af = adapter_values(A[a[t], : rk[t]], sc)
         z[t, : rk[t]] = Af @ xf[t]
     return z
 
 
-def expand(z, B, idx, scale, ranks=None, mask=None, cols=None):
+def expand(z, B, idx, scale, ranks=None, mask=None, cols=None, b_scale=None):
     """lora[t][n] = s * sum_j B[a_t][n][j] * z[t][j] for active tokens,
-    zero for the others (which receive no add at all).  float64 [M][N]."""
+    zero for the others (which receive no add at all).  float64 [M][N].
+    With b_scale ([L][N]), B holds FP8 codes and row n of adapter a is
+    e4m3(B[a][n]) * b_scale[a][n]."""
     L, _, r = B.shape
     act, a, rk = active_rows(idx, L, r, ranks, mask)
     Bsel = B if cols is None else B[:, np.asarray(cols)]
+    bsel = None if b_scale is None else (b_scale if cols is None else b_scale[:, np.asarray(cols)])
     out = np.zeros((z.shape[0], Bsel.shape[1]), dtype=np.float64)
     for t in np.nonzero(act)[0]:
-        Bf = bf16_to_f32(Bsel[a[t], :, : rk[t]]).astype(np.float64)
+        Bf = adapter_values(Bsel[a[t], :, : rk[t]], None if bsel is None else bsel[a[t]])
         out[t] = float(np.float32(scale)) * (Bf @ z[t, : rk[t]])
     return out, act
 
 
 def linear_lora(x, A, B, idx, scale, *, wq=None, sw=None, wc=None, bs=None,
-                gs=None, ranks=None, mask=None, rows=None, cols=None):
+                gs=None, ranks=None, mask=None, rows=None, cols=None, sa=None, sb=None):
     """The whole layer: per-token quantisation, base GEMM, shrink and the
     epilogue.  Exactly one weight format is given (wq+sw, or wc+bs+gs).
 
@@ -229,7 +258,9 @@ def linear_lora(x, A, B, idx, scale, *, wq=None, sw=None, wc=None, bs=None,
     y (float64: base plus the adapter term on active rows, base alone on
     the others) and the active-row flags.  `rows` restricts every result
     to a sample of tokens; to sample output channels either pass `cols`, or
-    pass the weights and B of the sampled channels only."""
+    pass the weights and B of the sampled channels only.  With sa and sb
+    the adapters are stored in FP8: A and B hold E4M3 codes, sa [L][r] and
+    sb [L][N] their row scales (quant_adapter_fp8)."""
     xs = _pick(x, rows)
     xq, sx = quant_act(xs)  # per-token quantisation is row-local
     if wq is not None:
@@ -238,8 +269,8 @@ def linear_lora(x, A, B, idx, scale, *, wq=None, sw=None, wc=None, bs=None,
         base = base_fp4(xq, sx, wc, bs, gs, cols=cols)
     idx_s = _pick(np.asarray(idx), rows)
     mask_s = None if mask is None else _pick(np.asarray(mask), rows)
-    z = shrink(xs, A, idx_s, ranks, mask_s)
-    lora, act = expand(z, B, idx_s, scale, ranks, mask_s, cols=cols)
+    z = shrink(xs, A, idx_s, ranks, mask_s, a_scale=sa)
+    lora, act = expand(z, B, idx_s, scale, ranks, mask_s, cols=cols, b_scale=sb)
     y = base.copy()
     y[act] = base[act] + lora[act]
     return dict(xq=xq, sx=sx, z=z, base=base, y=y, active=act)
@@ -258,7 +289,7 @@ def slice_bounds(slice_n):
 
 
 def linear_lora_sliced(x, A, B, idx, scale, slice_n, *, wq=None, sw=None, wc=None, bs=None, gs=None,
-                       ranks=None, mask=None, rows=None, cols=None, weights_of_cols=False):
+                       ranks=None, mask=None, rows=None, cols=None, weights_of_cols=False, sa=None, sb=None):
     """A projection whose outputs are several consecutive slices, each with
     its own adapter pair: attention's query / key / value (three slices of
     unequal widths) or the MLP's gate / up (two), as in "EpiLoRA ...",
@@ -273,7 +304,9 @@ def linear_lora_sliced(x, A, B, idx, scale, slice_n, *, wq=None, sw=None, wc=Non
     B[a_t][n][j] * z_s[t][j], with z_s = shrink(x, A[:, s]).  Other rows get
     no add.  The result's z is [M][S * r], slice s in columns s*r .. s*r+r.
     `cols` samples output columns (indices into N); with weights_of_cols the
-    weights passed are already those columns' rows, in that order."""
+    weights passed are already those columns' rows, in that order.  With sa
+    ([L][S][r]) and sb ([L][N]) the adapters are stored in FP8, as in
+    linear_lora."""
     L, S, r, K = A.shape
     bounds = slice_bounds(slice_n)
     if len(bounds) != S or bounds[-1][1] != B.shape[1]:
@@ -292,12 +325,12 @@ def linear_lora_sliced(x, A, B, idx, scale, slice_n, *, wq=None, sw=None, wc=Non
     z_all = np.zeros((xs.shape[0], S * r), dtype=np.float64)
     act = None
     for s, (n0, n1) in enumerate(bounds):
-        z = shrink(xs, A[:, s], idx_s, ranks, mask_s)
+        z = shrink(xs, A[:, s], idx_s, ranks, mask_s, a_scale=None if sa is None else sa[:, s])
         z_all[:, s * r:(s + 1) * r] = z
         pos = np.nonzero((colset >= n0) & (colset < n1))[0]   # positions in the output
         if pos.size == 0:
             continue
-        lora, act = expand(z, B, idx_s, scale, ranks, mask_s, cols=colset[pos])
+        lora, act = expand(z, B, idx_s, scale, ranks, mask_s, cols=colset[pos], b_scale=sb)
         y[np.ix_(act, pos)] = base[np.ix_(act, pos)] + lora[act]
     if act is None:
         act = active_rows(idx_s, L, r, ranks, mask_s)[0]

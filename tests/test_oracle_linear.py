@@ -464,3 +464,92 @@ def test_sliced_brute_force():
                         add += Bf[idx[t], n, j] * zt
                     want = want + 2.0 * add
                 assert abs(out["y"][t][n] - want) <= 1e-12 * max(1.0, abs(want))
+
+
+# --- adapters stored in FP8 -------------------------------------------------------------
+
+def test_fp8_adapters_equal_bf16_layer_on_exact_values():
+    """Adapters whose FP8 codes times a power-of-two row scale are exact in
+    bf16: the FP8-adapter layer equals the bf16-adapter layer on those
+    values (an independently pinned path), for plain and sliced
+    projections."""
+    rng = np.random.default_rng(50)
+    M, K, N, L, r = 6, 64, 40, 3, 8
+    x, w, _, _ = make(rng, M=M, K=K, N=N, L=L, r=r)
+    wq, sw = oracle.quant_weight_fp8(w)
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    A8 = rng.choice(finite, size=(L, r, K)).astype(np.uint8)
+    B8 = rng.choice(finite, size=(L, N, r)).astype(np.uint8)
+    sa = (2.0 ** rng.integers(-12, -6, size=(L, r))).astype(np.float32)
+    sb = (2.0 ** rng.integers(-14, -8, size=(L, N))).astype(np.float32)
+    A16 = bf16_bits((t_e4m3(A8).numpy() * sa[..., None]).astype(np.float32))
+    B16 = bf16_bits((t_e4m3(B8).numpy() * sb[..., None]).astype(np.float32))
+    assert np.array_equal(t_bf16(A16).numpy(), t_e4m3(A8).numpy() * sa[..., None])  # exact
+    idx = np.array([0, 2, -1, 1, 2, 0])
+    ranks = np.array([8, 5, 3])
+    got = oracle.linear_lora(x, A8, B8, idx, 2.0, wq=wq, sw=sw, ranks=ranks, sa=sa, sb=sb)
+    ref = oracle.linear_lora(x, A16, B16, idx, 2.0, wq=wq, sw=sw, ranks=ranks)
+    assert np.allclose(got["y"], ref["y"], rtol=1e-13, atol=1e-16)
+    assert np.allclose(got["z"], ref["z"], rtol=1e-13, atol=1e-16)
+    assert np.array_equal(got["y"][2], got["base"][2])
+    # sliced: slice s of A8 with its own scales
+    A8s = rng.choice(finite, size=(L, 2, r, K)).astype(np.uint8)
+    sas = (2.0 ** rng.integers(-12, -6, size=(L, 2, r))).astype(np.float32)
+    A16s = bf16_bits((t_e4m3(A8s).numpy() * sas[..., None]).astype(np.float32))
+    got = oracle.linear_lora_sliced(x, A8s, B8, idx, 2.0, (24, 16), wq=wq, sw=sw, ranks=ranks, sa=sas, sb=sb)
+    ref = oracle.linear_lora_sliced(x, A16s, B16, idx, 2.0, (24, 16), wq=wq, sw=sw, ranks=ranks)
+    assert np.allclose(got["y"], ref["y"], rtol=1e-13, atol=1e-16)
+
+
+def test_fp8_adapter_quantizer_and_error():
+    """The stored codes are the per-row rule (each row's largest magnitude
+    lands on 448), and the FP8 adapters' term is within the E4M3 rounding of
+    the bf16 adapters' term."""
+    rng = np.random.default_rng(51)
+    x, w, A, B = make(rng, M=8, K=128, N=48, L=3, r=16)
+    wq, sw = oracle.quant_weight_fp8(w)
+    A8, sa = oracle.quant_adapter_fp8(A)
+    B8, sb = oracle.quant_adapter_fp8(B)
+    assert A8.shape == A.shape and sa.shape == A.shape[:2] and sb.shape == B.shape[:2]
+    assert np.all(np.abs(t_e4m3(A8).numpy()).max(axis=2) == 448.0)
+    assert np.allclose(sa * 448.0, np.abs(t_bf16(A).numpy()).max(axis=2), rtol=2.0 ** -23)
+    idx = np.array([0, 1, 2, 0, 1, 2, -1, 0])
+    q = oracle.linear_lora(x, A8, B8, idx, 2.0, wq=wq, sw=sw, sa=sa, sb=sb)
+    b = oracle.linear_lora(x, A, B, idx, 2.0, wq=wq, sw=sw)
+    lq, lb = q["y"] - q["base"], b["y"] - b["base"]
+    rel = np.sqrt(np.mean((lq - lb) ** 2)) / np.sqrt(np.mean(lb ** 2))
+    assert 0 < rel < 0.1          # E4M3 keeps 3 mantissa bits: a few percent
+    # doubling every B row scale doubles the term exactly
+    z = oracle.shrink(x, A8, idx, a_scale=sa)
+    t1 = oracle.expand(z, B8, idx, 2.0, b_scale=sb)[0]
+    t2 = oracle.expand(z, B8, idx, 2.0, b_scale=(sb * np.float32(2.0)).astype(np.float32))[0]
+    assert np.array_equal(t2, 2.0 * t1) and np.abs(t1).max() > 0
+    assert np.allclose(t1, lq, rtol=1e-12, atol=1e-15)
+
+
+def test_fp8_adapters_brute_force():
+    """M=2, K=4, N=8, r=2: Python loops from the definition over the FP8
+    decode of each code (torch's float8_e4m3fn) times the row scales."""
+    rng = np.random.default_rng(52)
+    x, w, A, B = make(rng, M=2, K=4, N=8, L=2, r=2)
+    wq, sw = oracle.quant_weight_fp8(w)
+    A8, sa = oracle.quant_adapter_fp8(A)
+    B8, sb = oracle.quant_adapter_fp8(B)
+    Ad, Bd = t_e4m3(A8).numpy(), t_e4m3(B8).numpy()
+    xf = t_bf16(x).numpy()
+    for i0, i1 in itertools.product([-1, 0, 1], repeat=2):
+        idx = np.array([i0, i1])
+        out = oracle.linear_lora(x, A8, B8, idx, 2.0, wq=wq, sw=sw, sa=sa, sb=sb)
+        for t in range(2):
+            for n in range(8):
+                want = out["base"][t][n]
+                a = idx[t]
+                if a >= 0:
+                    acc = 0.0
+                    for j in range(2):
+                        zt = 0.0
+                        for k in range(4):
+                            zt += Ad[a, j, k] * float(sa[a, j]) * xf[t, k]
+                        acc += Bd[a, n, j] * float(sb[a, n]) * zt
+                    want = want + 2.0 * acc
+                assert abs(out["y"][t][n] - want) <= 1e-12 * max(1.0, abs(want))
