@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libepilora.so")
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 DEV_BAD_INDEX, DEV_WAIT_TIMEOUT, DEV_INTERNAL = 1, 2, 4
 W_FP8, W_FP4 = 0, 1
+A_BF16, A_FP8 = 0, 1
 OP_SHRINK, OP_GEMM, OP_EXPAND, OP_DECODE, OP_QUANT_W4 = 1, 2, 3, 4, 5
 DECODE_MAX_M = 64
 MAX_RANK = 128
@@ -47,6 +48,7 @@ class LayerArgs(ctypes.Structure):
         ("xq_out", ctypes.c_void_p), ("sx_out", ctypes.c_void_p), ("ldq_out", ctypes.c_int64),
         ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
         ("nslices", ctypes.c_int32), ("slice_n", ctypes.c_int64 * 4),
+        ("afmt", ctypes.c_int32), ("sa", ctypes.c_void_p), ("sb", ctypes.c_void_p),
     ]
 
 
@@ -65,10 +67,10 @@ SIGNATURES = {
     "epilora_quant_weight_fp8": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
     "epilora_quant_weight_fp4": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
     "epilora_lora_shrink": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
-    "epilora_lora_shrink_sliced": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _I32, _I32, _I32, _P, _P, _P, _P, _P,
-                                                  _SZ, _P]),
-    "epilora_lora_expand_add_sliced": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _I32, _I32, _P, _P, _P, _P, _F,
-                                                      _P, _I64, _P, _SZ, _P]),
+    "epilora_lora_shrink_ex": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _I32, _P, _I32, _I32, _I32, _P, _P, _P, _P,
+                                              _P, _SZ, _P]),
+    "epilora_lora_expand_add_ex": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _P, _I32, _I32, _I32, _P, _P, _P, _P,
+                                                  _F, _P, _I64, _P, _SZ, _P]),
     "epilora_gemm_lora": (ctypes.c_int, [ctypes.POINTER(LayerArgs), _P]),
     "epilora_lora_expand_add": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _I32, _P, _P, _P, _F, _P, _I64, _P, _SZ, _P]),
     "epilora_decode_lora": (ctypes.c_int, [ctypes.POINTER(LayerArgs), _P]),
@@ -175,17 +177,19 @@ def epilora_quant_weight_fp4(w, wc, bs, gs, ws, stream=None):
 
 # --- adapters ------------------------------------------------------------------------
 
-def epilora_lora_shrink(x, A, idx, z, ws, ranks=None, mask=None, stream=None):
+def epilora_lora_shrink(x, A, idx, z, ws, ranks=None, mask=None, sa=None, stream=None):
     """x: bf16 [M][K]; A: bf16 [L][r][K], or [L][S][r][K] for per-slice
-    adapters (then z is [M][S r]); idx: int32 [M]; z: fp32 [M][r]."""
-    _need(x, torch.bfloat16, "x"); _need(A, torch.bfloat16, "A"); _need(idx, torch.int32, "idx")
+    adapters (then z is [M][S r]); uint8 E4M3 codes with row scales sa
+    ([L][r] or [L][S][r]) for FP8-stored adapters; idx: int32 [M]; z: fp32."""
+    _need(x, torch.bfloat16, "x"); _need(idx, torch.int32, "idx")
     _need(z, torch.float32, "z"); _need(ranks, torch.int32, "ranks"); _need(mask, torch.uint8, "mask")
+    _need(A, torch.uint8 if sa is not None else torch.bfloat16, "A"); _need(sa, torch.float32, "sa")
     M, K = x.shape
-    if A.dim() == 4:
-        L, S, r, _ = A.shape
-        _check("epilora_lora_shrink_sliced", lib().epilora_lora_shrink_sliced(
-            _ptr(x), M, K, _ld(x), _ptr(A), L, S, r, _ptr(ranks), _ptr(idx), _ptr(mask), _ptr(z),
-            _ptr(ws), ws.numel(), _stream(stream)))
+    if A.dim() == 4 or sa is not None:
+        L, S, r = (A.shape[0], A.shape[1], A.shape[2]) if A.dim() == 4 else (A.shape[0], 1, A.shape[1])
+        _check("epilora_lora_shrink_ex", lib().epilora_lora_shrink_ex(
+            _ptr(x), M, K, _ld(x), _ptr(A), A_FP8 if sa is not None else A_BF16, _ptr(sa), L, S, r, _ptr(ranks),
+            _ptr(idx), _ptr(mask), _ptr(z), _ptr(ws), ws.numel(), _stream(stream)))
         return
     L, r, _ = A.shape
     _check("epilora_lora_shrink", lib().epilora_lora_shrink(
@@ -200,17 +204,19 @@ def _slice_array(slices):
     return arr
 
 
-def epilora_lora_expand_add(z, B, idx, scale, y, ws, ranks=None, mask=None, slices=None, stream=None):
+def epilora_lora_expand_add(z, B, idx, scale, y, ws, ranks=None, mask=None, slices=None, sb=None, stream=None):
     """y[t] += s * B[idx[t]] z[t] (bf16, in place) for active tokens;
-    `slices`: output slice widths of a projection with per-slice adapters."""
-    _need(z, torch.float32, "z"); _need(B, torch.bfloat16, "B"); _need(idx, torch.int32, "idx")
-    _need(y, torch.bfloat16, "y")
+    `slices`: output slice widths of a projection with per-slice adapters;
+    sb: row scales of an FP8-stored B (uint8 codes)."""
+    _need(z, torch.float32, "z"); _need(idx, torch.int32, "idx"); _need(y, torch.bfloat16, "y")
+    _need(B, torch.uint8 if sb is not None else torch.bfloat16, "B"); _need(sb, torch.float32, "sb")
     M, N = y.shape
     L, _, r = B.shape
-    if slices:
-        _check("epilora_lora_expand_add_sliced", lib().epilora_lora_expand_add_sliced(
-            _ptr(z), M, N, _ptr(B), L, r, len(slices), _slice_array(slices), _ptr(ranks), _ptr(idx), _ptr(mask),
-            float(scale), _ptr(y), _ld(y), _ptr(ws), ws.numel(), _stream(stream)))
+    if slices or sb is not None:
+        _check("epilora_lora_expand_add_ex", lib().epilora_lora_expand_add_ex(
+            _ptr(z), M, N, _ptr(B), A_FP8 if sb is not None else A_BF16, _ptr(sb), L, r,
+            len(slices) if slices else 1, _slice_array(slices) if slices else None, _ptr(ranks), _ptr(idx),
+            _ptr(mask), float(scale), _ptr(y), _ld(y), _ptr(ws), ws.numel(), _stream(stream)))
         return
     _check("epilora_lora_expand_add", lib().epilora_lora_expand_add(
         _ptr(z), M, N, _ptr(B), L, r, _ptr(ranks), _ptr(idx), _ptr(mask), float(scale), _ptr(y), _ld(y),
@@ -227,9 +233,14 @@ def _weights(a, w, sw=None, bs=None, gs=None):
         a.wfmt, a.w, a.bs, a.gs = W_FP4, _ptr(w), _ptr(bs), _ptr(gs)
 
 
-def _adapters(a, A, B, idx, ranks, mask, scale, slices=None):
-    _need(A, torch.bfloat16, "A"); _need(B, torch.bfloat16, "B"); _need(idx, torch.int32, "idx")
+def _adapters(a, A, B, idx, ranks, mask, scale, slices=None, sa=None, sb=None):
+    fp8 = sa is not None or sb is not None
+    ad_t = torch.uint8 if fp8 else torch.bfloat16
+    _need(A, ad_t, "A"); _need(B, ad_t, "B"); _need(idx, torch.int32, "idx")
     _need(ranks, torch.int32, "ranks"); _need(mask, torch.uint8, "mask")
+    _need(sa, torch.float32, "sa"); _need(sb, torch.float32, "sb")
+    if fp8:
+        a.afmt, a.sa, a.sb = A_FP8, _ptr(sa), _ptr(sb)
     if B is not None:
         a.L, a.r = B.shape[0], B.shape[2]
     elif A is not None:
@@ -242,7 +253,7 @@ def _adapters(a, A, B, idx, ranks, mask, scale, slices=None):
 
 
 def epilora_gemm_lora(xq, sx, w, y, *, sw=None, bs=None, gs=None, z=None, B=None, idx=None, ranks=None,
-                      mask=None, scale=1.0, ws=None, slices=None, stream=None):
+                      mask=None, scale=1.0, ws=None, slices=None, sb=None, stream=None):
     """y = bf16(dequant(w . xq) [+ s B[idx] z on active rows]); z=None: base
     only; `slices`: output slice widths (per-slice adapters, z [M][S r])."""
     _need(xq, torch.uint8, "xq"); _need(sx, torch.float32, "sx"); _need(y, torch.bfloat16, "y")
@@ -252,7 +263,7 @@ def epilora_gemm_lora(xq, sx, w, y, *, sw=None, bs=None, gs=None, z=None, B=None
     a.N = y.shape[1]
     a.xq, a.sx, a.ldq = _ptr(xq), _ptr(sx), _ld(xq)
     _weights(a, w, sw, bs, gs)
-    _adapters(a, None, B, idx, ranks, mask, scale, slices)
+    _adapters(a, None, B, idx, ranks, mask, scale, slices, None, sb)
     a.z = _ptr(z)
     a.y, a.ldy = _ptr(y), _ld(y)
     if ws is not None:
@@ -261,22 +272,25 @@ def epilora_gemm_lora(xq, sx, w, y, *, sw=None, bs=None, gs=None, z=None, B=None
 
 
 def epilora_decode_lora_noalloc(x, w, y, *, sw=None, bs=None, gs=None, A=None, B=None, idx=None, ranks=None,
-                                mask=None, scale=1.0, xq_out=None, sx_out=None, slices=None, stream=None):
+                                mask=None, scale=1.0, xq_out=None, sx_out=None, slices=None, sa=None, sb=None,
+                                stream=None):
     """The fused decode path on the library's fixed per-GPU scratch (no
     workspace argument; see the header)."""
-    a = _decode_args(x, w, y, sw, bs, gs, A, B, idx, ranks, mask, scale, None, xq_out, sx_out, slices)
+    a = _decode_args(x, w, y, sw, bs, gs, A, B, idx, ranks, mask, scale, None, xq_out, sx_out, slices, sa, sb)
     _check("epilora_decode_lora_noalloc", lib().epilora_decode_lora_noalloc(ctypes.byref(a), _stream(stream)))
 
 
 def epilora_decode_lora(x, w, y, *, sw=None, bs=None, gs=None, A=None, B=None, idx=None, ranks=None, mask=None,
-                        scale=1.0, ws=None, xq_out=None, sx_out=None, slices=None, stream=None):
+                        scale=1.0, ws=None, xq_out=None, sx_out=None, slices=None, sa=None, sb=None, stream=None):
     """The fused decode path: quantization, shrink and GEMM in one launch;
-    `slices`: output slice widths (per-slice adapters, A [L][S][r][K])."""
-    a = _decode_args(x, w, y, sw, bs, gs, A, B, idx, ranks, mask, scale, ws, xq_out, sx_out, slices)
+    `slices`: output slice widths (per-slice adapters, A [L][S][r][K]);
+    sa, sb: row scales of FP8-stored adapters (A, B uint8 codes)."""
+    a = _decode_args(x, w, y, sw, bs, gs, A, B, idx, ranks, mask, scale, ws, xq_out, sx_out, slices, sa, sb)
     _check("epilora_decode_lora", lib().epilora_decode_lora(ctypes.byref(a), _stream(stream)))
 
 
-def _decode_args(x, w, y, sw, bs, gs, A, B, idx, ranks, mask, scale, ws, xq_out, sx_out, slices=None):
+def _decode_args(x, w, y, sw, bs, gs, A, B, idx, ranks, mask, scale, ws, xq_out, sx_out, slices=None, sa=None,
+                 sb=None):
     _need(x, torch.bfloat16, "x"); _need(y, torch.bfloat16, "y")
     _need(xq_out, torch.uint8, "xq_out"); _need(sx_out, torch.float32, "sx_out")
     a = LayerArgs()
@@ -284,7 +298,7 @@ def _decode_args(x, w, y, sw, bs, gs, A, B, idx, ranks, mask, scale, ws, xq_out,
     a.N = y.shape[1]
     a.x, a.ldx = _ptr(x), _ld(x)
     _weights(a, w, sw, bs, gs)
-    _adapters(a, A, B, idx, ranks, mask, scale, slices)
+    _adapters(a, A, B, idx, ranks, mask, scale, slices, sa, sb)
     a.y, a.ldy = _ptr(y), _ld(y)
     a.xq_out, a.sx_out = _ptr(xq_out), _ptr(sx_out)
     a.ldq_out = 0 if xq_out is None else _ld(xq_out)

@@ -101,7 +101,19 @@ AdapterArgs adapters_of(const epilora_layer_args* a, bool on) {
   d.L = a->L; d.r = a->r; d.scale = a->scale;
   if (!on) { d.r = 16; d.L = 0; }
   set_slices(d, on ? a->nslices : 1, a->slice_n);
+  d.afmt = on ? a->afmt : EPILORA_A_BF16;
+  d.sa = a->sa; d.sb = a->sb;
   return d;
+}
+
+// Adapter storage: bf16, or FP8 codes with row scales (sa for A where A is
+// read, sb for B where B is read; 16-byte aligned).
+int check_afmt(int32_t afmt, const float* sa, bool need_sa, const float* sb, bool need_sb) {
+  if (afmt == EPILORA_A_BF16) return EPILORA_OK;
+  if (afmt != EPILORA_A_FP8) return EPILORA_ERR_INVALID_ARG;
+  if ((need_sa && sa == nullptr) || (need_sb && sb == nullptr)) return EPILORA_ERR_INVALID_ARG;
+  if ((sa && !aligned(sa, 16)) || (sb && !aligned(sb, 16))) return EPILORA_ERR_UNSUPPORTED;
+  return EPILORA_OK;
 }
 
 int32_t slices_of(const epilora_layer_args* a) { return a->nslices > 1 ? a->nslices : 1; }
@@ -127,6 +139,8 @@ int check_decode(const epilora_layer_args* a, int32_t& r) {
     st = check_adapters(a->L, a->r, a->A, true, a->B, true, a->ranks, a->idx);
     if (st != EPILORA_OK) return st;
     st = check_slices(a->nslices, a->slice_n, a->N, 16);
+    if (st != EPILORA_OK) return st;
+    st = check_afmt(a->afmt, a->sa, true, a->sb, true);
     if (st != EPILORA_OK) return st;
     r = a->r;
   }
@@ -240,14 +254,17 @@ int epilora_quant_weight_fp4(const uint16_t* w, int64_t N, int64_t K, uint8_t* w
   return hip_status(launch_quant_weight_fp4(w, N, K, wc, bs, gs, ws, as_stream(stream)));
 }
 
-int epilora_lora_shrink_sliced(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* A, int32_t L,
-                               int32_t nslices, int32_t r, const int32_t* ranks, const int32_t* idx,
-                               const uint8_t* mask, float* z, void* ws, size_t ws_bytes, void* stream) {
+int epilora_lora_shrink_ex(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const void* A, int32_t afmt,
+                           const float* sa, int32_t L, int32_t nslices, int32_t r, const int32_t* ranks,
+                           const int32_t* idx, const uint8_t* mask, float* z, void* ws, size_t ws_bytes,
+                           void* stream) {
   if (M < 0 || K < 0) return EPILORA_ERR_INVALID_ARG;
   if (nslices < 1 || nslices > kMaxSlices) return EPILORA_ERR_INVALID_ARG;
+  int st = check_afmt(afmt, sa, true, nullptr, false);
+  if (st != EPILORA_OK) return st;
   if (M == 0) return EPILORA_OK;
   if (x == nullptr || z == nullptr) return EPILORA_ERR_INVALID_ARG;
-  int st = check_adapters(L, r, A, true, nullptr, false, ranks, idx);
+  st = check_adapters(L, r, A, true, nullptr, false, ranks, idx);
   if (st != EPILORA_OK) return st;
   if (ldx < K) return EPILORA_ERR_INVALID_ARG;
   if (K % 16 != 0 || ldx % 16 != 0 || !aligned(x, 16) || !aligned(z, 16)) return EPILORA_ERR_UNSUPPORTED;
@@ -255,17 +272,19 @@ int epilora_lora_shrink_sliced(const uint16_t* x, int64_t M, int64_t K, int64_t 
   st = check_ws(ws, ws_bytes, shrink_ws(kStateBytes, M, K, r, nslices).total);
   if (st != EPILORA_OK) return st;
   AdapterArgs ad;
-  ad.A = A; ad.B = nullptr; ad.ranks = ranks; ad.idx = idx; ad.mask = mask;
+  ad.A = reinterpret_cast<const uint16_t*>(A); ad.B = nullptr; ad.ranks = ranks; ad.idx = idx; ad.mask = mask;
   ad.L = L; ad.r = r; ad.scale = 1.0f;
   ad.S = nslices; ad.zld = nslices * r;
   for (int i = 0; i < kMaxSlices; ++i) ad.slice_end[i] = INT64_MAX;
+  ad.afmt = afmt; ad.sa = sa; ad.sb = nullptr;
   return hip_status(launch_shrink(x, M, K, ldx, ad, z, ws, as_stream(stream)));
 }
 
 int epilora_lora_shrink(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* A, int32_t L,
                         int32_t r, const int32_t* ranks, const int32_t* idx, const uint8_t* mask, float* z,
                         void* ws, size_t ws_bytes, void* stream) {
-  return epilora_lora_shrink_sliced(x, M, K, ldx, A, L, 1, r, ranks, idx, mask, z, ws, ws_bytes, stream);
+  return epilora_lora_shrink_ex(x, M, K, ldx, A, EPILORA_A_BF16, nullptr, L, 1, r, ranks, idx, mask, z, ws, ws_bytes,
+                                stream);
 }
 
 int epilora_gemm_lora(const epilora_layer_args* a, void* stream) {
@@ -282,6 +301,8 @@ int epilora_gemm_lora(const epilora_layer_args* a, void* stream) {
   if (lora) {
     st = check_adapters(a->L, a->r, a->A, false, a->B, true, a->ranks, a->idx);
     if (st != EPILORA_OK) return st;
+    st = check_afmt(a->afmt, a->sa, false, a->sb, true);
+    if (st != EPILORA_OK) return st;
     // output tiles stay inside one slice: 16 rows (M <= 64), 128 (prefill)
     st = check_slices(a->nslices, a->slice_n, a->N, a->M <= EPILORA_DECODE_MAX_M ? 16 : 128);
     if (st != EPILORA_OK) return st;
@@ -293,12 +314,14 @@ int epilora_gemm_lora(const epilora_layer_args* a, void* stream) {
                                      a->z, a->y, a->ldy, a->ws, as_stream(stream)));
 }
 
-int epilora_lora_expand_add_sliced(const float* z, int64_t M, int64_t N, const uint16_t* B, int32_t L, int32_t r,
-                                   int32_t nslices, const int64_t* slice_n, const int32_t* ranks,
-                                   const int32_t* idx, const uint8_t* mask, float scale, uint16_t* y, int64_t ldy,
-                                   void* ws, size_t ws_bytes, void* stream) {
+int epilora_lora_expand_add_ex(const float* z, int64_t M, int64_t N, const void* B, int32_t afmt, const float* sb,
+                               int32_t L, int32_t r, int32_t nslices, const int64_t* slice_n, const int32_t* ranks,
+                               const int32_t* idx, const uint8_t* mask, float scale, uint16_t* y, int64_t ldy,
+                               void* ws, size_t ws_bytes, void* stream) {
   if (M < 0 || N < 0) return EPILORA_ERR_INVALID_ARG;
   int st = check_slices(nslices, slice_n, N, 1);
+  if (st != EPILORA_OK) return st;
+  st = check_afmt(afmt, nullptr, false, sb, true);
   if (st != EPILORA_OK) return st;
   if (M == 0 || N == 0) return EPILORA_OK;
   if (z == nullptr || y == nullptr) return EPILORA_ERR_INVALID_ARG;
@@ -309,17 +332,18 @@ int epilora_lora_expand_add_sliced(const float* z, int64_t M, int64_t N, const u
   st = check_ws(ws, ws_bytes, kCtrlBytes);
   if (st != EPILORA_OK) return st;
   AdapterArgs ad;
-  ad.A = nullptr; ad.B = B; ad.ranks = ranks; ad.idx = idx; ad.mask = mask;
+  ad.A = nullptr; ad.B = reinterpret_cast<const uint16_t*>(B); ad.ranks = ranks; ad.idx = idx; ad.mask = mask;
   ad.L = L; ad.r = r; ad.scale = scale;
   set_slices(ad, nslices, slice_n);
+  ad.afmt = afmt; ad.sa = nullptr; ad.sb = sb;
   return hip_status(launch_expand_add(z, M, N, ad, y, ldy, ws, as_stream(stream)));
 }
 
 int epilora_lora_expand_add(const float* z, int64_t M, int64_t N, const uint16_t* B, int32_t L, int32_t r,
                             const int32_t* ranks, const int32_t* idx, const uint8_t* mask, float scale, uint16_t* y,
                             int64_t ldy, void* ws, size_t ws_bytes, void* stream) {
-  return epilora_lora_expand_add_sliced(z, M, N, B, L, r, 1, nullptr, ranks, idx, mask, scale, y, ldy, ws, ws_bytes,
-                                        stream);
+  return epilora_lora_expand_add_ex(z, M, N, B, EPILORA_A_BF16, nullptr, L, r, 1, nullptr, ranks, idx, mask, scale, y,
+                                    ldy, ws, ws_bytes, stream);
 }
 
 int epilora_decode_lora(const epilora_layer_args* a, void* stream) {

@@ -63,6 +63,22 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
   return __uint_as_float(s | ((e + 120u) << 23) | (m << 20));
 }
 
+// Two E4M3 codes (bytes 0, 1 of w, or 2, 3 with HI) -> two bf16 in one dword,
+// the lower byte in the low half.  The hardware conversion to fp32 is exact
+// and every E4M3 value has at most 4 significant bits, so the upper half of
+// each fp32 is the exact bf16.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  typedef float f32x2_t __attribute__((ext_vector_type(2)));
+  const f32x2_t f = __builtin_amdgcn_cvt_pk_f32_fp8((int)w, HI);
+  return (__float_as_uint(f.x) >> 16) | (__float_as_uint(f.y) & 0xFFFF0000u);
+}
+// Eight E4M3 codes (element order in lo, then hi) -> eight bf16.
+__device__ __forceinline__ uint4 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  return make_uint4(fp8x2_to_bf16x2<false>(lo), fp8x2_to_bf16x2<true>(lo), fp8x2_to_bf16x2<false>(hi),
+                    fp8x2_to_bf16x2<true>(hi));
+}
+
 // E2M1 magnitude code (0..7) -> fp32.
 __device__ __forceinline__ float e2m1_magnitude(uint32_t c) {
   const uint32_t e = (c >> 1) & 3u, m = c & 1u;

@@ -263,6 +263,7 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(BM
   // (128 ranks), 16-byte chunks swizzled by (token % 16).
   if (p.z != nullptr) {
     const int r = p.ad.r;
+    const bool af8 = p.ad.afmt != 0;
     // The tile's outputs lie inside one output slice (the host requires
     // slice widths that are multiples of the tile width): its z columns.
     const int zsl = slice_of(p.ad, n0);
@@ -356,13 +357,17 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(BM
     auto b_dma = [&](int u, int slot) {
       const TokenSlot lead = tok[groups[u / NPASS]];
       const int pb = (u % NPASS) * PB;
-      const auto rBa = make_rsrc(p.ad.B + (int64_t)lead.a * p.N * r, (uint32_t)(p.N * r * 2));
+      // bf16 rows: 16-byte chunk c holds ranks 8c .. 8c+7; FP8 rows: chunk c
+      // holds ranks 16c .. 16c+15 (only the first r / 16 chunks are used).
+      const int esz = af8 ? 1 : 2, per_chunk = 16 / esz;
+      const auto rBa = make_rsrc(reinterpret_cast<const uint8_t*>(p.ad.B) + (int64_t)lead.a * p.N * r * esz,
+                                 (uint32_t)(p.N * r * esz));
 #pragma unroll
       for (int q = 0; q < 8; ++q) {
         const int j = wave * 8 + q;  // 4 rows of 256 bytes per wave instruction
         const int R = 4 * j + (lane >> 4), c = (lane & 15) ^ (R & 15);
         const int64_t n = n0 + (R >> 6) * WN + pb * 16 + (R & 63);
-        const uint32_t off = 8 * c < lead.rank ? (uint32_t)((n * r + 8 * c) * 2) : kOutOfRange;
+        const uint32_t off = per_chunk * c < lead.rank ? (uint32_t)((n * r + per_chunk * c) * esz) : kOutOfRange;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rBa, (__attribute__((address_space(3))) void*)(buf1 + slot * 32768 + j * 1024), 16, off, 0, 0, 0);
       }
@@ -385,7 +390,7 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(BM
       const int a = lead.a, rank = lead.rank;
       const int nch = (rank + 31) / 32;  // 32-rank chunks
       uint8_t* slot = buf1 + (NSLOT == 2 ? (u & 1) : 0) * 32768;
-      if (rank & 7) {  // clear the ranks past the adapter's rank in its partial chunk
+      if (!af8 && (rank & 7)) {  // clear the ranks past the adapter's rank in its partial chunk
         const int cp = rank >> 3;
         for (int R = tid; R < 128; R += kWideThreads) {
           uint16_t* q = reinterpret_cast<uint16_t*>(slot + R * 256 + ((cp ^ (R & 15)) << 4));
@@ -393,14 +398,34 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(BM
         }
         __syncthreads();
       }
+      if (af8 && (rank & 15)) {
+        const int cp = rank >> 4;
+        for (int R = tid; R < 128; R += kWideThreads) {
+          uint8_t* q = slot + R * 256 + ((cp ^ (R & 15)) << 4);
+          for (int e = rank & 15; e < 16; ++e) q[e] = 0;
+        }
+        __syncthreads();
+      }
       uint4 bfr[PB][4];
+      float sbv[PB];  // FP8 adapters: the row scale of this lane's output in each block
 #pragma unroll
       for (int i = 0; i < PB; ++i) {
         const int R = wn * 64 + i * 16 + (lane & 15);
+        const int64_t n = n0 + wn * WN + (pb + i) * 16 + (lane & 15);
+        sbv[i] = (af8 && n < p.N) ? p.ad.sb[(int64_t)a * p.N + n] : 1.0f;
 #pragma unroll
-        for (int kc = 0; kc < 4; ++kc)
-          bfr[i][kc] = kc < nch ? *reinterpret_cast<const uint4*>(slot + R * 256 + (((kc * 4 + (lane >> 4)) ^ (R & 15)) << 4))
-                                : zero4();
+        for (int kc = 0; kc < 4; ++kc) {
+          if (kc >= nch) {
+            bfr[i][kc] = zero4();
+          } else if (af8) {  // ranks 32 kc + 8 (l / 16) .. + 8: half of a 16-byte chunk, widened
+            const int g = lane >> 4;
+            const uint2 q = *reinterpret_cast<const uint2*>(slot + R * 256 + (((kc * 2 + (g >> 1)) ^ (R & 15)) << 4) +
+                                                            8 * (g & 1));
+            bfr[i][kc] = fp8x8_to_bf16x8(q.x, q.y);
+          } else {
+            bfr[i][kc] = *reinterpret_cast<const uint4*>(slot + R * 256 + (((kc * 4 + (lane >> 4)) ^ (R & 15)) << 4));
+          }
+        }
       }
       if (u + 1 < units) {
         if (NSLOT == 1) __syncthreads();  // every wave has read the slot
@@ -438,7 +463,8 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(BM
           const int tr = wm * WM + tb * 16 + 4 * (lane >> 4) + v;
           if (tok[tr].a == a) {
 #pragma unroll
-            for (int i = 0; i < PB; ++i) acc[tb][pb + i][v] = acc[tb][pb + i][v] + p.ad.scale * lacc[i][v];
+            for (int i = 0; i < PB; ++i)
+              acc[tb][pb + i][v] = acc[tb][pb + i][v] + p.ad.scale * (af8 ? lacc[i][v] * sbv[i] : lacc[i][v]);
           }
         }
       }

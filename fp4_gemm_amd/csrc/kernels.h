@@ -15,9 +15,12 @@ constexpr int kMaxSlices = 4;
 // down-projections side by side ([L][S][r][K]), B the rows of each slice's
 // up-projection in place ([L][N][r]), z the slices' results side by side
 // ([M][S r]).  S = 1 is the plain layer.
+// Adapters are bf16, or stored in FP8 (afmt 1): then A and B hold E4M3 codes
+// (one byte per element, the same shapes) and each row carries one fp32
+// scale, sa [L][S][r] for A's rank rows and sb [L][N] for B's output rows.
 struct AdapterArgs {
-  const uint16_t* A;     // [L][S][r][K]
-  const uint16_t* B;     // [L][N][r]
+  const uint16_t* A;     // [L][S][r][K] (bf16, or E4M3 bytes when afmt == 1)
+  const uint16_t* B;     // [L][N][r]    (bf16, or E4M3 bytes when afmt == 1)
   const int32_t* ranks;  // [L] or null (one rank for every slice of an adapter)
   const int32_t* idx;    // [M] or null (no adapters)
   const uint8_t* mask;   // [M] or null
@@ -26,6 +29,12 @@ struct AdapterArgs {
   int32_t S;                     // slices, 1..kMaxSlices
   int32_t zld;                   // z row stride: S * r
   int64_t slice_end[kMaxSlices]; // end (exclusive) of each slice's outputs
+  int32_t afmt;                  // 0: bf16 adapters; 1: FP8 adapters with row scales
+  const float* sa;               // [L][S][r] (afmt 1)
+  const float* sb;               // [L][N]    (afmt 1)
+
+  __host__ __device__ const uint8_t* A8() const { return reinterpret_cast<const uint8_t*>(A); }
+  __host__ __device__ const uint8_t* B8() const { return reinterpret_cast<const uint8_t*>(B); }
 };
 
 // The slice output n falls in.

@@ -53,13 +53,21 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_wide_kernel(ShrinkParam
 
   // Staging: 128 rows x 16 chunks = 2048 16-byte chunks, 8 per thread.
   uint4 stg[8];
-  auto a_load = [&](const uint16_t* Aa, int rank, int s) {
+  // FP8 adapters: 8 codes per chunk, widened to bf16 exactly on the way.
+  const bool af8 = p.ad.afmt != 0;
+  auto a_load = [&](int64_t aoff, int rank, int s) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int e = tid + i * kShrinkThreads;
       const int row = e >> 4, c = e & 15;
       const int64_t k = (int64_t)s * kShrinkStep + 8 * c;
-      stg[i] = (row < rank && k < K) ? ld16(Aa + (int64_t)row * K + k) : make_uint4(0, 0, 0, 0);
+      const bool ok = row < rank && k < K;
+      if (af8) {
+        const uint2 q = ok ? *reinterpret_cast<const uint2*>(p.ad.A8() + aoff + (int64_t)row * K + k) : make_uint2(0, 0);
+        stg[i] = fp8x8_to_bf16x8(q.x, q.y);
+      } else {
+        stg[i] = ok ? ld16(p.ad.A + aoff + (int64_t)row * K + k) : make_uint4(0, 0, 0, 0);
+      }
     }
   };
   auto a_store = [&]() {
@@ -80,7 +88,7 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_wide_kernel(ShrinkParam
     const int jbn = (rank + 15) >> 4;
     const bool mine = ((members >> (16 * wave)) & 0xFFFFull) != 0;
     const bool member = (members >> (16 * wave + col)) & 1;
-    const uint16_t* Aa = p.ad.A + ((int64_t)a * p.ad.S + slice) * r * K;
+    const int64_t Aa = ((int64_t)a * p.ad.S + slice) * r * K;  // element offset of the slot
     const uint16_t* xr = p.x + (t0 + 16 * wave + col) * p.ldx;
     if (s_begin < s_end) a_load(Aa, rank, s_begin);
     for (int s = s_begin; s < s_end; ++s) {
@@ -155,12 +163,19 @@ __global__ __launch_bounds__(256) void expand_add_kernel(const float* __restrict
   const int64_t n = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (n >= N) return;
   const int r = ad.r;
-  const uint16_t* br = ad.B + ((int64_t)a * N + n) * r;
+  const int64_t boff = ((int64_t)a * N + n) * r;  // elements
+  const uint16_t* br = ad.B + boff;
   const float* zr = z + t * ad.zld + slice_of(ad, n) * r;
   float acc = 0.f;
   int j = 0;
   for (; j + 8 <= rank; j += 8) {
-    const uint4 b = ld16(br + j);
+    uint4 b;
+    if (ad.afmt != 0) {
+      const uint2 q = *reinterpret_cast<const uint2*>(ad.B8() + boff + j);
+      b = fp8x8_to_bf16x8(q.x, q.y);
+    } else {
+      b = ld16(br + j);
+    }
     const uint32_t w[4] = {b.x, b.y, b.z, b.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -168,7 +183,9 @@ __global__ __launch_bounds__(256) void expand_add_kernel(const float* __restrict
       acc = fmaf(bf16_hi(w[i]), zr[j + 2 * i + 1], acc);
     }
   }
-  for (; j < rank; ++j) acc = fmaf(bf16_to_f32(br[j]), zr[j], acc);
+  for (; j < rank; ++j)
+    acc = fmaf(ad.afmt != 0 ? e4m3_decode(ad.B8()[boff + j]) : bf16_to_f32(br[j]), zr[j], acc);
+  if (ad.afmt != 0) acc *= ad.sb[(int64_t)a * N + n];  // FP8 adapters: the row scale, once
   uint16_t* yp = y + t * ldy + n;
   *yp = (uint16_t)f32_to_bf16(bf16_to_f32(*yp) + ad.scale * acc);
 }

@@ -79,7 +79,9 @@ __device__ __forceinline__ uint64_t shrink_tile(const ShrinkParams& p, int64_t t
     pending &= ~members;
     const bool member = (members >> col) & 1;
     const int jbn = (rank + 15) >> 4;
-    const uint16_t* Aa = p.ad.A + ((int64_t)a * p.ad.S + slice) * r * K;
+    const int64_t aoff = ((int64_t)a * p.ad.S + slice) * r * K;  // elements
+    const uint16_t* Aa = p.ad.A + aoff;
+    const uint8_t* Aa8 = p.ad.A8() + aoff;
     const uint16_t* xr = p.x + (t0 + col) * p.ldx;
     for (int s = s_begin + ws; s < s_end; s += WS) {
       const int64_t k = (int64_t)s * kShrinkStep + grp * 32;
@@ -92,11 +94,21 @@ __device__ __forceinline__ uint64_t shrink_tile(const ShrinkParams& p, int64_t t
         if (jb < jbn && jb % WJ == wj) {
           const int j = jb * 16 + col;
           const bool rowok = j < rank;
-          const uint16_t* ar = Aa + (int64_t)j * K + k;
           uint4 av[4];
+          if (p.ad.afmt != 0) {  // FP8 codes: 32 bytes, widened to bf16 exactly
+            const uint8_t* ar8 = Aa8 + (int64_t)j * K + k;
+            const uint4 q0 = (rowok && k < K) ? ld16(ar8) : make_uint4(0, 0, 0, 0);
+            const uint4 q1 = (rowok && k + 16 < K) ? ld16(ar8 + 16) : make_uint4(0, 0, 0, 0);
+            av[0] = fp8x8_to_bf16x8(q0.x, q0.y);
+            av[1] = fp8x8_to_bf16x8(q0.z, q0.w);
+            av[2] = fp8x8_to_bf16x8(q1.x, q1.y);
+            av[3] = fp8x8_to_bf16x8(q1.z, q1.w);
+          } else {
+            const uint16_t* ar = Aa + (int64_t)j * K + k;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            av[i] = (rowok && k + i * 8 < K) ? ld16(ar + i * 8) : make_uint4(0, 0, 0, 0);
+            for (int i = 0; i < 4; ++i)
+              av[i] = (rowok && k + i * 8 < K) ? ld16(ar + i * 8) : make_uint4(0, 0, 0, 0);
+          }
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[jb] = mfma_bf16_16x16x32(as_bf16x8(av[i]), as_bf16x8(xv[i]), acc[jb]);
         }
@@ -233,10 +245,24 @@ __device__ __forceinline__ bool shrink_finish(const ShrinkParams& p, int tile, i
   auto zoff = [&](int e) { return (uint32_t)(((e / r) * zld + e % r) * 4); };  // e: a word of the tile, row-major
   const uint32_t f = p.zflip;
   auto keep = [&](int e) { return f == 0u || ((active >> (e / r)) & 1ull) != 0; };
+  // FP8 adapters: the sums are of the codes, z_j = sa[a][slice][j] * sum
+  // (the row scale applied once, to the finished sum).
+  auto scaled = [&](int e, float4 v) {
+    if (p.ad.afmt == 0) return v;
+    int rk;
+    const int a = resolve_token(t0 + e / r, p.M, p.ad, nullptr, false, rk);
+    if (a < 0) return v;
+    const float4 sc = *reinterpret_cast<const float4*>(p.ad.sa + ((int64_t)a * p.ad.S + slice) * r + e % r);
+    return make_float4(v.x * sc.x, v.y * sc.y, v.z * sc.z, v.w * sc.w);
+  };
+  auto word = [&](const float4& v) {
+    return make_uint4(__float_as_uint(v.x) ^ f, __float_as_uint(v.y) ^ f, __float_as_uint(v.z) ^ f,
+                      __float_as_uint(v.w) ^ f);
+  };
   if (p.splits == 1) {
     for (int e = 4 * threadIdx.x; e < rows * r; e += 4 * NW * kWave) {
-      const uint4 v = *reinterpret_cast<const uint4*>(&red[e]);
-      if (keep(e)) buf_store16<kCoherent>(zr, zoff(e), make_uint4(v.x ^ f, v.y ^ f, v.z ^ f, v.w ^ f));
+      const float4 v = *reinterpret_cast<const float4*>(&red[e]);
+      if (keep(e)) buf_store16<kCoherent>(zr, zoff(e), word(scaled(e, v)));
     }
     wait_all_memory();
     __syncthreads();
@@ -249,9 +275,7 @@ __device__ __forceinline__ bool shrink_finish(const ShrinkParams& p, int tile, i
   if (!last) return false;
   // `red` is free again and holds the chunk sums.
   combine_partials<NW * kWave>(slice_partials(p, slice), p.splits, p.M, t0, rows, r, red, [&](int q, const float4& v) {
-    if (keep(4 * q))
-      buf_store16<kCoherent>(zr, zoff(4 * q), make_uint4(__float_as_uint(v.x) ^ f, __float_as_uint(v.y) ^ f,
-                                                         __float_as_uint(v.z) ^ f, __float_as_uint(v.w) ^ f));
+    if (keep(4 * q)) buf_store16<kCoherent>(zr, zoff(4 * q), word(scaled(4 * q, v)));
   });
   if (threadIdx.x == 0) store_relaxed(counter, 0);
   wait_all_memory();

@@ -444,11 +444,22 @@ struct Skinny {
     const int ch = r >> 4;
     const int j0 = jl * ch;
     if (j0 >= ts.rank) return v;
-    const uint16_t* src = p.ad.B + ((int64_t)ts.a * p.N + n) * r + j0;
-    if (ch == 8) v = *reinterpret_cast<const uint4*>(src);
-    else if (ch == 4) { const uint2 w = *reinterpret_cast<const uint2*>(src); v.x = w.x; v.y = w.y; }
-    else if (ch == 2) v.x = *reinterpret_cast<const uint32_t*>(src);
-    else v.x = *src;
+    const int64_t off = ((int64_t)ts.a * p.N + n) * r + j0;  // elements
+    if (p.ad.afmt != 0) {  // FP8 codes, widened to bf16 exactly
+      const uint8_t* src = p.ad.B8() + off;
+      uint32_t lo = 0, hi = 0;
+      if (ch == 8) { const uint2 w = *reinterpret_cast<const uint2*>(src); lo = w.x; hi = w.y; }
+      else if (ch == 4) lo = *reinterpret_cast<const uint32_t*>(src);
+      else if (ch == 2) lo = *reinterpret_cast<const uint16_t*>(src);
+      else lo = *src;
+      v = fp8x8_to_bf16x8(lo, hi);
+    } else {
+      const uint16_t* src = p.ad.B + off;
+      if (ch == 8) v = *reinterpret_cast<const uint4*>(src);
+      else if (ch == 4) { const uint2 w = *reinterpret_cast<const uint2*>(src); v.x = w.x; v.y = w.y; }
+      else if (ch == 2) v.x = *reinterpret_cast<const uint32_t*>(src);
+      else v.x = *src;
+    }
     if (j0 + ch > ts.rank) {  // clear the elements past the rank
       uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
@@ -494,6 +505,7 @@ struct Skinny {
       l += __shfl_xor(l, 1, 16);
       if (jl == 0 && n < p.N) {
         float y = (base[o] * sxs[t]) * (have_pre ? pws : weight_scale<FMT>(p.wt, n));
+        if (lora && p.ad.afmt != 0) l *= p.ad.sb[(int64_t)tok[t].a * p.N + n];  // FP8 adapters: the row scale
         if (lora) y = y + p.ad.scale * l;
         p.y[(int64_t)t * p.ldy + n] = (uint16_t)f32_to_bf16(y);
       }

@@ -84,6 +84,21 @@ enum epilora_wfmt {
                         16 consecutive elements along K; gs: one fp32 */
 };
 
+/* Adapter storage ("EpiLoRA ...", Design, "Multi-adapter kernels": adapters
+ * may be stored in FP8 and dequantized in registers, halving the adapter
+ * bytes the kernels read; "The vLLM plugin", Memory: low-precision adapters
+ * in smaller slots). */
+enum epilora_afmt {
+  EPILORA_A_BF16 = 0, /* A and B hold bf16 values */
+  EPILORA_A_FP8 = 1   /* A and B hold E4M3 codes of the same shapes (one byte
+                         per element), each row with one fp32 scale: sa
+                         [L][nslices][r] for A's rank rows, sb [L][N] for B's
+                         output rows; a row's values are e4m3(code) * scale
+                         (epilora_quant_weight_fp8 applied to the rows makes
+                         them).  z_j = sa_j * sum_k e4m3(A_jk) x_k and the
+                         output adds s * sb_n * sum_j e4m3(B_nj) z_j. */
+};
+
 /* Operations, for epilora_workspace_bytes. */
 enum epilora_op {
   EPILORA_OP_SHRINK = 1,
@@ -151,6 +166,12 @@ typedef struct epilora_layer_args {
      EPILORA_ERR_UNSUPPORTED. */
   int32_t nslices;
   int64_t slice_n[4];
+  /* Adapter storage (enum epilora_afmt) and, for EPILORA_A_FP8, the row
+     scales (16-byte aligned): sa [L][nslices][r] (read where A is), sb
+     [L][N] (read where B is). */
+  int32_t afmt;
+  const float* sa;
+  const float* sb;
 } epilora_layer_args;
 
 /* Library version (EPILORA_VERSION of the build). */
@@ -229,19 +250,21 @@ int epilora_lora_shrink(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                         const uint8_t* mask, float* z, void* ws,
                         size_t ws_bytes, void* stream);
 
-/* The shrink of a projection with per-slice adapters (see
- * epilora_layer_args.nslices): A is [L][nslices][r][K], z is
- * [M][nslices * r]; slice s's z_s[t] = A[idx[t]][s] x[t] goes to columns
- * s*r .. s*r+r, under the same activity rule, rank and determinism as
- * epilora_lora_shrink (which is this call with nslices = 1).  nslices in
- * 1..4; cdiv(M, 16) * nslices <= 4096.  Needs a workspace of
- * EPILORA_OP_SHRINK with r = nslices * r. */
-int epilora_lora_shrink_sliced(const uint16_t* x, int64_t M, int64_t K,
-                               int64_t ldx, const uint16_t* A, int32_t L,
-                               int32_t nslices, int32_t r,
-                               const int32_t* ranks, const int32_t* idx,
-                               const uint8_t* mask, float* z, void* ws,
-                               size_t ws_bytes, void* stream);
+/* The shrink with every adapter option: per-slice adapters (see
+ * epilora_layer_args.nslices: A is [L][nslices][r][K], z is
+ * [M][nslices * r], slice s's z_s[t] = A[idx[t]][s] x[t] in columns
+ * s*r .. s*r+r) and FP8-stored adapters (afmt EPILORA_A_FP8: A holds E4M3
+ * codes, sa [L][nslices][r] their row scales, z = sa * sum of code times x).
+ * Same activity rule, rank and determinism as epilora_lora_shrink, which is
+ * this call with afmt EPILORA_A_BF16 and nslices 1.  nslices in 1..4;
+ * cdiv(M, 16) * nslices <= 4096.  Needs a workspace of EPILORA_OP_SHRINK
+ * with r = nslices * r. */
+int epilora_lora_shrink_ex(const uint16_t* x, int64_t M, int64_t K,
+                           int64_t ldx, const void* A, int32_t afmt,
+                           const float* sa, int32_t L, int32_t nslices,
+                           int32_t r, const int32_t* ranks,
+                           const int32_t* idx, const uint8_t* mask, float* z,
+                           void* ws, size_t ws_bytes, void* stream);
 
 /* The low-precision GEMM with the multi-adapter epilogue
  * ("Multi-adapter kernels", K2; "Kernel details", one output tile of K2).
@@ -269,16 +292,17 @@ int epilora_lora_expand_add(const float* z, int64_t M, int64_t N,
                             int64_t ldy, void* ws, size_t ws_bytes,
                             void* stream);
 
-/* The separate up-projection of a projection with per-slice adapters: z is
- * [M][nslices * r] and output n of slice s uses z_s (slice widths slice_n,
- * a host array of nslices entries summing to N). */
-int epilora_lora_expand_add_sliced(const float* z, int64_t M, int64_t N,
-                                   const uint16_t* B, int32_t L, int32_t r,
-                                   int32_t nslices, const int64_t* slice_n,
-                                   const int32_t* ranks, const int32_t* idx,
-                                   const uint8_t* mask, float scale,
-                                   uint16_t* y, int64_t ldy, void* ws,
-                                   size_t ws_bytes, void* stream);
+/* The separate up-projection with every adapter option: per-slice adapters
+ * (z [M][nslices * r]; output n of slice s uses z_s; slice widths slice_n,
+ * a host array of nslices entries summing to N, or NULL with nslices <= 1)
+ * and FP8-stored B (afmt EPILORA_A_FP8, row scales sb [L][N]). */
+int epilora_lora_expand_add_ex(const float* z, int64_t M, int64_t N,
+                               const void* B, int32_t afmt, const float* sb,
+                               int32_t L, int32_t r, int32_t nslices,
+                               const int64_t* slice_n, const int32_t* ranks,
+                               const int32_t* idx, const uint8_t* mask,
+                               float scale, uint16_t* y, int64_t ldy,
+                               void* ws, size_t ws_bytes, void* stream);
 
 /* The fused small-batch (decode) path ("Multi-adapter kernels", The decode
  * path): quantization, shrink and the GEMM with its epilogue in ONE launch.

@@ -54,9 +54,9 @@ class DeviceGemm:
     """One projection's inputs on the device, weights quantized by the
     library's own load-time quantizer."""
 
-    def __init__(self, g, wfmt="fp8", x=None):
+    def __init__(self, g, wfmt="fp8", x=None, afmt="bf16"):
         lay = g.layer
-        self.g, self.wfmt = g, wfmt
+        self.g, self.wfmt, self.afmt = g, wfmt, afmt
         self.M, self.K, self.N = g.M, g.K, g.N
         self.x_np = g.x() if x is None else x
         self.w_np = g.w()
@@ -81,6 +81,20 @@ class DeviceGemm:
         self.B_np = g.B()
         self.A = to_dev(self.A_np)
         self.B = to_dev(self.B_np)
+        self.akw, self.bkw, self.adkw = {}, {}, {}
+        if afmt == "fp8":
+            # adapters stored in FP8: the library's per-row quantizer on the
+            # rows of A (length K) and of B (length r)
+            A8 = torch.empty(self.A.shape, dtype=torch.uint8, device=DEV)
+            B8 = torch.empty(self.B.shape, dtype=torch.uint8, device=DEV)
+            self.sa = torch.empty(self.A.shape[:-1], dtype=torch.float32, device=DEV)
+            self.sb = torch.empty(self.B.shape[:-1], dtype=torch.float32, device=DEV)
+            ep.epilora_quant_weight_fp8(self.A.reshape(-1, self.K), A8.view(-1, self.K), self.sa.view(-1))
+            ep.epilora_quant_weight_fp8(self.B.reshape(-1, self.B.shape[-1]), B8.view(-1, self.B.shape[-1]),
+                                        self.sb.view(-1))
+            self.A, self.B = A8, B8
+            self.akw, self.bkw = dict(sa=self.sa), dict(sb=self.sb)
+            self.adkw = dict(sa=self.sa, sb=self.sb)
         self.idx = to_dev(lay.idx.astype(np.int32))
         self.mask = None if lay.mask is None else to_dev(lay.mask.astype(np.uint8))
         self.ranks = None if lay.ranks is None else to_dev(lay.ranks.astype(np.int32))
@@ -97,7 +111,7 @@ class DeviceGemm:
     def shrink(self, ws=None):
         ws = ws if ws is not None else ep.new_workspace(ep.OP_SHRINK, self.M, self.N, self.K, self.r * self.S)
         z = torch.empty(self.M, self.r * self.S, dtype=torch.float32, device=DEV)
-        ep.epilora_lora_shrink(self.x, self.A, self.idx, z, ws, ranks=self.ranks, mask=self.mask)
+        ep.epilora_lora_shrink(self.x, self.A, self.idx, z, ws, ranks=self.ranks, mask=self.mask, **self.akw)
         return z, ws
 
     def gemm(self, xq, sx, z=None, ws=None):
@@ -107,7 +121,8 @@ class DeviceGemm:
         else:
             ws = ws if ws is not None else ep.new_workspace(ep.OP_GEMM, self.M, self.N, self.K, self.r)
             ep.epilora_gemm_lora(xq, sx, self.wq, y, z=z, B=self.B, idx=self.idx, ranks=self.ranks,
-                                 mask=self.mask, scale=self.scale, ws=ws, slices=self.slices, **self.wkw)
+                                 mask=self.mask, scale=self.scale, ws=ws, slices=self.slices, **self.bkw,
+                                 **self.wkw)
         return y
 
     def separate(self):
@@ -123,7 +138,7 @@ class DeviceGemm:
         sx = torch.empty(self.M, dtype=torch.float32, device=DEV) if keep_xq else None
         ep.epilora_decode_lora(self.x, self.wq, y, A=self.A, B=self.B, idx=self.idx, ranks=self.ranks,
                                mask=self.mask, scale=self.scale, ws=ws, xq_out=xq, sx_out=sx,
-                               slices=self.slices, **self.wkw)
+                               slices=self.slices, **self.adkw, **self.wkw)
         return dict(xq=xq, sx=sx, y=y, ws=ws)
 
     # -- the oracle on the same inputs ----------------------------------------
@@ -139,12 +154,22 @@ class DeviceGemm:
         else:
             wc, bs, gs = oracle.quant_weight_fp4(self.w_np, rows=cols)
             wkw = dict(wc=wc, bs=bs, gs=gs)
+        A_or, B_full, akw = self.A_np, self.B_np, {}
+        if self.afmt == "fp8":
+            A_or, sa = oracle.quant_adapter_fp8(self.A_np)
+            B_full, sb = oracle.quant_adapter_fp8(self.B_np)
+            assert np.array_equal(to_np(self.A), A_or) and np.array_equal(to_np(self.sa), sa), "adapter codes"
+            assert np.array_equal(to_np(self.B), B_full) and np.array_equal(to_np(self.sb), sb), "adapter codes"
+            akw = dict(sa=sa, sb=sb)
         if self.slices:
-            out = oracle.linear_lora_sliced(self.x_np, self.A_np, self.B_np, lay.idx, lay.scale, self.slices,
+            out = oracle.linear_lora_sliced(self.x_np, A_or, B_full, lay.idx, lay.scale, self.slices,
                                             ranks=lay.ranks, mask=lay.mask, rows=rows, cols=cols,
-                                            weights_of_cols=cols is not None, **wkw)
+                                            weights_of_cols=cols is not None, **akw, **wkw)
         else:
-            out = oracle.linear_lora(self.x_np, self.A_np, B, lay.idx, lay.scale, ranks=lay.ranks,
-                                     mask=lay.mask, rows=rows, **wkw)
+            Bsel = B_full if cols is None else B_full[:, np.asarray(cols)]
+            if "sb" in akw and cols is not None:
+                akw["sb"] = akw["sb"][:, np.asarray(cols)]
+            out = oracle.linear_lora(self.x_np, A_or, Bsel, lay.idx, lay.scale, ranks=lay.ranks,
+                                     mask=lay.mask, rows=rows, **akw, **wkw)
         out["w"] = wkw
         return out

@@ -49,7 +49,7 @@ def test_version_and_strerror(L):
 def test_layer_args_layout_matches_header():
     # 3 sizes, x+ldx, xq+sx+ldq, wfmt(+pad), 4 weight ptrs, L+r, 6 ptrs, scale(+pad),
     # y+ldy, xq_out+sx_out+ldq_out, ws+ws_bytes
-    assert ctypes.sizeof(ep.LayerArgs) == 8 * 3 + 16 + 24 + 8 + 32 + 8 + 48 + 8 + 16 + 24 + 16 + 8 + 32
+    assert ctypes.sizeof(ep.LayerArgs) == 8 * 3 + 16 + 24 + 8 + 32 + 8 + 48 + 8 + 16 + 24 + 16 + 8 + 32 + 24
     assert ep.LayerArgs.slice_n.offset == 8 * 3 + 16 + 24 + 8 + 32 + 8 + 48 + 8 + 16 + 24 + 16 + 8
     assert ep.LayerArgs.scale.offset == 8 * 3 + 16 + 24 + 8 + 32 + 8 + 48
 
@@ -153,12 +153,27 @@ def test_slice_validation(L):
     d = lambda **kw: L.epilora_decode_lora(ctypes.byref(_layer(**kw)), None)
     assert d(nslices=3, slice_n=_sl(256, 128, 112)) == ep.ERR_INVALID_ARG
     assert d(nslices=3, slice_n=_sl(256, 136, 120)) == ep.ERR_UNSUPPORTED
-    sh = L.epilora_lora_shrink_sliced
-    assert sh(P, 4, 256, 256, P, 4, 0, 16, None, P, None, P, P, 1 << 20, None) == ep.ERR_INVALID_ARG
-    assert sh(P, 4, 256, 256, P, 4, 5, 16, None, P, None, P, P, 1 << 20, None) == ep.ERR_INVALID_ARG
-    assert sh(P, 65536, 256, 256, P, 4, 3, 16, None, P, None, P, P, 1 << 40, None) == ep.ERR_UNSUPPORTED
-    e = L.epilora_lora_expand_add_sliced
-    assert e(P, 4, 512, P, 4, 16, 2, _sl(500, 10), None, P, None, 2.0, P2, 512, P, 256, None) == ep.ERR_INVALID_ARG
+    sh = L.epilora_lora_shrink_ex
+    assert sh(P, 4, 256, 256, P, 0, None, 4, 0, 16, None, P, None, P, P, 1 << 20, None) == ep.ERR_INVALID_ARG
+    assert sh(P, 4, 256, 256, P, 0, None, 4, 5, 16, None, P, None, P, P, 1 << 20, None) == ep.ERR_INVALID_ARG
+    assert sh(P, 65536, 256, 256, P, 0, None, 4, 3, 16, None, P, None, P, P, 1 << 40, None) == ep.ERR_UNSUPPORTED
+    e = L.epilora_lora_expand_add_ex
+    assert e(P, 4, 512, P, 0, None, 4, 16, 2, _sl(500, 10), None, P, None, 2.0, P2, 512, P, 256,
+             None) == ep.ERR_INVALID_ARG
+
+
+def test_fp8_adapter_validation(L):
+    g = lambda **kw: L.epilora_gemm_lora(ctypes.byref(_layer(z=P, **kw)), None)
+    assert g(afmt=2) == ep.ERR_INVALID_ARG
+    assert g(afmt=ep.A_FP8) == ep.ERR_INVALID_ARG                  # no B row scales
+    assert g(afmt=ep.A_FP8, sb=P + 4) == ep.ERR_UNSUPPORTED        # scales not 16-byte aligned
+    d = lambda **kw: L.epilora_decode_lora(ctypes.byref(_layer(**kw)), None)
+    assert d(afmt=ep.A_FP8, sb=P) == ep.ERR_INVALID_ARG            # no A row scales
+    sh = L.epilora_lora_shrink_ex
+    assert sh(P, 4, 256, 256, P, ep.A_FP8, None, 4, 1, 16, None, P, None, P, P, 1 << 20, None) == ep.ERR_INVALID_ARG
+    e = L.epilora_lora_expand_add_ex
+    assert e(P, 4, 512, P, ep.A_FP8, None, 4, 16, 1, None, None, P, None, 2.0, P2, 512, P, 256,
+             None) == ep.ERR_INVALID_ARG
     # the workspace need grows with the slices
     w1 = L.epilora_workspace_bytes(ep.OP_DECODE, 8, 6144, 4096, 64)
     w3 = L.epilora_workspace_bytes(ep.OP_DECODE, 8, 6144, 4096, 3 * 64)

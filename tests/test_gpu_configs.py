@@ -162,3 +162,22 @@ def test_config5_sliced_gate_up(wfmt):
     starts = np.flatnonzero(np.r_[True, lay.idx[1:] != lay.idx[:-1]])
     rows = np.unique(np.concatenate([sample(d.M, 64, 55), starts]))
     check(d, out, rows=rows, seed=56, what=f"cfg5 sliced gate_up {wfmt}")
+
+
+@pytest.mark.parametrize("name", ["qkv", "gate_up", "down"])
+def test_config3_fp8_adapters(name):
+    # the many-distinct-adapters decode batch with adapters stored in FP8
+    say(f"config 3 FP8 adapters {name}")
+    d = DeviceGemm(config(3).gemm(name), afmt="fp8")
+    fused = d.decode()
+    check(d, fused, seed=34, what=f"cfg3 fp8 adapters {name}")
+
+
+def test_config5_fp8_adapters():
+    say("config 5 FP8 adapters gate_up 32 segments")
+    lay = config(5, segments=32)
+    d = DeviceGemm(lay.gemm("gate_up"), afmt="fp8")
+    out = d.separate()
+    starts = np.flatnonzero(np.r_[True, lay.idx[1:] != lay.idx[:-1]])
+    rows = np.unique(np.concatenate([sample(d.M, 64, 57), starts]))
+    check(d, out, rows=rows, seed=58, what="cfg5 fp8 adapters gate_up")

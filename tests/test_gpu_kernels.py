@@ -451,3 +451,48 @@ def test_sliced_vs_oracle(M, K, slices, L, r, kind, use_mask, use_ranks, wfmt):
     bound = 2.0 ** -8 * (np.abs(ref["base"]) + np.abs(ref["y"])) * 1.001 + 1e-4 * rms
     assert np.all(np.abs(yg - ref["y"]) <= bound)
     assert ep.epilora_device_error(sep["ws"]) == 0
+
+
+# --- adapters stored in FP8 (E4M3 codes, one fp32 scale per row) --------------------------
+
+FP8_ADAPTER_CASES = [
+    # M, K, N, slices, L, r, idx kind, mask, ranks, wfmt
+    (1, 4096, 2048, None, 1, 64, "zero", False, False, "fp8"),
+    (7, 512, 384, None, 4, 16, "mixed", True, True, "fp8"),
+    (32, 1024, 512, (256, 128, 128), 40, 32, "distinct", False, True, "fp8"),
+    (64, 512, 256, None, 9, 128, "mixed", True, False, "fp4"),
+    (300, 512, 640, (384, 256), 6, 64, "sorted", True, True, "fp8"),
+    (1100, 256, 6144, None, 4, 128, "sorted", False, True, "fp8"),
+    (150, 1024, 300, None, 5, 48, "mixed", False, True, "fp4"),
+]
+
+
+@pytest.mark.parametrize("M,K,N,slices,L,r,kind,use_mask,use_ranks,wfmt", FP8_ADAPTER_CASES)
+def test_fp8_adapters_vs_oracle(M, K, N, slices, L, r, kind, use_mask, use_ranks, wfmt):
+    say(f"fp8 adapters M={M} K={K} N={N} slices={slices} L={L} r={r} {kind} {wfmt}")
+    rng = np.random.default_rng(9000 + M + K + N)
+    idx = _idx(kind, M, L, rng)
+    mask = rng.integers(0, 2, M).astype(np.uint8) if use_mask else None
+    ranks = rng.choice([0, 16, r // 2, r, 13], size=L).astype(np.int32) if use_ranks else None
+    lay = custom_layer("a8", 900 + M + N, M, K, N, L, r, idx, mask=mask, ranks=ranks, wfmt=wfmt, slices=slices)
+    d = DeviceGemm(lay.gemms[0], wfmt, afmt="fp8")
+    sep = d.separate()
+    ref = d.oracle()   # also checks the library's adapter codes and scales bit for bit
+    zg = to_np(sep["z"]).astype(np.float64)
+    scale = max(np.sqrt(np.mean(ref["z"] ** 2)), 1e-30)
+    assert np.abs(zg - ref["z"]).max() <= 1e-4 * scale
+    compare(to_np(sep["y"]), ref["y"], f"fp8 adapters M={M}")
+    base = to_np(d.gemm(sep["xq"], sep["sx"]))
+    assert np.array_equal(to_np(sep["y"])[~ref["active"]], base[~ref["active"]])
+    if M <= ep.DECODE_MAX_M:
+        fused = d.decode()
+        assert torch.equal(fused["y"], sep["y"])
+        assert ep.epilora_device_error(fused["ws"]) == 0
+    y = d.gemm(sep["xq"], sep["sx"])
+    ep.epilora_lora_expand_add(sep["z"], d.B, d.idx, d.scale, y, sep["ws"], ranks=d.ranks, mask=d.mask,
+                               slices=slices, sb=d.sb)
+    yg = bf16_np_to_f64(to_np(y))
+    rms = np.sqrt(np.mean(ref["y"] ** 2))
+    bound = 2.0 ** -8 * (np.abs(ref["base"]) + np.abs(ref["y"])) * 1.001 + 1e-4 * rms
+    assert np.all(np.abs(yg - ref["y"]) <= bound)
+    assert ep.epilora_device_error(sep["ws"]) == 0
