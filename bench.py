@@ -60,11 +60,13 @@ def dev(a):
 
 
 class Proj:
-    """One projection on the device: ROTATE copies of weights and adapters."""
+    """One projection on the device: ROTATE copies of weights and adapters
+    (afmt "fp8": adapters stored as E4M3 codes with row scales)."""
 
-    def __init__(self, g, wfmt="fp8", copies=ROTATE):
+    def __init__(self, g, wfmt="fp8", copies=ROTATE, afmt="bf16"):
         lay = g.layer
         self.g, self.M, self.K, self.N, self.r = g, g.M, g.K, g.N, lay.r
+        self.afmt = afmt
         self.slices = g.slices
         self.S = len(g.slices) if g.slices else 1
         self.wfmt = wfmt
@@ -85,6 +87,15 @@ class Proj:
                                                    for _ in range(copies - 1)]
         del w
         A, B = dev(g.A_sliced() if self.slices else g.A()), dev(g.B())
+        self.sa = self.sb = None
+        if afmt == "fp8":
+            A8 = torch.empty(A.shape, dtype=torch.uint8, device=DEV)
+            B8 = torch.empty(B.shape, dtype=torch.uint8, device=DEV)
+            self.sa = torch.empty(A.shape[:-1], dtype=torch.float32, device=DEV)
+            self.sb = torch.empty(B.shape[:-1], dtype=torch.float32, device=DEV)
+            ep.epilora_quant_weight_fp8(A.reshape(-1, A.shape[-1]), A8.view(-1, A.shape[-1]), self.sa.view(-1))
+            ep.epilora_quant_weight_fp8(B.reshape(-1, B.shape[-1]), B8.view(-1, B.shape[-1]), self.sb.view(-1))
+            A, B = A8, B8
         self.A = [A] + [A.clone() for _ in range(copies - 1)]
         self.B = [B] + [B.clone() for _ in range(copies - 1)]
         self.idx = dev(lay.idx.astype(np.int32))
@@ -120,14 +131,17 @@ class Proj:
 
     def adapters(self, c):
         c %= self.copies
-        return dict(B=self.B[c], idx=self.idx, ranks=self.ranks, mask=self.mask, scale=self.scale,
-                    slices=self.slices)
+        kw = dict(B=self.B[c], idx=self.idx, ranks=self.ranks, mask=self.mask, scale=self.scale,
+                  slices=self.slices)
+        if self.sb is not None:
+            kw["sb"] = self.sb
+        return kw
 
     # paths ------------------------------------------------------------------
     def fused(self, c):
         w, kw = self.w[c % self.copies]
         ep.epilora_decode_lora(self.x, w, self.y, A=self.A[c % self.copies], ws=self.ws_dec, xq_out=self.xq,
-                               sx_out=self.sx, **self.adapters(c), **kw)
+                               sx_out=self.sx, sa=self.sa, **self.adapters(c), **kw)
 
     def fused_base(self, c):
         w, kw = self.w[c % self.copies]
@@ -138,7 +152,7 @@ class Proj:
 
     def shrink(self, c):
         ep.epilora_lora_shrink(self.x, self.A[c % self.copies], self.idx, self.z, self.ws_shr, ranks=self.ranks,
-                               mask=self.mask)
+                               mask=self.mask, sa=self.sa)
 
     def gemm_lora(self, c):
         w, kw = self.w[c % self.copies]
@@ -150,7 +164,7 @@ class Proj:
 
     def expand(self, c):
         ep.epilora_lora_expand_add(self.z, self.B[c % self.copies], self.idx, self.scale, self.y, self.ws_shr,
-                                   ranks=self.ranks, mask=self.mask, slices=self.slices)
+                                   ranks=self.ranks, mask=self.mask, slices=self.slices, sb=self.sb)
 
     # algorithmic counts -------------------------------------------------------
     def adapter_ranks(self):
@@ -167,7 +181,9 @@ class Proj:
             wb = self.K * self.N + 4 * self.N
         else:
             wb = self.K * self.N // 2 + self.K * self.N // 16 + 4
-        ab = sum(2 * rk(a) * (self.S * self.K + self.N) for a in distinct)
+        esz = 1 if self.afmt == "fp8" else 2  # FP8 adapters: a byte per element plus a scale per row
+        ab = sum(esz * rk(a) * (self.S * self.K + self.N) + (4 * (self.S * rk(a) + self.N) if esz == 1 else 0)
+                 for a in distinct)
         return wb + ab + 2 * self.M * self.K + 2 * self.M * self.N
 
     def flops(self):
@@ -304,21 +320,22 @@ def decode_72b(steps, warmup):
     return out
 
 
-def decode_multitenant(steps, warmup):
+def decode_multitenant(steps, warmup, afmt="bf16"):
     """The 32-token multi-tenant decode layer on Llama-8B shapes: 64 resident
     rank-64 adapters, 32 distinct tenants of which 4 tokens carry none, so 28
     distinct adapters are read (each A and B once); fused path, two rotated
     copies of weights and adapters (2 x 468 MB, more than the Infinity
     Cache)."""
     layer = config(3)
-    log("multi-tenant decode layer M=32 ...")
-    projs = [Proj(g, copies=2) for g in layer.gemms]
+    log(f"multi-tenant decode layer M=32 ({afmt} adapters) ...")
+    projs = [Proj(g, copies=2, afmt=afmt) for g in layer.gemms]
     torch.cuda.synchronize()
     us, _ = per_step_us(projs, ["fused"], steps, warmup)
     base_us, _ = per_step_us(projs, ["fused_base"], steps, warmup)
     nbytes = sum(p.bytes() for p in projs)
     wbytes = sum(p.K * p.N + 4 * p.N for p in projs)
-    out = {"fused_us": round(us, 2), "base_only_us": round(base_us, 2), "bytes": nbytes, "weight_bytes": wbytes,
+    out = {"adapters": afmt, "fused_us": round(us, 2), "base_only_us": round(base_us, 2), "bytes": nbytes,
+           "weight_bytes": wbytes,
            "GBps": round(nbytes / us / 1e3, 1), "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4),
            "distinct_tenants": len(projs[0].adapter_ranks()[1]),
            "per_projection_us": {p.g.name: round(float(np.mean(call_samples([p], ["fused"], 20, 2, copies=2))), 2)
@@ -590,7 +607,10 @@ def main():
     del projs
     torch.cuda.empty_cache()
 
-    mt = None if args.no_mt else decode_multitenant(max(20, args.steps // 2), max(4, args.warmup // 2))
+    mt = None
+    if not args.no_mt:
+        mt = decode_multitenant(max(20, args.steps // 2), max(4, args.warmup // 2))
+        mt["fp8_adapters"] = decode_multitenant(max(20, args.steps // 2), max(4, args.warmup // 2), afmt="fp8")
     sliced = sliced_rows(max(20, args.steps // 2), max(4, args.warmup // 2), not args.no_prefill)
 
     # ---- prefill: M = 2048, tenant segments ----
@@ -615,6 +635,18 @@ def main():
                     "gemm_frac_fp8_peak": round(p.flops() / g_us / 1e6 / FP8_PEAK_TFLOPS, 4)}
                 del p
                 torch.cuda.empty_cache()
+        g = config(5, segments=32).gemm("gate_up")
+        log("prefill fp8 32 segments gate_up, FP8 adapters ...")
+        p = Proj(g, "fp8", copies=3, afmt="fp8")
+        p.quant(0)
+        p.shrink(0)
+        gemm = pct(call_samples([p], ["gemm_lora"], 10, 2, copies=3))
+        path = pct(call_samples([p], ["quant", "shrink", "gemm_lora"], 5, 1, copies=3))
+        prefill["gate_up_fp8_32seg_fp8_adapters"] = {
+            "gemm_us": gemm, "path_us": path, "gemm_tflops": round(p.flops() / gemm["median_us"] / 1e6, 1),
+            "gemm_frac_fp8_peak": round(p.flops() / gemm["median_us"] / 1e6 / FP8_PEAK_TFLOPS, 4)}
+        del p
+        torch.cuda.empty_cache()
 
     d72 = None
     if not args.no_72b:

@@ -52,4 +52,6 @@ from .linear import (  # noqa: F401
     linear_lora,
     slice_bounds,
     linear_lora_sliced,
+    rmsnorm,
+    norm_quant_shrink,
 )

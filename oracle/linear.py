@@ -35,6 +35,7 @@ import numpy as np
 from .formats import (
     FOLD_SHIFT,
     bf16_to_f32,
+    f32_to_bf16,
     e2m1_decode_table,
     e2m1_encode,
     e4m3_decode,
@@ -335,3 +336,47 @@ def linear_lora_sliced(x, A, B, idx, scale, slice_n, *, wq=None, sw=None, wc=Non
     if act is None:
         act = active_rows(idx_s, L, r, ranks, mask_s)[0]
     return dict(xq=xq, sx=sx, z=z_all, base=base, y=y, active=act)
+
+
+# ---------------------------------------------------------------------------
+# The normalization in front of qkv and gate_up, with the quantizer and the
+# shrink fused into it
+# ---------------------------------------------------------------------------
+
+
+def rmsnorm(x, gamma, eps):
+    """RMS normalization of each token row, as the normalization kernel in
+    front of the query / key / value and gate / up projections computes it
+    ("EpiLoRA ...", appendix "Discussion and Limitations": the down-projection
+    can be computed inside the normalization kernel that already reads the
+    input).  The pages do not spell the normalization out; this is the
+    common decoder form: ms = mean_k x_k^2 (the sum of the exact squares in
+    fp64, the mean rounded to fp32), inv = fp32(1 / fp32(sqrt(fp32(ms + eps))))
+    with correctly rounded fp32 operations, then h_k = bf16(fp32(x_k * inv))
+    and xn_k = bf16(fp32(h_k * gamma_k)).  x, gamma: bf16 bits ([M][K],
+    [K]) -> xn bf16 bits [M][K]."""
+    xf = bf16_to_f32(x)
+    ss = np.sum(xf.astype(np.float64) ** 2, axis=1)
+    ms = (ss / xf.shape[1]).astype(np.float32)
+    v = (ms + np.float32(eps)).astype(np.float32)
+    inv = (np.float32(1.0) / np.sqrt(v).astype(np.float32)).astype(np.float32)
+    h = f32_to_bf16((xf * inv[:, None]).astype(np.float32))
+    return f32_to_bf16((bf16_to_f32(h) * bf16_to_f32(gamma)[None, :]).astype(np.float32))
+
+
+def norm_quant_shrink(x, gamma, eps, A=None, idx=None, *, ranks=None, mask=None, sa=None):
+    """The normalization with the per-token FP8 quantizer and the shrink
+    taken from its output: xn = rmsnorm(x); (xq, sx) = quant_act(xn);
+    z = shrink(xn, A) (A [L][r][K], or [L][S][r][K] per slice, giving z
+    [M][S r]; FP8-stored when sa is given).  Returns dict(xn, xq, sx, z)."""
+    xn = rmsnorm(x, gamma, eps)
+    xq, sx = quant_act(xn)
+    out = dict(xn=xn, xq=xq, sx=sx, z=None)
+    if A is not None:
+        if A.ndim == 3:
+            out["z"] = shrink(xn, A, idx, ranks, mask, a_scale=sa)
+        else:
+            out["z"] = np.concatenate([shrink(xn, A[:, s], idx, ranks, mask,
+                                              a_scale=None if sa is None else sa[:, s])
+                                       for s in range(A.shape[1])], axis=1)
+    return out

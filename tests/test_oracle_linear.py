@@ -553,3 +553,66 @@ def test_fp8_adapters_brute_force():
                         acc += Bd[a, n, j] * float(sb[a, n]) * zt
                     want = want + 2.0 * acc
                 assert abs(out["y"][t][n] - want) <= 1e-12 * max(1.0, abs(want))
+
+
+# --- the normalization with the quantizer and shrink fused in ------------------------------
+
+def test_rmsnorm_exact_cases():
+    """A constant row c = +-2^k with eps = 0 normalizes to +-1 exactly, so
+    xn = +-gamma bit for bit; scaling a row by a power of two (eps = 0)
+    leaves xn unchanged bit for bit."""
+    rng = np.random.default_rng(60)
+    K = 96
+    gamma = rand_bf16(rng, (K,), 1.0)
+    rows = np.array([[2.0 ** k * sgn] * K for k, sgn in ((-3, 1.0), (0, -1.0), (5, 1.0))], np.float32)
+    xn = oracle.rmsnorm(bf16_bits(rows), gamma, 0.0)
+    for i, sgn in enumerate((1.0, -1.0, 1.0)):
+        want = bf16_bits((t_bf16(gamma).numpy() * sgn).astype(np.float32))
+        assert np.array_equal(xn[i], want)
+    x = rand_bf16(rng, (5, K), 1.0)
+    x4 = bf16_bits((t_bf16(x).numpy() * 4.0).astype(np.float32))
+    assert np.array_equal(oracle.rmsnorm(x, gamma, 0.0), oracle.rmsnorm(x4, gamma, 0.0))
+
+
+def test_rmsnorm_matches_torch():
+    """Against torch's own RMS normalization of the same bf16 values: the
+    two bf16 roundings (of x * inv, then of the product with gamma) leave
+    every element within 2^-8 (two half-ulps of bf16) of it, relatively."""
+    rng = np.random.default_rng(61)
+    M, K, eps = 9, 512, 1e-5
+    x = rand_bf16(rng, (M, K), 1.0)
+    x[2] = bf16_bits((t_bf16(x[2]).numpy() * 1e-3).astype(np.float32))
+    gamma = rand_bf16(rng, (K,), 0.5)
+    xn = t_bf16(oracle.rmsnorm(x, gamma, eps)).numpy()
+    ref = torch.nn.functional.rms_norm(t_bf16(x), (K,), t_bf16(gamma), eps).numpy()
+    assert np.all(np.abs(xn - ref) <= 2.0 ** -8 * (1 + 2.0 ** -6) * np.abs(ref) + 1e-30)
+    assert np.mean(np.abs(xn - ref) <= 2.0 ** -9 * (1 + 2.0 ** -6) * np.abs(ref) + 1e-30) > 0.5
+
+
+def test_norm_quant_shrink_brute_force():
+    """M=2, K=8, r=2: Python loops from the definition (math.fsum for the
+    squares, numpy float32 scalars for the fp32 steps)."""
+    import math
+    rng = np.random.default_rng(62)
+    M, K, L, r = 2, 8, 2, 2
+    x = rand_bf16(rng, (M, K), 1.0)
+    gamma = rand_bf16(rng, (K,), 1.0)
+    A = rand_bf16(rng, (L, r, K), 0.3)
+    idx = np.array([1, 0])
+    out = oracle.norm_quant_shrink(x, gamma, 1e-6, A, idx)
+    xf, gf, Af = t_bf16(x).numpy(), t_bf16(gamma).numpy(), t_bf16(A).numpy()
+    for t in range(M):
+        ms = np.float32(math.fsum(float(v) ** 2 for v in xf[t]) / K)
+        inv = np.float32(np.float32(1.0) / np.float32(np.sqrt(np.float32(ms + np.float32(1e-6)))))
+        row = []
+        for k in range(K):
+            h = t_bf16(bf16_bits(np.array([np.float32(xf[t, k]) * inv], np.float32))).numpy()[0]
+            v = t_bf16(bf16_bits(np.array([np.float32(h) * np.float32(gf[k])], np.float32))).numpy()[0]
+            row.append(v)
+        row = np.array(row)
+        assert np.array_equal(t_bf16(out["xn"][t]).numpy(), row)
+        for j in range(r):
+            zt = math.fsum(Af[idx[t], j, k] * row[k] for k in range(K))
+            assert abs(out["z"][t, j] - zt) <= 1e-12 * max(1.0, abs(zt))
+    xq, sx = oracle.quant_act(out["xn"])
+    assert np.array_equal(xq, out["xq"]) and np.array_equal(sx, out["sx"])
