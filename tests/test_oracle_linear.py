@@ -577,7 +577,8 @@ def test_rmsnorm_exact_cases():
 def test_rmsnorm_matches_torch():
     """Against torch's own RMS normalization of the same bf16 values: the
     two bf16 roundings (of x * inv, then of the product with gamma) leave
-    every element within 2^-8 (two half-ulps of bf16) of it, relatively."""
+    every element within 2^-7 (two half-ulps of bf16 at the bottom of a
+    binade) of it, relatively, and the mean error well below that."""
     rng = np.random.default_rng(61)
     M, K, eps = 9, 512, 1e-5
     x = rand_bf16(rng, (M, K), 1.0)
@@ -585,8 +586,8 @@ def test_rmsnorm_matches_torch():
     gamma = rand_bf16(rng, (K,), 0.5)
     xn = t_bf16(oracle.rmsnorm(x, gamma, eps)).numpy()
     ref = torch.nn.functional.rms_norm(t_bf16(x), (K,), t_bf16(gamma), eps).numpy()
-    assert np.all(np.abs(xn - ref) <= 2.0 ** -8 * (1 + 2.0 ** -6) * np.abs(ref) + 1e-30)
-    assert np.mean(np.abs(xn - ref) <= 2.0 ** -9 * (1 + 2.0 ** -6) * np.abs(ref) + 1e-30) > 0.5
+    assert np.all(np.abs(xn - ref) <= 2.0 ** -7 * (1 + 2.0 ** -6) * np.abs(ref) + 1e-30)
+    assert np.abs(xn - ref).sum() <= 2.0 ** -8 * np.abs(ref).sum()
 
 
 def test_norm_quant_shrink_brute_force():
