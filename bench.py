@@ -38,7 +38,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 import fp4_gemm_amd as ep  # noqa: E402
-from workloads import config  # noqa: E402
+from workloads import bf16_bits as workloads_bf16, config  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
@@ -386,6 +386,47 @@ def sliced_rows(steps, warmup, prefill):
     return out
 
 
+def norm_rows(steps, warmup):
+    """The normalization kernel with the quantizer and the shrink inside, for
+    the projections whose input is a normalization's output (qkv and gate_up
+    of the Llama-8B decode layer, M = 1, one rank-64 tenant): per
+    projection, the plain normalization followed by the fused decode path,
+    against the normalization with quantizer and shrink followed by the GEMM
+    with z given (the GEMM never waits), and the separate chain."""
+    out = {}
+    layer = config(2)
+    rng = np.random.default_rng(12)
+    for g in layer.gemms:
+        if g.name not in ("qkv", "gate_up"):
+            continue
+        log(f"normalization paths, {g.name} ...")
+        p = Proj(g)
+        gamma = dev(workloads_bf16((1.0 + 0.1 * rng.standard_normal(g.K)).astype(np.float32)))
+        p.xn = torch.empty(p.M, p.K, dtype=torch.bfloat16, device=DEV)
+        x_raw = p.x
+
+        def norm_only(c, p=p, gamma=gamma):
+            ep.epilora_rmsnorm_quant_shrink(x_raw, gamma, 1e-5, None, None, xn=p.xn)
+
+        def norm_qs(c, p=p, gamma=gamma):
+            ep.epilora_rmsnorm_quant_shrink(x_raw, gamma, 1e-5, p.xq, p.sx, A=p.A[c % p.copies], idx=p.idx,
+                                            z=p.z, ws=p.ws_shr, ranks=p.ranks, mask=p.mask, sa=p.sa)
+
+        p.norm_only, p.norm_qs = norm_only, norm_qs
+        p.x = p.xn  # the GEMM paths read the normalized rows
+        norm_only(0)
+        before = pct(call_samples([p], ["norm_only", "fused"], 25, 2))
+        after = pct(call_samples([p], ["norm_qs", "gemm_lora"], 25, 2))
+        chain = pct(call_samples([p], ["norm_only", "quant", "shrink", "gemm_lora"], 25, 2))
+        nq = pct(call_samples([p], ["norm_qs"], 25, 2))
+        n0 = pct(call_samples([p], ["norm_only"], 25, 2))
+        out[g.name] = {"norm_then_fused_us": before, "norm_quant_shrink_then_gemm_us": after,
+                       "separate_chain_us": chain, "norm_quant_shrink_alone_us": nq, "norm_alone_us": n0}
+        del p
+        torch.cuda.empty_cache()
+    return out
+
+
 class ReadProbe:
     """The streaming-read probe (libepilora_probe.so, a measurement kernel of
     its own, outside the layer's library)."""
@@ -612,6 +653,7 @@ def main():
         mt = decode_multitenant(max(20, args.steps // 2), max(4, args.warmup // 2))
         mt["fp8_adapters"] = decode_multitenant(max(20, args.steps // 2), max(4, args.warmup // 2), afmt="fp8")
     sliced = sliced_rows(max(20, args.steps // 2), max(4, args.warmup // 2), not args.no_prefill)
+    norm = norm_rows(max(20, args.steps // 2), max(4, args.warmup // 2))
 
     # ---- prefill: M = 2048, tenant segments ----
     prefill = {}
@@ -695,6 +737,7 @@ def main():
                      "algorithmic_bytes": dom.bytes(), "launch_us": round(dom_us, 2)},
         "decode_multitenant_m32": mt,
         "sliced_adapters": sliced,
+        "norm_fused_shrink": norm,
         "prefill": prefill,
         "decode_72b_preft": d72,
         "cpu_baseline": cpu,

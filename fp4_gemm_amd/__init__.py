@@ -67,6 +67,8 @@ SIGNATURES = {
     "epilora_quant_weight_fp8": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P]),
     "epilora_quant_weight_fp4": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, _SZ, _P]),
     "epilora_lora_shrink": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
+    "epilora_rmsnorm_quant_shrink": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _F, _P, _I64, _P, _I64, _P, _P, _I32,
+                                                    _P, _I32, _I32, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "epilora_lora_shrink_ex": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _I32, _P, _I32, _I32, _I32, _P, _P, _P, _P,
                                               _P, _SZ, _P]),
     "epilora_lora_expand_add_ex": (ctypes.c_int, [_P, _I64, _I64, _P, _I32, _P, _I32, _I32, _I32, _P, _P, _P, _P,
@@ -195,6 +197,27 @@ def epilora_lora_shrink(x, A, idx, z, ws, ranks=None, mask=None, sa=None, stream
     _check("epilora_lora_shrink", lib().epilora_lora_shrink(
         _ptr(x), M, K, _ld(x), _ptr(A), L, r, _ptr(ranks), _ptr(idx), _ptr(mask), _ptr(z),
         _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def epilora_rmsnorm_quant_shrink(x, gamma, eps, xq, sx, *, xn=None, A=None, idx=None, z=None, ws=None,
+                                 ranks=None, mask=None, sa=None, stream=None):
+    """RMS normalization of x (bf16 [M][K]) with gamma (bf16 [K]), the
+    per-token FP8 quantizer of the result into xq / sx, the normalized rows
+    into xn (optional), and with A the shrink of the normalized rows into z
+    (A as for epilora_lora_shrink)."""
+    _need(x, torch.bfloat16, "x"); _need(gamma, torch.bfloat16, "gamma"); _need(xn, torch.bfloat16, "xn")
+    _need(xq, torch.uint8, "xq"); _need(sx, torch.float32, "sx"); _need(z, torch.float32, "z")
+    _need(idx, torch.int32, "idx"); _need(ranks, torch.int32, "ranks"); _need(mask, torch.uint8, "mask")
+    _need(A, torch.uint8 if sa is not None else torch.bfloat16, "A"); _need(sa, torch.float32, "sa")
+    M, K = x.shape
+    L = S = r = 0
+    if A is not None:
+        L, S, r = (A.shape[0], A.shape[1], A.shape[2]) if A.dim() == 4 else (A.shape[0], 1, A.shape[1])
+    _check("epilora_rmsnorm_quant_shrink", lib().epilora_rmsnorm_quant_shrink(
+        _ptr(x), M, K, _ld(x), _ptr(gamma), float(eps), _ptr(xn), 0 if xn is None else _ld(xn), _ptr(xq),
+        0 if xq is None else _ld(xq),
+        _ptr(sx), _ptr(A), A_FP8 if sa is not None else A_BF16, _ptr(sa), L, S, r, _ptr(ranks), _ptr(idx),
+        _ptr(mask), _ptr(z), _ptr(ws), 0 if ws is None else ws.numel(), _stream(stream)))
 
 
 def _slice_array(slices):

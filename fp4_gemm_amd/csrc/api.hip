@@ -3,6 +3,7 @@
 // the stream, except the diagnostic epilora_device_error.
 #include <atomic>
 #include <climits>
+#include <cmath>
 
 #include "../../include/epilora.h"
 #include "kernels.h"
@@ -278,6 +279,40 @@ int epilora_lora_shrink_ex(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
   for (int i = 0; i < kMaxSlices; ++i) ad.slice_end[i] = INT64_MAX;
   ad.afmt = afmt; ad.sa = sa; ad.sb = nullptr;
   return hip_status(launch_shrink(x, M, K, ldx, ad, z, ws, as_stream(stream)));
+}
+
+int epilora_rmsnorm_quant_shrink(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* gamma,
+                                 float eps, uint16_t* xn, int64_t ldn, uint8_t* xq, int64_t ldq, float* sx,
+                                 const void* A, int32_t afmt, const float* sa, int32_t L, int32_t nslices, int32_t r,
+                                 const int32_t* ranks, const int32_t* idx, const uint8_t* mask, float* z, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  if (M < 0 || K < 0) return EPILORA_ERR_INVALID_ARG;
+  if (!(eps >= 0.0f) || eps == INFINITY) return EPILORA_ERR_INVALID_ARG;
+  if (M == 0) return EPILORA_OK;
+  if (x == nullptr || gamma == nullptr || (xq == nullptr) != (sx == nullptr)) return EPILORA_ERR_INVALID_ARG;
+  if (ldx < K || (xq != nullptr && ldq < K) || (xn != nullptr && ldn < K)) return EPILORA_ERR_INVALID_ARG;
+  if (K == 0 || K % 16 != 0 || ldx % 16 != 0 || !aligned(x, 16) || !aligned(gamma, 16)) return EPILORA_ERR_UNSUPPORTED;
+  if (xq != nullptr && (ldq % 16 != 0 || !aligned(xq, 16) || !aligned(sx, 4))) return EPILORA_ERR_UNSUPPORTED;
+  if (xn != nullptr && (ldn % 16 != 0 || !aligned(xn, 16))) return EPILORA_ERR_UNSUPPORTED;
+  AdapterArgs ad{};
+  ad.S = 1; ad.r = 16; ad.zld = 16;
+  for (int i = 0; i < kMaxSlices; ++i) ad.slice_end[i] = INT64_MAX;
+  if (A != nullptr) {  // the shrink too
+    if (nslices < 1 || nslices > kMaxSlices || z == nullptr) return EPILORA_ERR_INVALID_ARG;
+    int st = check_afmt(afmt, sa, true, nullptr, false);
+    if (st != EPILORA_OK) return st;
+    st = check_adapters(L, r, A, true, nullptr, false, ranks, idx);
+    if (st != EPILORA_OK) return st;
+    if (!aligned(z, 16)) return EPILORA_ERR_UNSUPPORTED;
+    if (cdiv(M, kShrinkTokens) * nslices > kMaxShrinkTiles) return EPILORA_ERR_UNSUPPORTED;
+    st = check_ws(ws, ws_bytes, shrink_ws(kStateBytes, M, K, r, nslices).total);
+    if (st != EPILORA_OK) return st;
+    ad.A = reinterpret_cast<const uint16_t*>(A); ad.ranks = ranks; ad.idx = idx; ad.mask = mask;
+    ad.L = L; ad.r = r; ad.scale = 1.0f; ad.S = nslices; ad.zld = nslices * r;
+    ad.afmt = afmt; ad.sa = sa;
+  }
+  return hip_status(launch_norm_quant_shrink(x, M, K, ldx, gamma, eps, xn, ldn, xq, ldq, sx, ad, z, ws,
+                                             as_stream(stream)));
 }
 
 int epilora_lora_shrink(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* A, int32_t L,

@@ -48,8 +48,8 @@ struct DecodeParams {
   int* done;    // kDoneGroups sub-counters, kDoneStride words apart
 };
 
-template <int MB, int FMT, int NW, bool XLDS, int UB = 0>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((XLDS && NW == 8) ? 4 : 2))) void decode_kernel(DecodeParams p) {
+template <int MB, int FMT, int NW, bool XLDS, int UB = 0, bool GEN = false>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((XLDS && NW == 8 && !GEN) ? 4 : 2))) void decode_kernel(DecodeParams p) {
   extern __shared__ __align__(16) char smem[];
   const GemmParams& g = p.job.g;
   int* ctrl = g.ctrl;
@@ -75,14 +75,14 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((XLDS &
     shrink_range(p.s, split, s_begin, s_end);
     float* red = reinterpret_cast<float*>(smem);
     const uint64_t active =
-        shrink_tile<NW>(p.s, (int64_t)tile * kShrinkTokens, slice, s_begin, s_end, red, split == 0 && slice == 0);
-    shrink_finish<NW>(p.s, tile, slice, split, red, active);
+        shrink_tile<NW, GEN>(p.s, (int64_t)tile * kShrinkTokens, slice, s_begin, s_end, red, split == 0 && slice == 0);
+    shrink_finish<NW, kShrinkTokens, GEN>(p.s, tile, slice, split, red, active);
     return;
   }
 
   // ---- GEMM workgroup (persistent over its tiles)
   {
-    Skinny<MB, FMT, NW, XLDS, true, UB> sk(p.job, smem, bid - p.nq - p.ns);
+    Skinny<MB, FMT, NW, XLDS, true, UB, GEN> sk(p.job, smem, bid - p.nq - p.ns);
     sk.run();
   }
   if (!p.flags) return;
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((XLDS &
   }
 }
 
-template <int MB, int FMT, int NW, bool XLDS, int UB>
+template <int MB, int FMT, int NW, bool XLDS, int UB, bool GEN>
 static void launch_decode_u(DecodeParams& p, bool want_xq, hipStream_t stream) {
   const GemmParams& g = p.job.g;
   const int r = p.s.ad.r;
@@ -130,9 +130,9 @@ static void launch_decode_u(DecodeParams& p, bool want_xq, hipStream_t stream) {
   if (shrink_lds > lds) lds = shrink_lds;
   // The quantizing and shrink workgroups are dispatched first and hold their
   // slots only until they finish.
-  p.job.gwgs = skinny_groups(g.N, resident_groups(decode_kernel<MB, FMT, NW, XLDS, UB>, NW * 64, lds), StashCfg<MB>::n);
+  p.job.gwgs = skinny_groups(g.N, resident_groups(decode_kernel<MB, FMT, NW, XLDS, UB, GEN>, NW * 64, lds), StashCfg<MB>::n);
   const unsigned grid = (unsigned)(p.nq + p.ns + p.job.gwgs);
-  hipLaunchKernelGGL((decode_kernel<MB, FMT, NW, XLDS, UB>), dim3(grid), dim3(NW * 64), lds, stream, p);
+  hipLaunchKernelGGL((decode_kernel<MB, FMT, NW, XLDS, UB, GEN>), dim3(grid), dim3(NW * 64), lds, stream, p);
 }
 
 // Single-token-block eight-wave grids over short K and at most 512 tiles
@@ -141,8 +141,15 @@ static void launch_decode_u(DecodeParams& p, bool want_xq, hipStream_t stream) {
 template <int MB, int FMT, int NW, bool XLDS>
 static void launch_decode_x(DecodeParams& p, bool want_xq, hipStream_t stream) {
   const GemmParams& g = p.job.g;
-  if (MB == 1 && NW == 8 && g.K <= 4096 && cdiv(g.N, 16) <= 512) launch_decode_u<MB, FMT, NW, XLDS, 1>(p, want_xq, stream);
-  else launch_decode_u<MB, FMT, NW, XLDS, 0>(p, want_xq, stream);
+  // the general adapters (slices, FP8 storage) in a kernel of their own
+  if (g.ad.idx != nullptr && (g.ad.S > 1 || g.ad.afmt != 0)) {
+    launch_decode_u<MB, FMT, NW, XLDS, 0, true>(p, want_xq, stream);
+    return;
+  }
+  if (MB == 1 && NW == 8 && g.K <= 4096 && cdiv(g.N, 16) <= 512)
+    launch_decode_u<MB, FMT, NW, XLDS, 1, false>(p, want_xq, stream);
+  else
+    launch_decode_u<MB, FMT, NW, XLDS, 0, false>(p, want_xq, stream);
 }
 
 template <int MB, int FMT>

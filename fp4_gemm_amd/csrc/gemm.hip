@@ -9,21 +9,29 @@ namespace epilora {
 // Skinny kernel (M <= 64): persistent workgroups over 16-row tiles; see
 // skinny.h.
 // ---------------------------------------------------------------------------
-template <int MB, int FMT, int NW, bool XLDS>
+template <int MB, int FMT, int NW, bool XLDS, bool GEN>
 __global__ __launch_bounds__(NW * 64) void gemm_skinny_kernel(SkinnyJob J) {
   extern __shared__ __align__(16) char lds[];
-  Skinny<MB, FMT, NW, XLDS, false> s(J, lds, blockIdx.x);
+  Skinny<MB, FMT, NW, XLDS, false, 0, GEN> s(J, lds, blockIdx.x);
   s.run();
 }
 
 // ---------------------------------------------------------------------------
 
-template <int MB, int FMT, int NW, bool XLDS>
-static void launch_skinny_x(SkinnyJob& J, hipStream_t stream) {
+template <int MB, int FMT, int NW, bool XLDS, bool GEN>
+static void launch_skinny_g(SkinnyJob& J, hipStream_t stream) {
   const GemmParams& p = J.g;
   const size_t lds = skinny_lds(p.M, p.K, MB, NW, p.ad.r, false, XLDS, FMT);
-  J.gwgs = skinny_groups(p.N, resident_groups(gemm_skinny_kernel<MB, FMT, NW, XLDS>, NW * 64, lds));
-  hipLaunchKernelGGL((gemm_skinny_kernel<MB, FMT, NW, XLDS>), dim3(J.gwgs), dim3(NW * 64), lds, stream, J);
+  J.gwgs = skinny_groups(p.N, resident_groups(gemm_skinny_kernel<MB, FMT, NW, XLDS, GEN>, NW * 64, lds));
+  hipLaunchKernelGGL((gemm_skinny_kernel<MB, FMT, NW, XLDS, GEN>), dim3(J.gwgs), dim3(NW * 64), lds, stream, J);
+}
+
+// The general adapters (slices, FP8 storage) run in a kernel of their own.
+template <int MB, int FMT, int NW, bool XLDS>
+static void launch_skinny_x(SkinnyJob& J, hipStream_t stream) {
+  const AdapterArgs& ad = J.g.ad;
+  if (J.g.z != nullptr && (ad.S > 1 || ad.afmt != 0)) launch_skinny_g<MB, FMT, NW, XLDS, true>(J, stream);
+  else launch_skinny_g<MB, FMT, NW, XLDS, false>(J, stream);
 }
 
 template <int MB, int FMT, int NW>

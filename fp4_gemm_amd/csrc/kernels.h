@@ -70,6 +70,12 @@ hipError_t launch_gemm_lora(const uint8_t* xq, const float* sx, int64_t ldq, int
                             int64_t K, const WeightArgs& wt, const AdapterArgs& ad, const float* z,
                             uint16_t* y, int64_t ldy, void* ws, hipStream_t stream);
 
+// The RMS normalization with the quantizer and (when ad.idx is set) the
+// shrink from its output.
+hipError_t launch_norm_quant_shrink(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, const uint16_t* gamma,
+                                    float eps, uint16_t* xn, int64_t ldn, uint8_t* xq, int64_t ldq, float* sx,
+                                    const AdapterArgs& ad, float* z, void* ws, hipStream_t stream);
+
 // The fused decode path.
 hipError_t launch_decode_lora(const uint16_t* x, int64_t ldx, int64_t M, int64_t N, int64_t K,
                               const WeightArgs& wt, const AdapterArgs& ad, uint16_t* y, int64_t ldy,

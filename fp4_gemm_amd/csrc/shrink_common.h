@@ -49,10 +49,21 @@ __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<
 // result in `red` (LDS of kShrinkWaves * 16 * r floats) and returns the
 // tile's active tokens as a bit mask (bit i: token t0 + i).  Every thread of
 // the block must call it.
+// The activations the shrink multiplies, as loaded: 8 bf16 of token column
+// `col` at K offset k.  The shrink taken inside the normalization kernel
+// passes a transform that normalizes them on the fly.
+struct XIdentity {
+  __device__ __forceinline__ uint4 operator()(const uint4& v, int64_t, int) const { return v; }
+};
+
 // `slice`: which of the projection's output slices (its own A) this is.
-template <int NW>
+// `xt` maps the loaded activations to the values the shrink multiplies.
+// GEN: the general adapters (several output slices, FP8 storage) may occur;
+// without it the code assumes one slice of bf16 adapters (fewer registers in
+// the kernels that carry this code beside a weight stream).
+template <int NW, bool GEN = true, typename XT = XIdentity>
 __device__ __forceinline__ uint64_t shrink_tile(const ShrinkParams& p, int64_t t0, int slice, int s_begin, int s_end,
-                                                float* red, bool report) {
+                                                float* red, bool report, const XT& xt = XT()) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, grp = lane >> 4;
   const int r = p.ad.r;
@@ -79,7 +90,7 @@ __device__ __forceinline__ uint64_t shrink_tile(const ShrinkParams& p, int64_t t
     pending &= ~members;
     const bool member = (members >> col) & 1;
     const int jbn = (rank + 15) >> 4;
-    const int64_t aoff = ((int64_t)a * p.ad.S + slice) * r * K;  // elements
+    const int64_t aoff = ((int64_t)a * (GEN ? p.ad.S : 1) + slice) * r * K;  // elements
     const uint16_t* Aa = p.ad.A + aoff;
     const uint8_t* Aa8 = p.ad.A8() + aoff;
     const uint16_t* xr = p.x + (t0 + col) * p.ldx;
@@ -88,14 +99,14 @@ __device__ __forceinline__ uint64_t shrink_tile(const ShrinkParams& p, int64_t t
       uint4 xv[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        xv[i] = (member && k + i * 8 < K) ? ld16(xr + k + i * 8) : make_uint4(0, 0, 0, 0);
+        xv[i] = (member && k + i * 8 < K) ? xt(ld16(xr + k + i * 8), k + i * 8, col) : make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int jb = 0; jb < kMaxJB; ++jb) {
         if (jb < jbn && jb % WJ == wj) {
           const int j = jb * 16 + col;
           const bool rowok = j < rank;
           uint4 av[4];
-          if (p.ad.afmt != 0) {  // FP8 codes: 32 bytes, widened to bf16 exactly
+          if (GEN && p.ad.afmt != 0) {  // FP8 codes: 32 bytes, widened to bf16 exactly
             const uint8_t* ar8 = Aa8 + (int64_t)j * K + k;
             const uint4 q0 = (rowok && k < K) ? ld16(ar8) : make_uint4(0, 0, 0, 0);
             const uint4 q1 = (rowok && k + 16 < K) ? ld16(ar8 + 16) : make_uint4(0, 0, 0, 0);
@@ -234,12 +245,12 @@ __device__ __forceinline__ void shrink_store_partial(const ShrinkParams& p, int 
 // consumer polls could otherwise land after that clear and survive, as a
 // stale nonzero word, into the next call on the same workspace.
 // `slice`: the tile's z goes to columns slice * r .. + r of the [M][S r] z.
-template <int NW, int TT = kShrinkTokens>
+template <int NW, int TT = kShrinkTokens, bool GEN = true>
 __device__ __forceinline__ bool shrink_finish(const ShrinkParams& p, int tile, int slice, int split, float* red,
                                               uint64_t active) {
   __shared__ int last;
   const int64_t t0 = (int64_t)tile * TT;
-  const int r = p.ad.r, zld = p.ad.zld;
+  const int r = p.ad.r, zld = GEN ? p.ad.zld : p.ad.r;
   const int64_t rows = p.M - t0 < TT ? p.M - t0 : TT;
   const auto zr = make_rsrc(p.z + t0 * zld + slice * r, (uint32_t)(((rows - 1) * zld + r) * 4));
   auto zoff = [&](int e) { return (uint32_t)(((e / r) * zld + e % r) * 4); };  // e: a word of the tile, row-major
@@ -248,7 +259,7 @@ __device__ __forceinline__ bool shrink_finish(const ShrinkParams& p, int tile, i
   // FP8 adapters: the sums are of the codes, z_j = sa[a][slice][j] * sum
   // (the row scale applied once, to the finished sum).
   auto scaled = [&](int e, float4 v) {
-    if (p.ad.afmt == 0) return v;
+    if (!GEN || p.ad.afmt == 0) return v;
     int rk;
     const int a = resolve_token(t0 + e / r, p.M, p.ad, nullptr, false, rk);
     if (a < 0) return v;
@@ -269,7 +280,7 @@ __device__ __forceinline__ bool shrink_finish(const ShrinkParams& p, int tile, i
     return true;
   }
   shrink_store_partial<NW, TT>(p, tile, slice, split, red);
-  int* counter = &p.counters[tile * p.ad.S + slice];
+  int* counter = &p.counters[GEN ? tile * p.ad.S + slice : tile];
   if (threadIdx.x == 0) last = atomic_add_relaxed(counter, 1) == p.splits - 1;
   __syncthreads();
   if (!last) return false;

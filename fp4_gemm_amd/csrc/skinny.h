@@ -229,8 +229,11 @@ struct SelfQuant {
   }
 };
 
-// UB (> 0) overrides the steps per load batch.
-template <int MB, int FMT, int NW, bool XLDS, bool FUSED, int UB = 0>
+// UB (> 0) overrides the steps per load batch.  GEN: the general adapters
+// (several output slices, FP8 storage) may occur; without it the epilogue
+// assumes one slice of bf16 adapters and carries none of that code, which
+// keeps the registers of the weight stream free.
+template <int MB, int FMT, int NW, bool XLDS, bool FUSED, int UB = 0, bool GEN = true>
 struct Skinny {
   // The fused kernel's 8-wave workgroups take half batches so that two fit
   // on a compute unit (four waves per SIMD), beside a producer workgroup.
@@ -294,6 +297,9 @@ struct Skinny {
   }
 
   __device__ __forceinline__ int64_t n0_of(int j) const { return (int64_t)(g + (j / nb) * J.gwgs) * 16; }
+  __device__ __forceinline__ bool af8() const { return GEN && p.ad.afmt != 0; }
+  __device__ __forceinline__ int zld() const { return GEN ? p.ad.zld : p.ad.r; }
+  __device__ __forceinline__ int slice(int64_t n) const { return GEN ? slice_of(p.ad, n) : 0; }
 
   // ---- loads ----------------------------------------------------------------
   __device__ __forceinline__ void load_w(SkinnyBatch<MB, U>& b, int j) const {
@@ -445,7 +451,7 @@ struct Skinny {
     const int j0 = jl * ch;
     if (j0 >= ts.rank) return v;
     const int64_t off = ((int64_t)ts.a * p.N + n) * r + j0;  // elements
-    if (p.ad.afmt != 0) {  // FP8 codes, widened to bf16 exactly
+    if (af8()) {  // FP8 codes, widened to bf16 exactly
       const uint8_t* src = p.ad.B8() + off;
       uint32_t lo = 0, hi = 0;
       if (ch == 8) { const uint2 w = *reinterpret_cast<const uint2*>(src); lo = w.x; hi = w.y; }
@@ -505,7 +511,7 @@ struct Skinny {
       l += __shfl_xor(l, 1, 16);
       if (jl == 0 && n < p.N) {
         float y = (base[o] * sxs[t]) * (have_pre ? pws : weight_scale<FMT>(p.wt, n));
-        if (lora && p.ad.afmt != 0) l *= p.ad.sb[(int64_t)tok[t].a * p.N + n];  // FP8 adapters: the row scale
+        if (lora && af8()) l *= p.ad.sb[(int64_t)tok[t].a * p.N + n];  // FP8 adapters: the row scale
         if (lora) y = y + p.ad.scale * l;
         p.y[(int64_t)t * p.ldy + n] = (uint16_t)f32_to_bf16(y);
       }
@@ -522,7 +528,7 @@ struct Skinny {
   __device__ __forceinline__ bool poll_z(int slice) const {
     const int r = p.ad.r;
     const int n = (int)p.M * r;
-    const auto zr = make_rsrc(p.z + slice * r, (uint32_t)(((p.M - 1) * p.ad.zld + r) * 4));
+    const auto zr = make_rsrc(p.z + slice * r, (uint32_t)(((p.M - 1) * zld() + r) * 4));
     int* err = p.ctrl + kCtrlError;
     const int64_t start = wall_clock64();
     for (;;) {
@@ -532,7 +538,7 @@ struct Skinny {
         if (tok[e / r].a < 0) {
           zs[e] = 0.f;
         } else {
-          const uint32_t w = buf_load4<kCoherent>(zr, 4u * ((e / r) * p.ad.zld + e % r));
+          const uint32_t w = buf_load4<kCoherent>(zr, 4u * ((e / r) * zld() + e % r));
           if (w == 0u) missing = 1;
           else zs[e] = __uint_as_float(~w);
         }
@@ -562,10 +568,10 @@ struct Skinny {
   // barrier (the previous slice's values may still be read).
   __device__ __forceinline__ void stage_z(int slice) const {
     const int r = p.ad.r;
-    const auto zr = make_rsrc(p.z + slice * r, (uint32_t)(((p.M - 1) * p.ad.zld + r) * 4));
+    const auto zr = make_rsrc(p.z + slice * r, (uint32_t)(((p.M - 1) * zld() + r) * 4));
     __syncthreads();
     for (int e = threadIdx.x; e < p.M * r; e += NW * kWave)
-      zs[e] = tok[e / r].a >= 0 ? __uint_as_float(buf_load4<XPOL>(zr, 4u * ((e / r) * p.ad.zld + e % r))) : 0.f;
+      zs[e] = tok[e / r].a >= 0 ? __uint_as_float(buf_load4<XPOL>(zr, 4u * ((e / r) * zld() + e % r))) : 0.f;
     __syncthreads();
   }
 
@@ -599,8 +605,8 @@ struct Skinny {
       return;
     }
     reduce_tile(acc, red);
-    if (adapters && p.ad.S > 1) {  // a tile lies inside one slice; the slices come in order
-      const int sl = slice_of(p.ad, n0_of(j));
+    if (GEN && adapters && p.ad.S > 1) {  // a tile lies inside one slice; the slices come in order
+      const int sl = slice(n0_of(j));
       if (sl != zslice) {
         stage_z(sl);
         zslice = sl;
@@ -626,8 +632,8 @@ struct Skinny {
     // The tiles come in output order: for each slice they span (one unless
     // the projection has several), poll that slice's z into LDS, then write
     // the outputs of the tiles inside it.
-    const int sl0 = mine > 0 ? slice_of(p.ad, n0_of(0)) : 0;
-    const int sl1 = mine > 0 ? slice_of(p.ad, n0_of((mine - 1) * nb)) : 0;
+    const int sl0 = mine > 0 ? slice(n0_of(0)) : 0;
+    const int sl1 = mine > 0 ? slice(n0_of((mine - 1) * nb)) : 0;
     for (int sl = sl0; sl <= sl1; ++sl) {
       if (adapters) {
         if (sl > sl0) __syncthreads();  // the previous slice's z is no longer read
@@ -636,7 +642,7 @@ struct Skinny {
       }
 #pragma unroll
       for (int s = 0; s < S; ++s)
-        if (s < mine && (sl0 == sl1 || slice_of(p.ad, n0_of(s * nb)) == sl))
+        if (s < mine && (sl0 == sl1 || slice(n0_of(s * nb)) == sl))
           outputs(n0_of(s * nb), stash + s * T * 16, true, pb[s], pw[s]);
     }
   }
@@ -671,7 +677,7 @@ struct Skinny {
     if (!FUSED) {
       for (int t = threadIdx.x; t < M; t += NT) sxs[t] = p.sx[t];
       if (adapters) {
-        zslice = total > 0 ? slice_of(p.ad, n0_of(0)) : 0;
+        zslice = total > 0 ? slice(n0_of(0)) : 0;
         stage_z(zslice);
       }
     }

@@ -217,6 +217,33 @@ int epilora_device_error(void* ws, int32_t clear, int32_t* out_code,
 int epilora_quant_act(const uint16_t* x, int64_t M, int64_t K, int64_t ldx,
                       uint8_t* xq, int64_t ldq, float* sx, void* stream);
 
+/* The RMS normalization in front of the query / key / value and gate / up
+ * projections, with the per-token FP8 quantizer and the shrink taken from
+ * its output in the same kernel ("EpiLoRA ...", appendix "Discussion and
+ * Limitations": computing the down-projection inside the normalization
+ * kernel that already reads the input hides it for these projections; the
+ * GEMM then finds z ready: epilora_gemm_lora).
+ * Per token row t: ms = fp32(sum_k x_k^2 / K) (the squares summed in fp64),
+ * inv = fp32(1 / fp32(sqrt(fp32(ms + eps)))) (correctly rounded),
+ * xn_k = bf16(bf16(x_k * inv) * gamma_k) (round to nearest even);
+ * xq, sx = the epilora_quant_act result for xn (bit for bit); with A != NULL,
+ * z = the epilora_lora_shrink_ex result for xn (same arguments and rules).
+ * x: bf16 [M][ldx]; gamma: bf16 [K]; xn: bf16 [M][ldn] or NULL (not
+ * written); xq: [M][ldq] and sx: [M], or both NULL (no codes: the plain
+ * normalization when xn is given); eps >= 0.  K % 16 == 0, ldx, ldq, ldn
+ * multiples of 16, x, gamma, xn, xq 16-byte aligned.  A == NULL: no shrink
+ * (the adapter arguments, z and the workspace are ignored); otherwise a
+ * workspace of EPILORA_OP_SHRINK (r = nslices * r). */
+int epilora_rmsnorm_quant_shrink(const uint16_t* x, int64_t M, int64_t K,
+                                 int64_t ldx, const uint16_t* gamma, float eps,
+                                 uint16_t* xn, int64_t ldn, uint8_t* xq,
+                                 int64_t ldq, float* sx, const void* A,
+                                 int32_t afmt, const float* sa, int32_t L,
+                                 int32_t nslices, int32_t r,
+                                 const int32_t* ranks, const int32_t* idx,
+                                 const uint8_t* mask, float* z, void* ws,
+                                 size_t ws_bytes, void* stream);
+
 /* Load-time FP8 weight quantization, one scale per output channel (the
  * pages' FP8 bases are quantized when the model loads: Evaluation, Setup).
  * Same rule as epilora_quant_act applied to the rows of W.

@@ -32,7 +32,7 @@ def L():
 
 def test_exports_every_declared_function(L):
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     for n in names:
         assert hasattr(L, n), n
         assert n in ep.SIGNATURES, n
@@ -208,3 +208,19 @@ def test_binding_without_gpu_refuses_cpu_tensors():
     x = torch.zeros(2, 32, dtype=torch.bfloat16)
     with pytest.raises(TypeError):
         ep.epilora_quant_act(x, torch.zeros(2, 32, dtype=torch.uint8), torch.zeros(2))
+
+
+def test_norm_validation(L):
+    n = L.epilora_rmsnorm_quant_shrink
+    args = lambda **kw: [kw.get(k, v) for k, v in (
+        ("x", P), ("M", 4), ("K", 256), ("ldx", 256), ("gamma", P), ("eps", 1e-5), ("xn", None), ("ldn", 0),
+        ("xq", P2), ("ldq", 256), ("sx", P), ("A", None), ("afmt", 0), ("sa", None), ("L", 0), ("S", 1),
+        ("r", 16), ("ranks", None), ("idx", None), ("mask", None), ("z", None), ("ws", None), ("wsb", 0),
+        ("stream", None))]
+    assert n(*args(M=0)) == ep.OK
+    assert n(*args(gamma=None)) == ep.ERR_INVALID_ARG
+    assert n(*args(eps=-1.0)) == ep.ERR_INVALID_ARG
+    assert n(*args(K=264, ldx=272, ldq=272)) == ep.ERR_UNSUPPORTED
+    assert n(*args(xn=P, ldn=100)) == ep.ERR_INVALID_ARG
+    assert n(*args(A=P, L=4, idx=P, z=P)) == ep.ERR_WORKSPACE          # the shrink needs a workspace
+    assert n(*args(A=P, L=4, idx=P, z=None, ws=P, wsb=1 << 20)) == ep.ERR_INVALID_ARG

@@ -496,3 +496,103 @@ def test_fp8_adapters_vs_oracle(M, K, N, slices, L, r, kind, use_mask, use_ranks
     bound = 2.0 ** -8 * (np.abs(ref["base"]) + np.abs(ref["y"])) * 1.001 + 1e-4 * rms
     assert np.all(np.abs(yg - ref["y"]) <= bound)
     assert ep.epilora_device_error(sep["ws"]) == 0
+
+
+# --- the normalization with the quantizer and shrink fused in -----------------------------
+
+NORM_CASES = [
+    # M, K, L, r, slices, adapter format, with adapters
+    (1, 4096, 1, 64, 1, "bf16", True),
+    (7, 512, 4, 16, 1, "bf16", True),
+    (33, 4096, 6, 32, 3, "bf16", True),
+    (64, 8192, 9, 16, 1, "fp8", True),
+    (300, 1024, 6, 64, 2, "bf16", True),
+    (2048, 4096, 16, 128, 1, "bf16", True),
+    (5, 256, 1, 16, 1, "bf16", False),
+]
+
+
+@pytest.mark.parametrize("M,K,L,r,S,afmt,with_a", NORM_CASES)
+def test_norm_quant_shrink_vs_oracle(M, K, L, r, S, afmt, with_a):
+    say(f"norm+quant+shrink M={M} K={K} L={L} r={r} S={S} {afmt} adapters={with_a}")
+    rng = np.random.default_rng(9500 + M + K)
+    x = bf16_bits((rng.standard_normal((M, K)) * rng.uniform(0.1, 10.0, (M, 1))).astype(np.float32))
+    x[0, : K // 2] = 0                                   # a half-zero row
+    gamma = bf16_bits((1.0 + 0.2 * rng.standard_normal(K)).astype(np.float32))
+    idx = rng.integers(-1, L, M).astype(np.int32)
+    ranks = rng.choice([0, 16, r], size=L).astype(np.int32) if M > 40 else None
+    eps = 1e-5
+    A_np = bf16_bits((rng.standard_normal((L, S, r, K)) / np.sqrt(K)).astype(np.float32))
+    sa_np = None
+    xd, gd = to_dev(x), to_dev(gamma)
+    xn = torch.empty(M, K, dtype=torch.bfloat16, device=DEV)
+    xq = torch.empty(M, K, dtype=torch.uint8, device=DEV)
+    sx = torch.empty(M, dtype=torch.float32, device=DEV)
+    z = torch.empty(M, S * r, dtype=torch.float32, device=DEV)
+    kw = {}
+    if with_a:
+        A_dev = to_dev(A_np if S > 1 else A_np[:, 0])
+        if afmt == "fp8":
+            A8 = torch.empty(A_dev.shape, dtype=torch.uint8, device=DEV)
+            sa = torch.empty(A_dev.shape[:-1], dtype=torch.float32, device=DEV)
+            ep.epilora_quant_weight_fp8(A_dev.reshape(-1, K), A8.view(-1, K), sa.view(-1))
+            A_dev, kw["sa"] = A8, sa
+            sa_np = to_np(sa).reshape(L, S, r) if S > 1 else to_np(sa)
+        ws = ep.new_workspace(ep.OP_SHRINK, M, 0, K, S * r)
+        kw.update(A=A_dev, idx=to_dev(idx), z=z, ws=ws, ranks=None if ranks is None else to_dev(ranks))
+    ep.epilora_rmsnorm_quant_shrink(xd, gd, eps, xq, sx, xn=xn, **kw)
+    torch.cuda.synchronize()
+    xn_g = to_np(xn)
+    ref = oracle.rmsnorm(x, gamma, eps)
+    diff = xn_g != ref
+    ulp = np.abs(xn_g.astype(np.int64) - ref.astype(np.int64))
+    say(f"  xn: {int(diff.sum())} of {diff.size} values differ from the oracle (max {int(ulp.max())} ulp)")
+    assert ulp.max() <= 1 and diff.mean() <= 1e-4
+    # the codes and scales of the GPU's own normalized rows: bit for bit
+    xq_ref, sx_ref = oracle.quant_act(xn_g)
+    assert np.array_equal(to_np(sx), sx_ref) and np.array_equal(to_np(xq), xq_ref)
+    if not with_a:
+        return
+    A_or = A_np if S > 1 else A_np[:, 0]
+    if afmt == "fp8":
+        A_or, sa_or = oracle.quant_adapter_fp8(A_or)
+        assert np.array_equal(to_np(kw["A"]), A_or) and np.array_equal(to_np(kw["sa"]), sa_or)
+    zs = [oracle.shrink(xn_g, A_or if S == 1 else A_or[:, s], idx, ranks,
+                        a_scale=None if sa_np is None else (sa_np if S == 1 else sa_np[:, s])) for s in range(S)]
+    z_ref = np.concatenate(zs, axis=1)
+    zg = to_np(z).astype(np.float64)
+    scale = max(np.sqrt(np.mean(z_ref ** 2)), 1e-30)
+    assert np.abs(zg - z_ref).max() <= 1e-4 * scale
+    act = oracle.active_rows(idx, L, r, ranks)[0]
+    assert not zg[~act].any()
+    assert ep.epilora_device_error(kw["ws"]) == 0
+    # bitwise the separate shrink on the normalized rows (same summation order)
+    z2 = torch.empty_like(z)
+    ep.epilora_lora_shrink(xn, kw["A"], kw["idx"], z2, kw["ws"], ranks=kw["ranks"], sa=kw.get("sa"))
+    assert torch.equal(z, z2)
+
+
+def test_norm_path_equals_fused_decode():
+    # qkv-shaped projection with per-slice adapters: normalization kernel
+    # (quantizer and shrink inside), then the GEMM with z given, against the
+    # fused decode path on the normalized rows: bit for bit.
+    say("norm path vs fused decode, qkv shape")
+    from workloads import config
+    g = config(2, sliced=True).gemm("qkv")
+    rng = np.random.default_rng(77)
+    gamma = bf16_bits((1.0 + 0.1 * rng.standard_normal(g.K)).astype(np.float32))
+    d = DeviceGemm(g)
+    xn = torch.empty(d.M, d.K, dtype=torch.bfloat16, device=DEV)
+    xq = torch.empty(d.M, d.K, dtype=torch.uint8, device=DEV)
+    sx = torch.empty(d.M, dtype=torch.float32, device=DEV)
+    z = torch.empty(d.M, d.S * d.r, dtype=torch.float32, device=DEV)
+    ws = ep.new_workspace(ep.OP_SHRINK, d.M, d.N, d.K, d.S * d.r)
+    ep.epilora_rmsnorm_quant_shrink(d.x, to_dev(gamma), 1e-5, xq, sx, xn=xn, A=d.A, idx=d.idx, z=z, ws=ws)
+    y = d.gemm(xq, sx, z, ws)
+    d2 = DeviceGemm(g, x=to_np(xn))
+    fused = d2.decode()
+    assert torch.equal(fused["xq"], xq) and torch.equal(fused["sx"], sx)
+    assert torch.equal(fused["y"], y)
+    ref = d2.oracle(cols=np.arange(0, d.N, 7))
+    from gpu_harness import compare
+    compare(to_np(y)[:, np.arange(0, d.N, 7)], ref["y"], "norm path")
