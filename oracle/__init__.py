@@ -43,6 +43,7 @@ from .linear import (  # noqa: F401
     fold_decode_fp4,
     exact_decode_fp4,
     base_fp8,
+    base_w8a16,
     base_fp4,
     active_rows,
     quant_adapter_fp8,

@@ -161,6 +161,19 @@ def base_fp8(xq, sx, wq, sw, rows=None, cols=None):
     return (acc * s_t[:, None]) * s_n[None, :]
 
 
+def base_w8a16(x, wq, sw, rows=None, cols=None):
+    """The matched engine's GEMM ("EpiLoRA ...", Design, "LoRA RL on the same
+    base": a W8A16 GEMM on the FP8 weights whose activations stay in bf16,
+    so the engine rounds nothing the trainer does not): each FP8 weight is
+    widened exactly, acc[t][n] = sum_k bf16(x[t][k]) * e4m3(wq[n][k]), and
+    base = acc * sw[n]; no activation quantization, no activation scale."""
+    X = bf16_to_f32(_pick(x, rows)).astype(np.float64)
+    W = e4m3_decode(_pick(wq, cols))
+    acc = X @ W.T
+    s_n = _pick(np.asarray(sw, np.float32), cols).astype(np.float64)
+    return acc * s_n[None, :]
+
+
 def base_fp4(xq, sx, wc, bs, gs, rows=None, cols=None):
     """4-bit base through the fold: each weight is the FP8 byte
     T[code][block scale]; base = (acc * sx[t]) * (gs * 2**3)."""
@@ -251,7 +264,7 @@ def expand(z, B, idx, scale, ranks=None, mask=None, cols=None, b_scale=None):
 
 
 def linear_lora(x, A, B, idx, scale, *, wq=None, sw=None, wc=None, bs=None,
-                gs=None, ranks=None, mask=None, rows=None, cols=None, sa=None, sb=None):
+                gs=None, ranks=None, mask=None, rows=None, cols=None, sa=None, sb=None, a16=False):
     """The whole layer: per-token quantisation, base GEMM, shrink and the
     epilogue.  Exactly one weight format is given (wq+sw, or wc+bs+gs).
 
@@ -261,13 +274,19 @@ def linear_lora(x, A, B, idx, scale, *, wq=None, sw=None, wc=None, bs=None,
     to a sample of tokens; to sample output channels either pass `cols`, or
     pass the weights and B of the sampled channels only.  With sa and sb
     the adapters are stored in FP8: A and B hold E4M3 codes, sa [L][r] and
-    sb [L][N] their row scales (quant_adapter_fp8)."""
+    sb [L][N] their row scales (quant_adapter_fp8).  With a16 the base is
+    the W8A16 GEMM on the bf16 activations (base_w8a16; FP8 weights only)
+    and xq, sx are None."""
     xs = _pick(x, rows)
-    xq, sx = quant_act(xs)  # per-token quantisation is row-local
-    if wq is not None:
-        base = base_fp8(xq, sx, wq, sw, cols=cols)
+    if a16:
+        xq = sx = None
+        base = base_w8a16(xs, wq, sw, cols=cols)
     else:
-        base = base_fp4(xq, sx, wc, bs, gs, cols=cols)
+        xq, sx = quant_act(xs)  # per-token quantisation is row-local
+        if wq is not None:
+            base = base_fp8(xq, sx, wq, sw, cols=cols)
+        else:
+            base = base_fp4(xq, sx, wc, bs, gs, cols=cols)
     idx_s = _pick(np.asarray(idx), rows)
     mask_s = None if mask is None else _pick(np.asarray(mask), rows)
     z = shrink(xs, A, idx_s, ranks, mask_s, a_scale=sa)
@@ -290,7 +309,8 @@ def slice_bounds(slice_n):
 
 
 def linear_lora_sliced(x, A, B, idx, scale, slice_n, *, wq=None, sw=None, wc=None, bs=None, gs=None,
-                       ranks=None, mask=None, rows=None, cols=None, weights_of_cols=False, sa=None, sb=None):
+                       ranks=None, mask=None, rows=None, cols=None, weights_of_cols=False, sa=None, sb=None,
+                       a16=False):
     """A projection whose outputs are several consecutive slices, each with
     its own adapter pair: attention's query / key / value (three slices of
     unequal widths) or the MLP's gate / up (two), as in "EpiLoRA ...",
@@ -306,19 +326,23 @@ def linear_lora_sliced(x, A, B, idx, scale, slice_n, *, wq=None, sw=None, wc=Non
     no add.  The result's z is [M][S * r], slice s in columns s*r .. s*r+r.
     `cols` samples output columns (indices into N); with weights_of_cols the
     weights passed are already those columns' rows, in that order.  With sa
-    ([L][S][r]) and sb ([L][N]) the adapters are stored in FP8, as in
-    linear_lora."""
+    ([L][S][r]) and sb ([L][N]) the adapters are stored in FP8, and with a16
+    the base is the W8A16 GEMM, as in linear_lora."""
     L, S, r, K = A.shape
     bounds = slice_bounds(slice_n)
     if len(bounds) != S or bounds[-1][1] != B.shape[1]:
         raise ValueError("slice widths must match A's slices and B's rows")
     xs = _pick(x, rows)
-    xq, sx = quant_act(xs)
     wcols = None if weights_of_cols else cols
-    if wq is not None:
-        base = base_fp8(xq, sx, wq, sw, cols=wcols)
+    if a16:
+        xq = sx = None
+        base = base_w8a16(xs, wq, sw, cols=wcols)
     else:
-        base = base_fp4(xq, sx, wc, bs, gs, cols=wcols)
+        xq, sx = quant_act(xs)
+        if wq is not None:
+            base = base_fp8(xq, sx, wq, sw, cols=wcols)
+        else:
+            base = base_fp4(xq, sx, wc, bs, gs, cols=wcols)
     idx_s = _pick(np.asarray(idx), rows)
     mask_s = None if mask is None else _pick(np.asarray(mask), rows)
     colset = np.arange(B.shape[1]) if cols is None else np.asarray(cols)

@@ -617,3 +617,41 @@ def test_norm_quant_shrink_brute_force():
             assert abs(out["z"][t, j] - zt) <= 1e-12 * max(1.0, abs(zt))
     xq, sx = oracle.quant_act(out["xn"])
     assert np.array_equal(xq, out["xq"]) and np.array_equal(sx, out["sx"])
+
+
+# --- the matched W8A16 GEMM -------------------------------------------------------------
+
+def test_w8a16_equals_w8a8_on_representable_rows():
+    """Rows built as e4m3 codes times 2^k (exact in bf16, one element at
+    +-448 2^k) quantize to themselves, so the W8A8 layer (independently
+    pinned) and the W8A16 layer must agree on them."""
+    rng = np.random.default_rng(70)
+    M, K, N = 5, 96, 40
+    finite = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], np.uint8)
+    codes = rng.choice(finite, size=(M, K))
+    codes[:, 7] = 0x7E
+    x = bf16_bits((t_e4m3(codes).numpy() * 2.0 ** rng.integers(-6, 4, size=(M, 1))).astype(np.float32))
+    w = rand_bf16(rng, (N, K), 0.02)
+    wq, sw = oracle.quant_weight_fp8(w)
+    _, _, A, B = make(rng, M=M, K=K, N=N, L=2, r=4)
+    idx = np.array([0, 1, -1, 1, 0])
+    a = oracle.linear_lora(x, A, B, idx, 2.0, wq=wq, sw=sw, a16=True)
+    b = oracle.linear_lora(x, A, B, idx, 2.0, wq=wq, sw=sw)
+    assert np.allclose(a["base"], b["base"], rtol=1e-13, atol=1e-16)
+    assert np.allclose(a["y"], b["y"], rtol=1e-13, atol=1e-16)
+    assert a["xq"] is None and np.array_equal(b["xq"], codes)
+
+
+def test_w8a16_matches_torch_matmul():
+    """Against torch: its own float8_e4m3fn decode of the weights times the
+    per-channel scale, the bf16 activations, an fp64 matmul."""
+    rng = np.random.default_rng(71)
+    x, w, A, B = make(rng, M=9, K=128, N=36)
+    wq, sw = oracle.quant_weight_fp8(w)
+    out = oracle.linear_lora(x, A, B, np.full(9, -1), 2.0, wq=wq, sw=sw, a16=True)
+    ref = (t_bf16(x) @ (t_e4m3(wq) * torch.from_numpy(sw.astype(np.float64))[:, None]).T).numpy()
+    assert np.allclose(out["y"], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    # closer to the unquantized product than the W8A8 layer (no activation rounding)
+    exact = (t_bf16(x) @ t_bf16(w).T).numpy()
+    w8a8 = oracle.linear_lora(x, A, B, np.full(9, -1), 2.0, wq=wq, sw=sw)["y"]
+    assert np.abs(out["y"] - exact).mean() < np.abs(w8a8 - exact).mean()
