@@ -21,6 +21,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 DEV_BAD_INDEX, DEV_WAIT_TIMEOUT, DEV_INTERNAL = 1, 2, 4
 W_FP8, W_FP4 = 0, 1
 A_BF16, A_FP8 = 0, 1
+ACT_FP8, ACT_BF16 = 0, 1
 OP_SHRINK, OP_GEMM, OP_EXPAND, OP_DECODE, OP_QUANT_W4 = 1, 2, 3, 4, 5
 DECODE_MAX_M = 64
 MAX_RANK = 128
@@ -49,6 +50,7 @@ class LayerArgs(ctypes.Structure):
         ("ws", ctypes.c_void_p), ("ws_bytes", ctypes.c_size_t),
         ("nslices", ctypes.c_int32), ("slice_n", ctypes.c_int64 * 4),
         ("afmt", ctypes.c_int32), ("sa", ctypes.c_void_p), ("sb", ctypes.c_void_p),
+        ("amode", ctypes.c_int32),
     ]
 
 
@@ -276,15 +278,19 @@ def _adapters(a, A, B, idx, ranks, mask, scale, slices=None, sa=None, sb=None):
 
 
 def epilora_gemm_lora(xq, sx, w, y, *, sw=None, bs=None, gs=None, z=None, B=None, idx=None, ranks=None,
-                      mask=None, scale=1.0, ws=None, slices=None, sb=None, stream=None):
+                      mask=None, scale=1.0, ws=None, slices=None, sb=None, x16=None, stream=None):
     """y = bf16(dequant(w . xq) [+ s B[idx] z on active rows]); z=None: base
-    only; `slices`: output slice widths (per-slice adapters, z [M][S r])."""
+    only; `slices`: output slice widths (per-slice adapters, z [M][S r]);
+    x16 (bf16 [M][K], with xq = sx = None): the matched W8A16 GEMM."""
     _need(xq, torch.uint8, "xq"); _need(sx, torch.float32, "sx"); _need(y, torch.bfloat16, "y")
-    _need(z, torch.float32, "z")
+    _need(z, torch.float32, "z"); _need(x16, torch.bfloat16, "x16")
     a = LayerArgs()
-    a.M, a.K = xq.shape
+    a.M, a.K = (x16 if x16 is not None else xq).shape
     a.N = y.shape[1]
-    a.xq, a.sx, a.ldq = _ptr(xq), _ptr(sx), _ld(xq)
+    if x16 is not None:
+        a.amode, a.x, a.ldx = ACT_BF16, _ptr(x16), _ld(x16)
+    else:
+        a.xq, a.sx, a.ldq = _ptr(xq), _ptr(sx), _ld(xq)
     _weights(a, w, sw, bs, gs)
     _adapters(a, None, B, idx, ranks, mask, scale, slices, None, sb)
     a.z = _ptr(z)
@@ -304,11 +310,14 @@ def epilora_decode_lora_noalloc(x, w, y, *, sw=None, bs=None, gs=None, A=None, B
 
 
 def epilora_decode_lora(x, w, y, *, sw=None, bs=None, gs=None, A=None, B=None, idx=None, ranks=None, mask=None,
-                        scale=1.0, ws=None, xq_out=None, sx_out=None, slices=None, sa=None, sb=None, stream=None):
+                        scale=1.0, ws=None, xq_out=None, sx_out=None, slices=None, sa=None, sb=None, a16=False,
+                        stream=None):
     """The fused decode path: quantization, shrink and GEMM in one launch;
     `slices`: output slice widths (per-slice adapters, A [L][S][r][K]);
-    sa, sb: row scales of FP8-stored adapters (A, B uint8 codes)."""
+    sa, sb: row scales of FP8-stored adapters (A, B uint8 codes); a16: the
+    matched W8A16 GEMM on the bf16 x (no quantization)."""
     a = _decode_args(x, w, y, sw, bs, gs, A, B, idx, ranks, mask, scale, ws, xq_out, sx_out, slices, sa, sb)
+    a.amode = ACT_BF16 if a16 else ACT_FP8
     _check("epilora_decode_lora", lib().epilora_decode_lora(ctypes.byref(a), _stream(stream)))
 
 

@@ -123,11 +123,14 @@ int32_t slices_of(const epilora_layer_args* a) { return a->nslices > 1 ? a->nsli
 // workspace); `r` receives the slot width the workspace is sized for.
 int check_decode(const epilora_layer_args* a, int32_t& r) {
   if (a->M < 0 || a->N < 0 || a->K < 0) return EPILORA_ERR_INVALID_ARG;
+  if (a->amode != EPILORA_ACT_FP8 && a->amode != EPILORA_ACT_BF16) return EPILORA_ERR_INVALID_ARG;
+  if (a->amode == EPILORA_ACT_BF16 && (a->xq_out != nullptr || a->sx_out != nullptr)) return EPILORA_ERR_INVALID_ARG;
   if (a->M == 0 || a->N == 0) return EPILORA_OK;
   if (a->M > EPILORA_DECODE_MAX_M) return EPILORA_ERR_UNSUPPORTED;
   if (a->x == nullptr || a->y == nullptr) return EPILORA_ERR_INVALID_ARG;
   int st = check_weights(a);
   if (st != EPILORA_OK) return st;
+  if (a->amode == EPILORA_ACT_BF16 && a->wfmt != EPILORA_W_FP8) return EPILORA_ERR_UNSUPPORTED;
   if (a->ldx < a->K || a->ldy < a->N) return EPILORA_ERR_INVALID_ARG;
   if (a->ldx % 16 != 0 || !aligned(a->x, 16) || !aligned(a->y, 2)) return EPILORA_ERR_UNSUPPORTED;
   if (a->xq_out != nullptr) {
@@ -325,13 +328,23 @@ int epilora_lora_shrink(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, co
 int epilora_gemm_lora(const epilora_layer_args* a, void* stream) {
   if (a == nullptr) return EPILORA_ERR_INVALID_ARG;
   if (a->M < 0 || a->N < 0 || a->K < 0) return EPILORA_ERR_INVALID_ARG;
+  if (a->amode != EPILORA_ACT_FP8 && a->amode != EPILORA_ACT_BF16) return EPILORA_ERR_INVALID_ARG;
   if (a->M == 0 || a->N == 0) return EPILORA_OK;
-  if (a->xq == nullptr || a->sx == nullptr || a->y == nullptr) return EPILORA_ERR_INVALID_ARG;
+  const bool a16 = a->amode == EPILORA_ACT_BF16;
+  if (a->y == nullptr) return EPILORA_ERR_INVALID_ARG;
   int st = check_weights(a);
   if (st != EPILORA_OK) return st;
-  if (a->ldq < a->K || a->ldy < a->N) return EPILORA_ERR_INVALID_ARG;
-  if (a->ldq % 16 != 0 || !aligned(a->xq, 16) || !aligned(a->sx, 4) || !aligned(a->y, 2))
-    return EPILORA_ERR_UNSUPPORTED;
+  if (a16) {  // the W8A16 GEMM reads the bf16 rows
+    if (a->x == nullptr) return EPILORA_ERR_INVALID_ARG;
+    if (a->ldx < a->K || a->ldy < a->N) return EPILORA_ERR_INVALID_ARG;
+    if (a->wfmt != EPILORA_W_FP8 || a->ldx % 16 != 0 || !aligned(a->x, 16) || !aligned(a->y, 2))
+      return EPILORA_ERR_UNSUPPORTED;
+  } else {
+    if (a->xq == nullptr || a->sx == nullptr) return EPILORA_ERR_INVALID_ARG;
+    if (a->ldq < a->K || a->ldy < a->N) return EPILORA_ERR_INVALID_ARG;
+    if (a->ldq % 16 != 0 || !aligned(a->xq, 16) || !aligned(a->sx, 4) || !aligned(a->y, 2))
+      return EPILORA_ERR_UNSUPPORTED;
+  }
   const bool lora = a->z != nullptr;
   if (lora) {
     st = check_adapters(a->L, a->r, a->A, false, a->B, true, a->ranks, a->idx);
@@ -345,8 +358,9 @@ int epilora_gemm_lora(const epilora_layer_args* a, void* stream) {
     st = check_ws(a->ws, a->ws_bytes, kCtrlBytes);
     if (st != EPILORA_OK) return st;
   }
-  return hip_status(launch_gemm_lora(a->xq, a->sx, a->ldq, a->M, a->N, a->K, weights_of(a), adapters_of(a, lora),
-                                     a->z, a->y, a->ldy, a->ws, as_stream(stream)));
+  return hip_status(launch_gemm_lora(a->xq, a->sx, a->ldq, a16 ? a->x : nullptr, a->ldx, a->M, a->N, a->K,
+                                     weights_of(a), adapters_of(a, lora), a->z, a->y, a->ldy, a->ws,
+                                     as_stream(stream)));
 }
 
 int epilora_lora_expand_add_ex(const float* z, int64_t M, int64_t N, const void* B, int32_t afmt, const float* sb,
@@ -389,7 +403,8 @@ int epilora_decode_lora(const epilora_layer_args* a, void* stream) {
   const int st = check_ws(a->ws, a->ws_bytes, decode_need(a, r));
   if (st != EPILORA_OK) return st;
   return hip_status(launch_decode_lora(a->x, a->ldx, a->M, a->N, a->K, weights_of(a), adapters_of(a, a->idx != nullptr),
-                                       a->y, a->ldy, a->xq_out, a->sx_out, a->ldq_out, a->ws, as_stream(stream)));
+                                       a->y, a->ldy, a->xq_out, a->sx_out, a->ldq_out, a->ws,
+                                       a->amode == EPILORA_ACT_BF16, as_stream(stream)));
 }
 
 int epilora_decode_lora_noalloc(const epilora_layer_args* a, void* stream) {
@@ -407,7 +422,8 @@ int epilora_decode_lora_noalloc(const epilora_layer_args* a, void* stream) {
   hipStream_t s = as_stream(stream);
   if (launch_fill_u32(ws, 0u, (int64_t)(kStateBytes / 4), s) != hipSuccess) return EPILORA_ERR_HIP;
   return hip_status(launch_decode_lora(a->x, a->ldx, a->M, a->N, a->K, weights_of(a), adapters_of(a, a->idx != nullptr),
-                                       a->y, a->ldy, a->xq_out, a->sx_out, a->ldq_out, ws, s));
+                                       a->y, a->ldy, a->xq_out, a->sx_out, a->ldq_out, ws,
+                                       a->amode == EPILORA_ACT_BF16, s));
 }
 
 }  // extern "C"

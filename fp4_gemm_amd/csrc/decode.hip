@@ -1,186 +1,13 @@
-// The fused small-batch (decode) path in one persistent launch.
-//
-// The method launches the down-projection first and the GEMM as its
-// programmatic dependent, which waits for the down-projection only before
-// its epilogue, so the GEMM's weight streaming overlaps it ("EpiLoRA: Fusing
-// Many LoRA Adapters into Low-Precision GEMMs for Serving and RL", Design,
-// "Multi-adapter kernels", The decode path; Background, "Programmatic
-// dependent launch").  HIP has no programmatic dependent launch, so one grid
-// plays both kernels:
-//   workgroups [0, nq)         quantize one token row each and count up the
-//                              quantized-rows flag (nq = 0 when every GEMM
-//                              workgroup quantizes the few rows into its own
-//                              LDS and the caller keeps no copy);
-//   the next tiles*splits*S    compute the shrink (bf16 x, fp32 partials,
-//                              the last split of a tile adds them in a fixed
-//                              order; one set per output slice with its own
-//                              adapter pair) and store z in place, each word as its
-//                              bitwise complement into a region that reads
-//                              zero until then;
-//   the rest                   own 16-row weight tiles: request their first
-//                              weight batch, obtain the quantized rows,
-//                              stream the weights through the matrix cores
-//                              into an LDS stash, and poll z itself (no flag)
-//                              only once all their tiles are in, before the
-//                              epilogues.
-// Data crosses workgroups only through device-coherent stores and loads
-// (sc1): z words in place, the quantized rows behind a flag that their
-// producer bumps (a relaxed agent-scope atomic) only after its stores have
-// completed, so no workgroup has to write back or invalidate its L2.  Workgroups are dispatched in index order, so the
-// producers are resident before any consumer spins; every wait is bounded by
-// a wall-clock limit and a timeout raises EPILORA_DEV_WAIT_TIMEOUT instead of
-// hanging.  The last GEMM workgroup to finish puts the flags back to zero and
-// clears z for the next call.  The quantizer, shrink and GEMM arithmetic is the same code
-// as in the separate kernels, with the same summation orders, so every output
-// is bitwise equal to the separate quant + shrink + GEMM calls.
-#include "quant_row.h"
-#include "shrink_common.h"
-#include "skinny.h"
+// The fused small-batch (decode) path: workspace layout and launch
+// parameters (the kernel and its launch shapes are in decode.h).
+#include "decode.h"
 
 namespace epilora {
 
-struct DecodeParams {
-  SkinnyJob job;  // job.g.xq / job.g.sx: where the quantized rows go; job.g.z: ws z
-  ShrinkParams s;
-  int nq, ns, tiles;
-  int count_q;  // the GEMM workgroups wait for the quantized rows
-  int flags;    // a flag is counted or z handed over: the GEMM workgroups reset / clear at the end
-  int* done;    // kDoneGroups sub-counters, kDoneStride words apart
-};
-
-template <int MB, int FMT, int NW, bool XLDS, int UB = 0, bool GEN = false>
-__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((XLDS && NW == 8 && !GEN) ? 4 : 2))) void decode_kernel(DecodeParams p) {
-  extern __shared__ __align__(16) char smem[];
-  const GemmParams& g = p.job.g;
-  int* ctrl = g.ctrl;
-  const int bid = blockIdx.x;
-
-  if (bid < p.nq) {  // ---- quantize one token row
-    const auto qr = make_rsrc(g.xq + (int64_t)bid * g.ldq, (uint32_t)g.K);
-    const auto sr = make_rsrc(g.sx + bid, 4u);
-    quant_row<NW * 64, kCoherent>(p.job.x + (int64_t)bid * p.job.ldx, g.K, qr, 0u, sr, 0u,
-                                  reinterpret_cast<uint32_t*>(smem));
-    if (p.count_q) {
-      wait_all_memory();
-      __syncthreads();
-      if (threadIdx.x == 0) atomic_add_relaxed(ctrl + kCtrlQuantDone, 1);
-    }
-    return;
-  }
-  if (bid < p.nq + p.ns) {  // ---- shrink
-    const int sb = bid - p.nq;
-    const int tile = sb % p.tiles, rest = sb / p.tiles;
-    const int split = rest % p.s.splits, slice = rest / p.s.splits;
-    int s_begin, s_end;
-    shrink_range(p.s, split, s_begin, s_end);
-    float* red = reinterpret_cast<float*>(smem);
-    const uint64_t active =
-        shrink_tile<NW, GEN>(p.s, (int64_t)tile * kShrinkTokens, slice, s_begin, s_end, red, split == 0 && slice == 0);
-    shrink_finish<NW, kShrinkTokens, GEN>(p.s, tile, slice, split, red, active);
-    return;
-  }
-
-  // ---- GEMM workgroup (persistent over its tiles)
-  {
-    Skinny<MB, FMT, NW, XLDS, true, UB, GEN> sk(p.job, smem, bid - p.nq - p.ns);
-    sk.run();
-  }
-  if (!p.flags) return;
-  // Every flag and z read of this workgroup is behind it: count it done.
-  // The last of each group counts the group, and the last group puts the
-  // flags back to zero and clears z; each counter is reset by the one that
-  // completed it.
-  int* last = reinterpret_cast<int*>(smem);
-  __syncthreads();
-  if (threadIdx.x == 0) *last = 0;
-  if (threadIdx.x == 0) {
-    const int gi = bid - p.nq - p.ns;
-    const int ng = (int)gridDim.x - p.nq - p.ns;
-    const int groups = ng < kDoneGroups ? ng : kDoneGroups;
-    const int grp = gi % groups;
-    const int members = ng / groups + (grp < ng % groups ? 1 : 0);
-    int* sub = p.done + grp * kDoneStride;
-    if (atomic_add_relaxed(sub, 1) == members - 1) {
-      store_relaxed(sub, 0);
-      if (atomic_add_relaxed(ctrl + kCtrlGemmDone, 1) == groups - 1) {
-        store_relaxed(ctrl + kCtrlQuantDone, 0);
-        store_relaxed(ctrl + kCtrlGemmDone, 0);
-        *last = 1;
-      }
-    }
-  }
-  __syncthreads();
-  if (*last != 0 && p.ns > 0) {
-    const int n = (int)(g.M * p.s.ad.zld);
-    const auto zr = make_rsrc(g.z, (uint32_t)(n * 4));
-    for (int e = 4 * threadIdx.x; e < n; e += 4 * NW * 64) buf_store16<kCoherent>(zr, 4u * e, make_uint4(0u, 0u, 0u, 0u));
-  }
-}
-
-template <int MB, int FMT, int NW, bool XLDS, int UB, bool GEN>
-static void launch_decode_u(DecodeParams& p, bool want_xq, hipStream_t stream) {
-  const GemmParams& g = p.job.g;
-  const int r = p.s.ad.r;
-  p.nq = (XLDS && !want_xq) ? 0 : (int)g.M;
-  p.job.qtarget = (int)g.M;
-  p.count_q = XLDS ? 0 : 1;
-  p.flags = p.count_q || p.ns > 0;
-  size_t lds = skinny_lds(g.M, g.K, MB, NW, r, true, XLDS, FMT);
-  const size_t shrink_lds = (size_t)kShrinkWaves * 16 * r * sizeof(float);
-  if (shrink_lds > lds) lds = shrink_lds;
-  // The quantizing and shrink workgroups are dispatched first and hold their
-  // slots only until they finish.
-  p.job.gwgs = skinny_groups(g.N, resident_groups(decode_kernel<MB, FMT, NW, XLDS, UB, GEN>, NW * 64, lds), StashCfg<MB>::n);
-  const unsigned grid = (unsigned)(p.nq + p.ns + p.job.gwgs);
-  hipLaunchKernelGGL((decode_kernel<MB, FMT, NW, XLDS, UB, GEN>), dim3(grid), dim3(NW * 64), lds, stream, p);
-}
-
-// Single-token-block eight-wave grids over short K and at most 512 tiles
-// (the Llama-8B qkv and o projections) stream faster in single-step batches;
-// longer streams (gate_up, down) in two-step batches, as measured.
-template <int MB, int FMT, int NW, bool XLDS>
-static void launch_decode_x(DecodeParams& p, bool want_xq, hipStream_t stream) {
-  const GemmParams& g = p.job.g;
-  // the general adapters (slices, FP8 storage) in a kernel of their own
-  if (g.ad.idx != nullptr && (g.ad.S > 1 || g.ad.afmt != 0)) {
-    launch_decode_u<MB, FMT, NW, XLDS, 0, true>(p, want_xq, stream);
-    return;
-  }
-  if (MB == 1 && NW == 8 && g.K <= 4096 && cdiv(g.N, 16) <= 512)
-    launch_decode_u<MB, FMT, NW, XLDS, 1, false>(p, want_xq, stream);
-  else
-    launch_decode_u<MB, FMT, NW, XLDS, 0, false>(p, want_xq, stream);
-}
-
-template <int MB, int FMT>
-static void launch_decode_nw(DecodeParams& p, bool want_xq, hipStream_t stream) {
-  const GemmParams& g = p.job.g;
-  // Eight-wave workgroups for up to 32 tokens whatever N (each tile's K then
-  // splits over eight waves, and a workgroup takes more, shorter tiles): the
-  // fused Llama-8B gate_up projection measured 2 us faster per launch than
-  // with four-wave workgroups, which the unfused skinny kernel keeps for
-  // large N.
-  if (MB <= 2) {
-    if (skinny_x_in_lds(g.M, g.K, MB, 8, p.s.ad.r, true, FMT)) launch_decode_x<MB, FMT, 8, true>(p, want_xq, stream);
-    else launch_decode_x<MB, FMT, 8, false>(p, want_xq, stream);
-  } else {
-    if (skinny_x_in_lds(g.M, g.K, MB, 4, p.s.ad.r, true, FMT)) launch_decode_x<MB, FMT, 4, true>(p, want_xq, stream);
-    else launch_decode_x<MB, FMT, 4, false>(p, want_xq, stream);
-  }
-}
-
-template <int FMT>
-static void dispatch_decode(DecodeParams& p, bool want_xq, hipStream_t stream) {
-  const int64_t M = p.job.g.M;
-  if (M <= 16) launch_decode_nw<1, FMT>(p, want_xq, stream);
-  else if (M <= 32) launch_decode_nw<2, FMT>(p, want_xq, stream);
-  else if (M <= 48) launch_decode_nw<3, FMT>(p, want_xq, stream);
-  else launch_decode_nw<4, FMT>(p, want_xq, stream);
-}
-
 hipError_t launch_decode_lora(const uint16_t* x, int64_t ldx, int64_t M, int64_t N, int64_t K,
                               const WeightArgs& wt, const AdapterArgs& ad, uint16_t* y, int64_t ldy,
-                              uint8_t* xq_out, float* sx_out, int64_t ldq_out, void* ws, hipStream_t stream) {
+                              uint8_t* xq_out, float* sx_out, int64_t ldq_out, void* ws, bool x16,
+                              hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   char* wsb = reinterpret_cast<char*>(ws);
   const DecodeWs lay = decode_ws(M, K, ad.r, ad.S);
@@ -192,6 +19,8 @@ hipError_t launch_decode_lora(const uint16_t* x, int64_t ldx, int64_t M, int64_t
   g.ldq = xq_out != nullptr ? ldq_out : K;
   g.sx = sx_out != nullptr ? sx_out : reinterpret_cast<float*>(wsb + lay.sx);
   g.M = M; g.N = N; g.K = K;
+  g.x16 = x16 ? x : nullptr;
+  g.ldx16 = ldx;
   g.wt = wt; g.ad = ad;
   const bool adapters = ad.idx != nullptr;
   g.z = adapters ? reinterpret_cast<float*>(wsb + kZOffset) : nullptr;
@@ -214,8 +43,9 @@ hipError_t launch_decode_lora(const uint16_t* x, int64_t ldx, int64_t M, int64_t
   p.tiles = (int)cdiv(M, kShrinkTokens);
   p.ns = adapters ? p.tiles * s.splits * ad.S : 0;
   const bool want_xq = xq_out != nullptr || sx_out != nullptr;
-  if (wt.fmt == EPILORA_W_FP8) dispatch_decode<EPILORA_W_FP8>(p, want_xq, stream);
-  else dispatch_decode<EPILORA_W_FP4>(p, want_xq, stream);
+  if (x16) decode_dispatch_a16(p, want_xq, stream);
+  else if (wt.fmt == EPILORA_W_FP8) decode_dispatch_fp8(p, want_xq, stream);
+  else decode_dispatch_fp4(p, want_xq, stream);
   return hipGetLastError();
 }
 

@@ -269,7 +269,7 @@ static void launch_big(const GemmParams& p, hipStream_t stream) {
 bool gemm_big_fits(const GemmParams& p) {
   // Base only, and at least two full rounds of workgroups over the 256
   // compute units, so that a partial last round costs little.
-  return p.z == nullptr && cdiv(p.M, kBM) * cdiv(p.N, kBN) >= 512;
+  return p.z == nullptr && p.x16 == nullptr && cdiv(p.M, kBM) * cdiv(p.N, kBN) >= 512;
 }
 
 void launch_gemm_big(const GemmParams& p, hipStream_t stream) {

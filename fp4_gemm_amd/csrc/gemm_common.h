@@ -11,6 +11,8 @@ struct GemmParams {
   const uint8_t* xq;
   const float* sx;
   int64_t ldq;
+  const uint16_t* x16;  // the W8A16 GEMM: bf16 activations [M][ldx16] (xq, sx unused)
+  int64_t ldx16;
   int64_t M, N, K;
   WeightArgs wt;
   AdapterArgs ad;

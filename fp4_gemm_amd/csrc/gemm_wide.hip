@@ -40,9 +40,18 @@ __device__ __forceinline__ int swz8(int row, int chunk) { return row * 128 + ((c
 
 }  // namespace
 
-template <int FMT, int BM, int BN>
+// A16: the matched W8A16 GEMM ("EpiLoRA ...", Design, "LoRA RL on the same
+// base"): the activations stay bf16 (p.x16).  A K step then covers 64
+// elements: 128-byte bf16 activation rows and 64-byte FP8 weight rows (the
+// first four chunks of the same swizzled 128-byte LDS rows).  Lane l takes
+// the 8 activations of chunk 4h + l/16 and the 8 weights at the same K
+// positions for the bf16 MFMA of half h, widening the weights to bf16
+// exactly; the accumulators take no activation scale.
+template <int FMT, int BM, int BN, bool A16 = false>
 __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(BM == 128 ? 2 : 1))) void gemm_wide_kernel(GemmParams p, int tiles_m, int tiles_n) {
   constexpr int WM = BM / 2, WN = BN / 2, TM = WM / 16, TN = WN / 16;
+  static_assert(!A16 || FMT == EPILORA_W_FP8, "W8A16 takes FP8 weights");
+  constexpr int KE = A16 ? 64 : kStep;  // K elements per step
   // Two operand buffers as distinct objects, so that the compiler sees that
   // the loads filling one never alias the reads of the other (and does not
   // wait for them before those reads).  Each holds A ([BM][128]) then B
@@ -85,18 +94,24 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(BM
   // offset.  4-bit weights go through registers and the fold.
   const int rows_a = (int)(p.M - m0 < BM ? p.M - m0 : BM);
   const int rows_b = (int)(p.N - n0 < BN ? p.N - n0 : BN);
-  const auto rA = make_rsrc(p.xq + m0 * p.ldq, (uint32_t)((rows_a - 1) * p.ldq + K));
+  const int64_t lda = A16 ? p.ldx16 * 2 : p.ldq;  // bytes
+  const auto rA = A16 ? make_rsrc(p.x16 + m0 * p.ldx16, (uint32_t)(((rows_a - 1) * p.ldx16 + K) * 2))
+                      : make_rsrc(p.xq + m0 * p.ldq, (uint32_t)((rows_a - 1) * p.ldq + K));
   const auto rB = make_rsrc(p.wt.w + n0 * (FMT == EPILORA_W_FP8 ? K : K / 2),
                             (uint32_t)(rows_b * (FMT == EPILORA_W_FP8 ? K : K / 2)));
   const auto rS = make_rsrc(FMT == EPILORA_W_FP4 ? p.wt.bs + n0 * (K / 16) : p.wt.w,
                             FMT == EPILORA_W_FP4 ? (uint32_t)(rows_b * (K / 16)) : 0u);
   const int dma_row = lane >> 3, dma_chunk = (lane & 7) ^ (lane >> 3);
-  auto dma = [&](__amdgpu_buffer_rsrc_t rsrc, int64_t ld, int per_wave, uint8_t* dst, int kt) {
-    const uint32_t k = (uint32_t)kt * kStep + 16u * dma_chunk;
+  // step_bytes: bytes of a row per K step; row_bytes: bytes of a whole row
+  // (chunks at or past it read as zero).
+  auto dma = [&](__amdgpu_buffer_rsrc_t rsrc, int64_t ld, int per_wave, uint8_t* dst, int kt, uint32_t step_bytes,
+                 int64_t row_bytes) {
+    const uint32_t k = (uint32_t)kt * step_bytes + 16u * dma_chunk;
+    const bool in = 16u * dma_chunk < step_bytes && (int64_t)k < row_bytes;
 #pragma unroll
     for (int q = 0; q < per_wave; ++q) {
       const int j = wave * per_wave + q;
-      const uint32_t off = (int64_t)k < K ? (uint32_t)((8 * j + dma_row) * ld) + k : kOutOfRange;
+      const uint32_t off = in ? (uint32_t)((8 * j + dma_row) * ld) + k : kOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(dst + j * 1024), 16,
                                                off, 0, 0, 0);
     }
@@ -128,8 +143,8 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(BM
     }
   };
   auto stage = [&](int kt, uint8_t* buf) {  // request step kt's operands into buf
-    dma(rA, p.ldq, BM / 32, buf, kt);
-    if (FMT == EPILORA_W_FP8) dma(rB, K, BN / 32, buf + BM * kStep, kt);
+    dma(rA, lda, BM / 32, buf, kt, kStep, A16 ? 2 * K : K);
+    if (FMT == EPILORA_W_FP8) dma(rB, K, BN / 32, buf + BM * kStep, kt, KE, K);
     else load_b4(kt);
   };
   f32x4 acc[TM][TN];
@@ -162,24 +177,40 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(BM
   const uint32_t tt0 = tid < BM ? (uint32_t)tid : 0u;
   const int pre_a = (int)buf_load4<kCached>(rI, 4u * tt0);
   const int pre_m = (int)__builtin_amdgcn_raw_buffer_load_b8(rM, tt0, 0, 0);
-  const int nk = (int)cdiv(K, kStep);
+  const int nk = (int)cdiv(K, KE);
   const int nk2 = nk + (nk & 1);
   i32x8 af[TM], bf[TN];
+  // A fragment of a row: FP8, 32 codes (chunks c0, c0 + 1); W8A16, the 8
+  // bf16 of chunk g = l / 16 (half 0) and of chunk 4 + g (half 1).
+  auto frag_a = [&](const uint8_t* a, int row) {
+    if (A16)
+      return as_i32x8(*reinterpret_cast<const uint4*>(a + swz8(row, lane >> 4)),
+                      *reinterpret_cast<const uint4*>(a + swz8(row, 4 + (lane >> 4))));
+    return as_i32x8(*reinterpret_cast<const uint4*>(a + swz8(row, c0)),
+                    *reinterpret_cast<const uint4*>(a + swz8(row, c0 + 1)));
+  };
+  // B fragment: FP8, 32 codes; W8A16, the 8 codes at the A fragment's K
+  // positions of each half (bytes 32 h + 8 g), raw in dwords 0..3.
+  auto frag_b = [&](const uint8_t* b, int row) {
+    if (A16) {
+      const int g = lane >> 4;
+      const uint2 h0 = *reinterpret_cast<const uint2*>(b + swz8(row, g >> 1) + 8 * (g & 1));
+      const uint2 h1 = *reinterpret_cast<const uint2*>(b + swz8(row, 2 + (g >> 1)) + 8 * (g & 1));
+      i32x8 f;
+      f[0] = (int)h0.x; f[1] = (int)h0.y; f[2] = (int)h1.x; f[3] = (int)h1.y;
+      f[4] = f[5] = f[6] = f[7] = 0;
+      return f;
+    }
+    return as_i32x8(*reinterpret_cast<const uint4*>(b + swz8(row, c0)),
+                    *reinterpret_cast<const uint4*>(b + swz8(row, c0 + 1)));
+  };
   auto read_frags = [&](const uint8_t* buf, i32x8 (&fa)[TM], i32x8 (&fb)[TN]) {
     const uint8_t* a = buf;
     const uint8_t* b = buf + BM * kStep;
 #pragma unroll
-    for (int nb = 0; nb < TN; ++nb) {
-      const int row = wn * WN + nb * 16 + (lane & 15);
-      fb[nb] = as_i32x8(*reinterpret_cast<const uint4*>(b + swz8(row, c0)),
-                        *reinterpret_cast<const uint4*>(b + swz8(row, c0 + 1)));
-    }
+    for (int nb = 0; nb < TN; ++nb) fb[nb] = frag_b(b, wn * WN + nb * 16 + (lane & 15));
 #pragma unroll
-    for (int tb = 0; tb < TM; ++tb) {
-      const int row = wm * WM + tb * 16 + (lane & 15);
-      fa[tb] = as_i32x8(*reinterpret_cast<const uint4*>(a + swz8(row, c0)),
-                        *reinterpret_cast<const uint4*>(a + swz8(row, c0 + 1)));
-    }
+    for (int tb = 0; tb < TM; ++tb) fa[tb] = frag_a(a, wm * WM + tb * 16 + (lane & 15));
   };
   // Step k from registers, step k+1's fragments from `next` (when there is a
   // step k+1), step k+2's operands into `self` (when there is one).
@@ -193,21 +224,34 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(BM
     if (k + 2 < nk2) stage(k + 2, self);
     const uint8_t* na = next;
     const uint8_t* nbp = next + BM * kStep;
+    // W8A16: the weights of the step widened once, used by every token block
+    uint4 bw[A16 ? TN : 1][2];
+    if (A16) {
+#pragma unroll
+      for (int nb = 0; nb < TN; ++nb)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) bw[nb][h] = fp8x8_to_bf16x8((uint32_t)bf[nb][2 * h], (uint32_t)bf[nb][2 * h + 1]);
+    }
 #pragma unroll
     for (int tb = 0; tb < TM; ++tb) {
 #pragma unroll
-      for (int nb = 0; nb < TN; ++nb) acc[tb][nb] = mfma_fp8_16x16x128(af[tb], bf[nb], acc[tb][nb]);
-      const int row = wm * WM + tb * 16 + (lane & 15);
-      af[tb] = as_i32x8(*reinterpret_cast<const uint4*>(na + swz8(row, c0)),
-                        *reinterpret_cast<const uint4*>(na + swz8(row, c0 + 1)));
+      for (int nb = 0; nb < TN; ++nb) {
+        if (A16) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            acc[tb][nb] = mfma_bf16_16x16x32(
+                __builtin_bit_cast(bf16x8, u32x4{(uint32_t)af[tb][4 * h], (uint32_t)af[tb][4 * h + 1],
+                                                 (uint32_t)af[tb][4 * h + 2], (uint32_t)af[tb][4 * h + 3]}),
+                as_bf16x8(bw[nb][h]), acc[tb][nb]);
+        } else {
+          acc[tb][nb] = mfma_fp8_16x16x128(af[tb], bf[nb], acc[tb][nb]);
+        }
+      }
+      af[tb] = frag_a(na, wm * WM + tb * 16 + (lane & 15));
     }
     i32x8 bn[TN];
 #pragma unroll
-    for (int nb = 0; nb < TN; ++nb) {
-      const int row = wn * WN + nb * 16 + (lane & 15);
-      bn[nb] = as_i32x8(*reinterpret_cast<const uint4*>(nbp + swz8(row, c0)),
-                        *reinterpret_cast<const uint4*>(nbp + swz8(row, c0 + 1)));
-    }
+    for (int nb = 0; nb < TN; ++nb) bn[nb] = frag_b(nbp, wn * WN + nb * 16 + (lane & 15));
 #pragma unroll
     for (int nb = 0; nb < TN; ++nb) bf[nb] = bn[nb];
     if (FMT == EPILORA_W_FP4 && k + 2 < nk2) store_b4(self + BM * kStep);
@@ -215,7 +259,7 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(BM
 
   // The tile's scales, requested now and put in LDS with the first operands.
   float pre_xs = 0.f, pre_ws = 0.f;
-  if (tid < BM && m0 + tid < p.M) pre_xs = p.sx[m0 + tid];
+  if (tid < BM && m0 + tid < p.M) pre_xs = A16 ? 1.0f : p.sx[m0 + tid];
   if (tid < BN && n0 + tid < p.N) pre_ws = weight_scale<FMT>(p.wt, n0 + tid);
   stage(0, buf0);
   if (FMT == EPILORA_W_FP4) {
@@ -500,10 +544,10 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(BM
   }
 }
 
-template <int FMT, int BM, int BN>
+template <int FMT, int BM, int BN, bool A16 = false>
 static void launch_wide(const GemmParams& p, hipStream_t stream) {
   const int tm = (int)cdiv(p.M, BM), tn = (int)cdiv(p.N, BN);
-  hipLaunchKernelGGL((gemm_wide_kernel<FMT, BM, BN>), dim3(tm * tn), dim3(kWideThreads), 0, stream, p, tm, tn);
+  hipLaunchKernelGGL((gemm_wide_kernel<FMT, BM, BN, A16>), dim3(tm * tn), dim3(kWideThreads), 0, stream, p, tm, tn);
 }
 
 // Tile shape: the largest tile that still gives every compute unit a tile
@@ -519,6 +563,10 @@ static void dispatch_wide(const GemmParams& p, hipStream_t stream) {
 }
 
 void launch_gemm_wide(const GemmParams& p, hipStream_t stream) {
+  if (p.x16 != nullptr) {  // the W8A16 GEMM: 128 x 128 tiles
+    launch_wide<EPILORA_W_FP8, 128, 128, true>(p, stream);
+    return;
+  }
   if (gemm_big_fits(p)) {
     launch_gemm_big(p, stream);
     return;

@@ -65,10 +65,12 @@ hipError_t launch_shrink(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, c
 hipError_t launch_expand_add(const float* z, int64_t M, int64_t N, const AdapterArgs& ad, uint16_t* y,
                              int64_t ldy, void* ws, hipStream_t stream);
 
-// The GEMM with the multi-adapter epilogue.  z == null: base only.
-hipError_t launch_gemm_lora(const uint8_t* xq, const float* sx, int64_t ldq, int64_t M, int64_t N,
-                            int64_t K, const WeightArgs& wt, const AdapterArgs& ad, const float* z,
-                            uint16_t* y, int64_t ldy, void* ws, hipStream_t stream);
+// The GEMM with the multi-adapter epilogue.  z == null: base only.  x16
+// non-null: the matched W8A16 GEMM on bf16 activations [M][ldx16] (xq, sx
+// unused; FP8 weights).
+hipError_t launch_gemm_lora(const uint8_t* xq, const float* sx, int64_t ldq, const uint16_t* x16, int64_t ldx16,
+                            int64_t M, int64_t N, int64_t K, const WeightArgs& wt, const AdapterArgs& ad,
+                            const float* z, uint16_t* y, int64_t ldy, void* ws, hipStream_t stream);
 
 // The RMS normalization with the quantizer and (when ad.idx is set) the
 // shrink from its output.
@@ -77,9 +79,10 @@ hipError_t launch_norm_quant_shrink(const uint16_t* x, int64_t M, int64_t K, int
                                     const AdapterArgs& ad, float* z, void* ws, hipStream_t stream);
 
 // The fused decode path.
+// x16: the matched W8A16 GEMM (x stays bf16; xq_out / sx_out unused).
 hipError_t launch_decode_lora(const uint16_t* x, int64_t ldx, int64_t M, int64_t N, int64_t K,
                               const WeightArgs& wt, const AdapterArgs& ad, uint16_t* y, int64_t ldy,
-                              uint8_t* xq_out, float* sx_out, int64_t ldq_out, void* ws,
+                              uint8_t* xq_out, float* sx_out, int64_t ldq_out, void* ws, bool x16,
                               hipStream_t stream);
 
 }  // namespace epilora

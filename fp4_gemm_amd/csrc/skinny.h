@@ -97,10 +97,12 @@ struct SkinnyJob {
   int64_t wait_ticks;
 };
 
-template <int MB, int U>
+// XV 16-byte vectors of activations per lane and step: 2 (32 FP8 codes) or
+// 4 (32 bf16 values, the W8A16 GEMM).
+template <int MB, int U, int XV>
 struct SkinnyBatch {
   u32x4 wa[U], wb[U];        // FP8: 32 bytes; 4-bit: wa = 32 codes, wb.x = two block scales
-  u32x4 xa[U][MB], xb[U][MB];
+  u32x4 xv[U][MB][XV];
 };
 
 // Thread 0 polls *flag (device-coherent loads, s_sleep between them) until it
@@ -229,17 +231,65 @@ struct SelfQuant {
   }
 };
 
+// The W8A16 GEMM's fused kernel keeps the few bf16 rows of x in LDS as they
+// are (no quantization): the loads are requested before the weights, as in
+// SelfQuant, and stored once they are in.  Row scales read 1.
+template <int NT, int RV>
+struct SelfCopy {
+  uint4 v[RV];
+
+  __device__ __forceinline__ void issue(const uint16_t* __restrict__ x, int64_t ldx, int M, int64_t K) {
+    const int nv = (int)(K / 8);
+#pragma unroll
+    for (int i = 0; i < RV; ++i) {
+      const int j = threadIdx.x + i * NT;
+      if (j < M * nv) {
+        const int t = j / nv;
+        v[i] = *reinterpret_cast<const uint4*>(x + t * ldx + 8 * (j - t * nv));
+      }
+    }
+  }
+
+  // Ends with a barrier.
+  __device__ __forceinline__ void finish(const uint16_t* __restrict__ x, int64_t ldx, int M, int64_t K, uint8_t* xs,
+                                         float* sxs) const {
+    const int nv = (int)(K / 8);
+    const int total = M * nv;
+#pragma unroll
+    for (int i = 0; i < RV; ++i) {
+      const int j = threadIdx.x + i * NT;
+      if (j < total) *reinterpret_cast<uint4*>(xs + 16 * j) = v[i];
+    }
+    for (int j = threadIdx.x + RV * NT; j < total; j += NT) {
+      const int t = j / nv;
+      *reinterpret_cast<uint4*>(xs + 16 * j) = *reinterpret_cast<const uint4*>(x + t * ldx + 8 * (j - t * nv));
+    }
+    for (int t = threadIdx.x; t < M; t += NT) sxs[t] = 1.0f;
+    __syncthreads();
+  }
+};
+
 // UB (> 0) overrides the steps per load batch.  GEN: the general adapters
 // (several output slices, FP8 storage) may occur; without it the epilogue
 // assumes one slice of bf16 adapters and carries none of that code, which
-// keeps the registers of the weight stream free.
-template <int MB, int FMT, int NW, bool XLDS, bool FUSED, int UB = 0, bool GEN = true>
+// keeps the registers of the weight stream free.  A16: the matched W8A16
+// GEMM ("EpiLoRA ...", Design, "LoRA RL on the same base"): the activations
+// stay bf16 (p.x16), each FP8 weight is widened to bf16 exactly in
+// registers, the products run on bf16 matrix cores (four 16x16x32 steps per
+// 128-wide K step, lane l taking the same 8 K positions of its 32 in both
+// operands) and the accumulators take no activation scale (it reads 1).
+template <int MB, int FMT, int NW, bool XLDS, bool FUSED, int UB = 0, bool GEN = true, bool A16 = false>
 struct Skinny {
   // The fused kernel's 8-wave workgroups take half batches so that two fit
   // on a compute unit (four waves per SIMD), beside a producer workgroup.
   static constexpr int U = UB > 0 ? UB : ((FUSED && NW == 8 && MB == 1) ? 2 : SkinnyCfg<MB>::U);
   static constexpr int T = MB * 16;
-  static constexpr int XPOL = FUSED ? kCoherent : kCached;
+  // Activations from other workgroups of a fused grid are read coherently;
+  // the W8A16 GEMM reads the caller's bf16 rows, which no workgroup writes.
+  static constexpr int XPOL = (FUSED && !A16) ? kCoherent : kCached;
+  static constexpr int XB = A16 ? 2 : 1;   // bytes per activation element
+  static constexpr int XV = A16 ? 4 : 2;   // 16-byte activation vectors per lane and step
+  static_assert(!A16 || FMT == EPILORA_W_FP8, "W8A16 takes FP8 weights");
 
   const SkinnyJob& J;
   const GemmParams& p;
@@ -260,7 +310,7 @@ struct Skinny {
 
   __device__ __forceinline__ Skinny(const SkinnyJob& j, char* lds, int gidx) : J(j), p(j.g), g(gidx) {
     const int64_t M = p.M, K = p.K;
-    L = sk_layout(MB, NW, p.ad.r, XLDS ? (uint32_t)(M * K) : 0u, FUSED ? StashCfg<MB>::n : 0, FMT);
+    L = sk_layout(MB, NW, p.ad.r, XLDS ? (uint32_t)(M * K * XB) : 0u, FUSED ? StashCfg<MB>::n : 0, FMT);
     part = reinterpret_cast<float*>(lds + L.part);
     red = reinterpret_cast<float*>(lds + L.red);
     tbl = reinterpret_cast<uint2*>(lds + L.tbl);
@@ -288,11 +338,11 @@ struct Skinny {
     total = mine * nb;
     adapters = p.z != nullptr;
     gscale = FMT == EPILORA_W_FP4 ? weight_scale<FMT>(p.wt, 0) : 0.f;
-    xr = make_rsrc(p.xq, (uint32_t)((M - 1) * p.ldq + K));
+    xr = A16 ? make_rsrc(p.x16, (uint32_t)(((M - 1) * p.ldx16 + K) * 2)) : make_rsrc(p.xq, (uint32_t)((M - 1) * p.ldq + K));
 #pragma unroll
-    for (int mb = 0; mb < MB; ++mb) {
+    for (int mb = 0; mb < MB; ++mb) {  // byte offsets of the token rows (in LDS or in memory)
       const int64_t t = mb * 16 + row;
-      xbase[mb] = t < M ? (uint32_t)(t * (XLDS ? K : p.ldq)) : kOutOfRange;
+      xbase[mb] = t < M ? (uint32_t)(t * (XLDS ? K : (A16 ? p.ldx16 : p.ldq)) * XB) : kOutOfRange;
     }
   }
 
@@ -302,7 +352,7 @@ struct Skinny {
   __device__ __forceinline__ int slice(int64_t n) const { return GEN ? slice_of(p.ad, n) : 0; }
 
   // ---- loads ----------------------------------------------------------------
-  __device__ __forceinline__ void load_w(SkinnyBatch<MB, U>& b, int j) const {
+  __device__ __forceinline__ void load_w(SkinnyBatch<MB, U, XV>& b, int j) const {
     const bool live = j < total;
     const int64_t K = p.K;
     const int64_t n0 = live ? n0_of(j) : 0;
@@ -335,7 +385,7 @@ struct Skinny {
     }
   }
 
-  __device__ __forceinline__ void load_x(SkinnyBatch<MB, U>& b, int j) const {
+  __device__ __forceinline__ void load_x(SkinnyBatch<MB, U, XV>& b, int j) const {
     if (XLDS) return;
     const int s0 = sb + (j < total ? j % nb : 0) * U;
 #pragma unroll
@@ -344,15 +394,15 @@ struct Skinny {
       const bool ok = j < total && s0 + u < se && (int64_t)k < p.K;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        const uint32_t off = ok ? xbase[mb] + k : kOutOfRange;
-        b.xa[u][mb] = bufv_load16<XPOL>(xr, off);
-        b.xb[u][mb] = bufv_load16<XPOL>(xr, off + 16);
+        const uint32_t off = ok ? xbase[mb] + k * XB : kOutOfRange;
+#pragma unroll
+        for (int v = 0; v < XV; ++v) b.xv[u][mb][v] = bufv_load16<XPOL>(xr, off + 16 * v);
       }
     }
   }
 
   // ---- multiply a batch (steps past the range were loaded as zeros) ---------
-  __device__ __forceinline__ void compute(const SkinnyBatch<MB, U>& b, int j, f32x4 (&acc)[MB]) const {
+  __device__ __forceinline__ void compute(const SkinnyBatch<MB, U, XV>& b, int j, f32x4 (&acc)[MB]) const {
     const int s0 = sb + (j < total ? j % nb : 0) * U;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
@@ -378,19 +428,36 @@ struct Skinny {
       }
       const uint32_t k = (uint32_t)(s0 + u) * 128u + kofs;
       const bool kin = s0 + u < se && (int64_t)k < p.K;
+      // W8A16: the lane's 32 FP8 weights as four groups of 8 bf16; group q
+      // meets the lane's activations at the same 8 K positions.
+      uint4 w16[4];
+      if (A16) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w16[q] = fp8x8_to_bf16x8((uint32_t)wf[2 * q], (uint32_t)wf[2 * q + 1]);
+      }
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
-        i32x8 xf;
+        u32x4 xq4[XV];
         if (XLDS) {
           const bool ok = kin && xbase[mb] != kOutOfRange;
-          const u32x4* q = reinterpret_cast<const u32x4*>(xs + (ok ? xbase[mb] + k : 0u));
+          const u32x4* q = reinterpret_cast<const u32x4*>(xs + (ok ? xbase[mb] + k * XB : 0u));
           const u32x4 zero = {0u, 0u, 0u, 0u};
-          const u32x4 q0 = q[0], q1 = q[1];
-          xf = cat8(ok ? q0 : zero, ok ? q1 : zero);
+#pragma unroll
+          for (int v = 0; v < XV; ++v) {
+            const u32x4 qv = q[v];
+            xq4[v] = ok ? qv : zero;
+          }
         } else {
-          xf = cat8(b.xa[u][mb], b.xb[u][mb]);
+#pragma unroll
+          for (int v = 0; v < XV; ++v) xq4[v] = b.xv[u][mb][v];
         }
-        acc[mb] = mfma_fp8_16x16x128(wf, xf, acc[mb]);
+        if (A16) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            acc[mb] = mfma_bf16_16x16x32(as_bf16x8(w16[q]), __builtin_bit_cast(bf16x8, xq4[q]), acc[mb]);
+        } else {
+          acc[mb] = mfma_fp8_16x16x128(wf, cat8(xq4[0], xq4[1]), acc[mb]);
+        }
       }
     }
   }
@@ -656,26 +723,32 @@ struct Skinny {
     // Activation loads first, then the first two weight batches; the set-up
     // below overlaps them.
     SelfQuant<NT, RV> sq;
-    if (XLDS && FUSED) sq.issue(J.x, J.ldx, (int)M, K);
+    SelfCopy<NT, RV> sc;
+    if (XLDS && FUSED && !A16) sq.issue(J.x, J.ldx, (int)M, K);
+    if (XLDS && FUSED && A16) sc.issue(J.x, J.ldx, (int)M, K);
     const TokenLoad tl = load_token();
     __builtin_amdgcn_sched_barrier(0);
-    SkinnyBatch<MB, U> A, B;
+    SkinnyBatch<MB, U, XV> A, B;
     load_w(A, 0);
     load_w(B, 1);
     __builtin_amdgcn_sched_barrier(0);
     if (FMT == EPILORA_W_FP4) build_fold_table(tbl);
     resolve_tokens(tl, g == 0);
     __syncthreads();  // tok[] is read below by threads of other waves
-    if (XLDS && FUSED) sq.finish(J.x, J.ldx, (int)M, K, xs, sxs, reinterpret_cast<uint32_t*>(red));
-    if (XLDS && !FUSED) {  // the skinny GEMM kernel: copy the quantized rows
-      const int64_t nv = M * K / 16;
+    if (XLDS && FUSED && !A16) sq.finish(J.x, J.ldx, (int)M, K, xs, sxs, reinterpret_cast<uint32_t*>(red));
+    if (XLDS && FUSED && A16) sc.finish(J.x, J.ldx, (int)M, K, xs, sxs);
+    if (XLDS && !FUSED) {  // the skinny GEMM kernel: copy the quantized (or bf16) rows
+      const int64_t row_bytes = K * XB;
+      const int64_t nv = M * row_bytes / 16;
+      const uint8_t* src = A16 ? reinterpret_cast<const uint8_t*>(p.x16) : p.xq;
+      const int64_t ld_bytes = A16 ? p.ldx16 * 2 : p.ldq;
       for (int64_t v = threadIdx.x; v < nv; v += NT) {
-        const int64_t t = v * 16 / K, k = v * 16 % K;
-        *reinterpret_cast<uint4*>(xs + 16 * v) = *reinterpret_cast<const uint4*>(p.xq + t * p.ldq + k);
+        const int64_t t = v * 16 / row_bytes, c = v * 16 % row_bytes;
+        *reinterpret_cast<uint4*>(xs + 16 * v) = *reinterpret_cast<const uint4*>(src + t * ld_bytes + c);
       }
     }
     if (!FUSED) {
-      for (int t = threadIdx.x; t < M; t += NT) sxs[t] = p.sx[t];
+      for (int t = threadIdx.x; t < M; t += NT) sxs[t] = A16 ? 1.0f : p.sx[t];
       if (adapters) {
         zslice = total > 0 ? slice(n0_of(0)) : 0;
         stage_z(zslice);
@@ -693,10 +766,14 @@ struct Skinny {
 #pragma unroll
     for (int s = 0; s < StashCfg<MB>::n; ++s) pw[s] = (FUSED && s < total / nb) ? row_wscale(n0_of(s * nb)) : 0.f;
 
-    if (FUSED && !XLDS) {  // the quantized rows come from other workgroups
+    if (FUSED && !XLDS && !A16) {  // the quantized rows come from other workgroups
       ok = wait_flag(J.qflag, J.qtarget, J.wait_ticks, err, p.ctrl + kCtrlForceTimeout, verdict);
       const auto sr = make_rsrc(p.sx, (uint32_t)(M * 4));
       for (int t = threadIdx.x; t < M; t += NT) sxs[t] = __uint_as_float(buf_load4<kCoherent>(sr, 4u * t));
+      __syncthreads();
+    }
+    if (FUSED && !XLDS && A16) {  // the caller's bf16 rows, read directly
+      for (int t = threadIdx.x; t < M; t += NT) sxs[t] = 1.0f;
       __syncthreads();
     }
     load_x(A, 0);
@@ -745,14 +822,15 @@ inline int skinny_groups(int64_t N, int resident, int max_rounds = 0) {
 }
 // Whether the quantized activations live in LDS (the fused kernel then
 // quantizes them itself), and the LDS bytes of the workgroup.
-inline bool skinny_x_in_lds(int64_t M, int64_t K, int MB, int NW, int r, bool fused, int fmt) {
-  if (M * K > kXInLdsMax || (fused && M > kSelfQuantMaxM)) return false;
+// xb: bytes per activation element (1 FP8, 2 bf16 for the W8A16 GEMM).
+inline bool skinny_x_in_lds(int64_t M, int64_t K, int MB, int NW, int r, bool fused, int fmt, int xb = 1) {
+  if (M * K * xb > kXInLdsMax || (fused && M > kSelfQuantMaxM)) return false;
   const int nstash = fused ? stash_tiles(MB) : 0;
-  return sk_layout(MB, NW, r, (uint32_t)(M * K), nstash, fmt).total <= kLdsBudget;
+  return sk_layout(MB, NW, r, (uint32_t)(M * K * xb), nstash, fmt).total <= kLdsBudget;
 }
-inline uint32_t skinny_lds(int64_t M, int64_t K, int MB, int NW, int r, bool fused, bool xlds, int fmt) {
+inline uint32_t skinny_lds(int64_t M, int64_t K, int MB, int NW, int r, bool fused, bool xlds, int fmt, int xb = 1) {
   const int nstash = fused ? stash_tiles(MB) : 0;
-  return sk_layout(MB, NW, r, xlds ? (uint32_t)(M * K) : 0u, nstash, fmt).total;
+  return sk_layout(MB, NW, r, xlds ? (uint32_t)(M * K * xb) : 0u, nstash, fmt).total;
 }
 
 }  // namespace epilora

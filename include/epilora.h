@@ -99,6 +99,12 @@ enum epilora_afmt {
                          output adds s * sb_n * sum_j e4m3(B_nj) z_j. */
 };
 
+/* Activation modes of the GEMM. */
+enum epilora_amode {
+  EPILORA_ACT_FP8 = 0, /* per-token FP8 activations (W8A8 / W4A8) */
+  EPILORA_ACT_BF16 = 1 /* bf16 activations: the matched W8A16 GEMM */
+};
+
 /* Operations, for epilora_workspace_bytes. */
 enum epilora_op {
   EPILORA_OP_SHRINK = 1,
@@ -172,6 +178,14 @@ typedef struct epilora_layer_args {
   int32_t afmt;
   const float* sa;
   const float* sb;
+  /* Activation mode (enum epilora_amode).  EPILORA_ACT_BF16 selects the
+     matched W8A16 GEMM: both calls read the bf16 activations x / ldx (not
+     xq / sx), the FP8 weights are widened to bf16 exactly, the products
+     accumulate in fp32 and base = acc * sw[n] ("EpiLoRA ...", Design, "LoRA
+     RL on the same base": the matched engine computes with the trainer's
+     arithmetic on the same FP8 weights).  FP8 weights only; xq_out and
+     sx_out must be NULL. */
+  int32_t amode;
 } epilora_layer_args;
 
 /* Library version (EPILORA_VERSION of the build). */

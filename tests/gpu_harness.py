@@ -54,9 +54,9 @@ class DeviceGemm:
     """One projection's inputs on the device, weights quantized by the
     library's own load-time quantizer."""
 
-    def __init__(self, g, wfmt="fp8", x=None, afmt="bf16"):
+    def __init__(self, g, wfmt="fp8", x=None, afmt="bf16", a16=False):
         lay = g.layer
-        self.g, self.wfmt, self.afmt = g, wfmt, afmt
+        self.g, self.wfmt, self.afmt, self.a16 = g, wfmt, afmt, a16
         self.M, self.K, self.N = g.M, g.K, g.N
         self.x_np = g.x() if x is None else x
         self.w_np = g.w()
@@ -115,18 +115,20 @@ class DeviceGemm:
         return z, ws
 
     def gemm(self, xq, sx, z=None, ws=None):
+        """The GEMM; xq = sx = None with a16: the W8A16 GEMM on x."""
         y = torch.empty(self.M, self.N, dtype=torch.bfloat16, device=DEV)
+        x16 = self.x if self.a16 else None
         if z is None:
-            ep.epilora_gemm_lora(xq, sx, self.wq, y, **self.wkw)
+            ep.epilora_gemm_lora(xq, sx, self.wq, y, x16=x16, **self.wkw)
         else:
             ws = ws if ws is not None else ep.new_workspace(ep.OP_GEMM, self.M, self.N, self.K, self.r)
             ep.epilora_gemm_lora(xq, sx, self.wq, y, z=z, B=self.B, idx=self.idx, ranks=self.ranks,
-                                 mask=self.mask, scale=self.scale, ws=ws, slices=self.slices, **self.bkw,
-                                 **self.wkw)
+                                 mask=self.mask, scale=self.scale, ws=ws, slices=self.slices, x16=x16,
+                                 **self.bkw, **self.wkw)
         return y
 
     def separate(self):
-        xq, sx = self.quant()
+        xq, sx = (None, None) if self.a16 else self.quant()
         z, ws = self.shrink()
         y = self.gemm(xq, sx, z, ws)
         return dict(xq=xq, sx=sx, z=z, y=y, ws=ws)
@@ -134,11 +136,12 @@ class DeviceGemm:
     def decode(self, ws=None, keep_xq=True):
         ws = ws if ws is not None else ep.new_workspace(ep.OP_DECODE, self.M, self.N, self.K, self.r * self.S)
         y = torch.empty(self.M, self.N, dtype=torch.bfloat16, device=DEV)
+        keep_xq = keep_xq and not self.a16
         xq = torch.empty(self.M, self.K, dtype=torch.uint8, device=DEV) if keep_xq else None
         sx = torch.empty(self.M, dtype=torch.float32, device=DEV) if keep_xq else None
         ep.epilora_decode_lora(self.x, self.wq, y, A=self.A, B=self.B, idx=self.idx, ranks=self.ranks,
                                mask=self.mask, scale=self.scale, ws=ws, xq_out=xq, sx_out=sx,
-                               slices=self.slices, **self.adkw, **self.wkw)
+                               slices=self.slices, a16=self.a16, **self.adkw, **self.wkw)
         return dict(xq=xq, sx=sx, y=y, ws=ws)
 
     # -- the oracle on the same inputs ----------------------------------------
@@ -161,6 +164,8 @@ class DeviceGemm:
             assert np.array_equal(to_np(self.A), A_or) and np.array_equal(to_np(self.sa), sa), "adapter codes"
             assert np.array_equal(to_np(self.B), B_full) and np.array_equal(to_np(self.sb), sb), "adapter codes"
             akw = dict(sa=sa, sb=sb)
+        if self.a16:
+            akw["a16"] = True
         if self.slices:
             out = oracle.linear_lora_sliced(self.x_np, A_or, B_full, lay.idx, lay.scale, self.slices,
                                             ranks=lay.ranks, mask=lay.mask, rows=rows, cols=cols,

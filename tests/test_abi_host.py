@@ -49,7 +49,7 @@ def test_version_and_strerror(L):
 def test_layer_args_layout_matches_header():
     # 3 sizes, x+ldx, xq+sx+ldq, wfmt(+pad), 4 weight ptrs, L+r, 6 ptrs, scale(+pad),
     # y+ldy, xq_out+sx_out+ldq_out, ws+ws_bytes
-    assert ctypes.sizeof(ep.LayerArgs) == 8 * 3 + 16 + 24 + 8 + 32 + 8 + 48 + 8 + 16 + 24 + 16 + 8 + 32 + 24
+    assert ctypes.sizeof(ep.LayerArgs) == 8 * 3 + 16 + 24 + 8 + 32 + 8 + 48 + 8 + 16 + 24 + 16 + 8 + 32 + 24 + 8
     assert ep.LayerArgs.slice_n.offset == 8 * 3 + 16 + 24 + 8 + 32 + 8 + 48 + 8 + 16 + 24 + 16 + 8
     assert ep.LayerArgs.scale.offset == 8 * 3 + 16 + 24 + 8 + 32 + 8 + 48
 
@@ -224,3 +224,14 @@ def test_norm_validation(L):
     assert n(*args(xn=P, ldn=100)) == ep.ERR_INVALID_ARG
     assert n(*args(A=P, L=4, idx=P, z=P)) == ep.ERR_WORKSPACE          # the shrink needs a workspace
     assert n(*args(A=P, L=4, idx=P, z=None, ws=P, wsb=1 << 20)) == ep.ERR_INVALID_ARG
+
+
+def test_w8a16_validation(L):
+    g = lambda **kw: L.epilora_gemm_lora(ctypes.byref(_layer(**kw)), None)
+    assert g(amode=2) == ep.ERR_INVALID_ARG
+    assert g(amode=ep.ACT_BF16, x=None) == ep.ERR_INVALID_ARG
+    assert g(amode=ep.ACT_BF16, wfmt=ep.W_FP4, bs=P, gs=P) == ep.ERR_UNSUPPORTED   # FP8 weights only
+    assert g(amode=ep.ACT_BF16, xq=None, sx=None, M=0) == ep.OK
+    d = lambda **kw: L.epilora_decode_lora(ctypes.byref(_layer(**kw)), None)
+    assert d(amode=ep.ACT_BF16, xq_out=P, ldq_out=256) == ep.ERR_INVALID_ARG     # nothing is quantized
+    assert d(amode=ep.ACT_BF16, wfmt=ep.W_FP4, bs=P, gs=P) == ep.ERR_UNSUPPORTED

@@ -181,3 +181,26 @@ def test_config5_fp8_adapters():
     starts = np.flatnonzero(np.r_[True, lay.idx[1:] != lay.idx[:-1]])
     rows = np.unique(np.concatenate([sample(d.M, 64, 57), starts]))
     check(d, out, rows=rows, seed=58, what="cfg5 fp8 adapters gate_up")
+
+
+@pytest.mark.parametrize("name", ["qkv", "down"])
+def test_config2_w8a16(name):
+    # the matched engine's GEMM on the Llama-8B decode projections
+    say(f"config 2 W8A16 {name}")
+    d = DeviceGemm(config(2).gemm(name), a16=True)
+    fused = d.decode()
+    cols = sample(d.N, 256, 24)
+    ref = d.oracle(cols=cols)
+    mx, mean = compare(to_np(fused["y"])[:, cols], ref["y"], f"cfg2 W8A16 {name}")
+    say(f"  cfg2 W8A16 {name}: max|dY|/rms {mx:.2e}  mean rel {mean:.2e}")
+
+
+def test_config5_w8a16_gate_up():
+    say("config 5 W8A16 gate_up 16 segments")
+    lay = config(5, segments=16)
+    d = DeviceGemm(lay.gemm("gate_up"), a16=True)
+    out = d.separate()
+    rows = sample(d.M, 64, 59)
+    cols = sample(d.N, 256, 60)
+    ref = d.oracle(rows=rows, cols=cols)
+    compare(to_np(out["y"])[np.ix_(rows, cols)], ref["y"], "cfg5 W8A16 gate_up")

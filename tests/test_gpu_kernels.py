@@ -596,3 +596,40 @@ def test_norm_path_equals_fused_decode():
     ref = d2.oracle(cols=np.arange(0, d.N, 7))
     from gpu_harness import compare
     compare(to_np(y)[:, np.arange(0, d.N, 7)], ref["y"], "norm path")
+
+
+# --- the matched W8A16 GEMM ----------------------------------------------------------------
+
+A16_CASES = [
+    # M, K, N, slices, L, r, idx kind, mask, ranks, adapter format
+    (1, 4096, 1024, None, 1, 64, "zero", False, False, "bf16"),
+    (4, 1024, 512, None, 4, 16, "mixed", True, True, "bf16"),
+    (24, 4096, 512, None, 6, 32, "mixed", False, False, "bf16"),
+    (64, 512, 256, (128, 128), 9, 16, "mixed", True, False, "fp8"),
+    (200, 1024, 384, None, 6, 64, "sorted", True, True, "bf16"),
+    (1100, 512, 2048, (1024, 1024), 4, 128, "sorted", False, True, "bf16"),
+    (130, 4096, 300, None, 5, 32, "mixed", False, False, "fp8"),
+]
+
+
+@pytest.mark.parametrize("M,K,N,slices,L,r,kind,use_mask,use_ranks,afmt", A16_CASES)
+def test_w8a16_vs_oracle(M, K, N, slices, L, r, kind, use_mask, use_ranks, afmt):
+    say(f"W8A16 M={M} K={K} N={N} slices={slices} L={L} r={r} {kind} adapters {afmt}")
+    rng = np.random.default_rng(9700 + M + K + N)
+    idx = _idx(kind, M, L, rng)
+    mask = rng.integers(0, 2, M).astype(np.uint8) if use_mask else None
+    ranks = rng.choice([0, 16, r // 2, r], size=L).astype(np.int32) if use_ranks else None
+    lay = custom_layer("a16", 970 + M + N, M, K, N, L, r, idx, mask=mask, ranks=ranks, slices=slices)
+    d = DeviceGemm(lay.gemms[0], afmt=afmt, a16=True)
+    sep = d.separate()
+    ref = d.oracle()
+    compare(to_np(sep["y"]), ref["y"], f"W8A16 M={M}")
+    base = to_np(d.gemm(None, None))
+    compare(base, ref["base"], "W8A16 base")
+    assert np.array_equal(to_np(sep["y"])[~ref["active"]], base[~ref["active"]])
+    if M <= ep.DECODE_MAX_M:
+        fused = d.decode()
+        assert torch.equal(fused["y"], sep["y"])
+        assert ep.epilora_device_error(fused["ws"]) == 0
+    again = d.gemm(None, None, sep["z"], sep["ws"])
+    assert torch.equal(again, sep["y"])
