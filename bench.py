@@ -42,6 +42,7 @@ from workloads import bf16_bits as workloads_bf16, config  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 FP8_PEAK_TFLOPS = 5000.0
+BF16_PEAK_TFLOPS = 2500.0
 ROTATE = 4
 DEV = "cuda"
 
@@ -61,12 +62,13 @@ def dev(a):
 
 class Proj:
     """One projection on the device: ROTATE copies of weights and adapters
-    (afmt "fp8": adapters stored as E4M3 codes with row scales)."""
+    (afmt "fp8": adapters stored as E4M3 codes with row scales; a16: the
+    matched W8A16 GEMM on the bf16 activations)."""
 
-    def __init__(self, g, wfmt="fp8", copies=ROTATE, afmt="bf16"):
+    def __init__(self, g, wfmt="fp8", copies=ROTATE, afmt="bf16", a16=False):
         lay = g.layer
         self.g, self.M, self.K, self.N, self.r = g, g.M, g.K, g.N, lay.r
-        self.afmt = afmt
+        self.afmt, self.a16 = afmt, a16
         self.slices = g.slices
         self.S = len(g.slices) if g.slices else 1
         self.wfmt = wfmt
@@ -140,12 +142,14 @@ class Proj:
     # paths ------------------------------------------------------------------
     def fused(self, c):
         w, kw = self.w[c % self.copies]
-        ep.epilora_decode_lora(self.x, w, self.y, A=self.A[c % self.copies], ws=self.ws_dec, xq_out=self.xq,
-                               sx_out=self.sx, sa=self.sa, **self.adapters(c), **kw)
+        q = {} if self.a16 else dict(xq_out=self.xq, sx_out=self.sx)
+        ep.epilora_decode_lora(self.x, w, self.y, A=self.A[c % self.copies], ws=self.ws_dec, sa=self.sa,
+                               a16=self.a16, **q, **self.adapters(c), **kw)
 
     def fused_base(self, c):
         w, kw = self.w[c % self.copies]
-        ep.epilora_decode_lora(self.x, w, self.y, ws=self.ws_dec, xq_out=self.xq, sx_out=self.sx, **kw)
+        q = {} if self.a16 else dict(xq_out=self.xq, sx_out=self.sx)
+        ep.epilora_decode_lora(self.x, w, self.y, ws=self.ws_dec, a16=self.a16, **q, **kw)
 
     def quant(self, c):
         ep.epilora_quant_act(self.x, self.xq, self.sx)
@@ -154,13 +158,18 @@ class Proj:
         ep.epilora_lora_shrink(self.x, self.A[c % self.copies], self.idx, self.z, self.ws_shr, ranks=self.ranks,
                                mask=self.mask, sa=self.sa)
 
+    def _act(self):
+        return dict(x16=self.x) if self.a16 else {}
+
     def gemm_lora(self, c):
         w, kw = self.w[c % self.copies]
-        ep.epilora_gemm_lora(self.xq, self.sx, w, self.y, z=self.z, ws=self.ws_shr, **self.adapters(c), **kw)
+        xq, sx = (None, None) if self.a16 else (self.xq, self.sx)
+        ep.epilora_gemm_lora(xq, sx, w, self.y, z=self.z, ws=self.ws_shr, **self._act(), **self.adapters(c), **kw)
 
     def gemm_base(self, c):
         w, kw = self.w[c % self.copies]
-        ep.epilora_gemm_lora(self.xq, self.sx, w, self.y, **kw)
+        xq, sx = (None, None) if self.a16 else (self.xq, self.sx)
+        ep.epilora_gemm_lora(xq, sx, w, self.y, **self._act(), **kw)
 
     def expand(self, c):
         ep.epilora_lora_expand_add(self.z, self.B[c % self.copies], self.idx, self.scale, self.y, self.ws_shr,
@@ -383,6 +392,40 @@ def sliced_rows(steps, warmup, prefill):
             "expand_ns_per_output_column": round(expand["median_us"] * 1e3 / g.N, 3)}
         del p
         torch.cuda.empty_cache()
+    return out
+
+
+def w8a16_rows(steps, warmup, prefill):
+    """The matched W8A16 GEMM (bf16 activations, FP8 weights widened in
+    registers) with the same adapter epilogue: the Llama-8B decode layer at
+    M = 1 (fused path, one rank-64 tenant; HBM-bound, beside the W8A8
+    figure) and the 2048-token prefill gate_up and down with 16 tenant
+    segments (TFLOP/s against the bf16 dense peak, 2.5 PFLOP/s, since the
+    products run on bf16 matrix cores)."""
+    out = {}
+    layer = config(2)
+    log("W8A16 decode layer ...")
+    projs = [Proj(g, a16=True) for g in layer.gemms]
+    torch.cuda.synchronize()
+    us, _ = per_step_us(projs, ["fused"], steps, warmup)
+    base_us, _ = per_step_us(projs, ["fused_base"], steps, warmup)
+    nbytes = sum(p.bytes() for p in projs)
+    out["decode_layer_m1"] = {"fused_us": round(us, 2), "base_only_us": round(base_us, 2), "bytes": nbytes,
+                              "GBps": round(nbytes / us / 1e3, 1), "hbm_frac": round(nbytes / us / 1e3 / HBM_PEAK_GBS, 4)}
+    del projs
+    torch.cuda.empty_cache()
+    if prefill:
+        for g in config(5, segments=16).gemms:
+            log(f"W8A16 prefill {g.name} ...")
+            p = Proj(g, "fp8", copies=3, a16=True)
+            p.shrink(0)
+            gemm = pct(call_samples([p], ["gemm_lora"], 10, 2, copies=3))
+            base = pct(call_samples([p], ["gemm_base"], 10, 2, copies=3))
+            tf = p.flops() / gemm["median_us"] / 1e6
+            out[f"prefill_{g.name}_16seg"] = {"gemm_us": gemm, "base_only_gemm_us": base, "gemm_tflops": round(tf, 1),
+                                              "gemm_frac_bf16_peak": round(tf / BF16_PEAK_TFLOPS, 4)}
+            del p
+            torch.cuda.empty_cache()
     return out
 
 
@@ -654,6 +697,7 @@ def main():
         mt["fp8_adapters"] = decode_multitenant(max(20, args.steps // 2), max(4, args.warmup // 2), afmt="fp8")
     sliced = sliced_rows(max(20, args.steps // 2), max(4, args.warmup // 2), not args.no_prefill)
     norm = norm_rows(max(20, args.steps // 2), max(4, args.warmup // 2))
+    a16 = w8a16_rows(max(20, args.steps // 2), max(4, args.warmup // 2), not args.no_prefill)
 
     # ---- prefill: M = 2048, tenant segments ----
     prefill = {}
@@ -738,6 +782,7 @@ def main():
         "decode_multitenant_m32": mt,
         "sliced_adapters": sliced,
         "norm_fused_shrink": norm,
+        "w8a16": a16,
         "prefill": prefill,
         "decode_72b_preft": d72,
         "cpu_baseline": cpu,

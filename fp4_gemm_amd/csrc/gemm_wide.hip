@@ -28,6 +28,7 @@
 // tokens then add s * (B z), the other rows get no add at all.  The bf16 tile
 // goes out through LDS as full 16-byte row chunks.
 #include "gemm_common.h"
+#include "occupancy.h"
 
 namespace epilora {
 
@@ -556,7 +557,7 @@ static void launch_wide(const GemmParams& p, hipStream_t stream) {
 // other's epilogue).
 template <int FMT>
 static void dispatch_wide(const GemmParams& p, hipStream_t stream) {
-  const int64_t cus = 256;
+  const int64_t cus = device_cus();
   const int64_t wide_tiles = cdiv(p.M, 256) * cdiv(p.N, 128);
   if (wide_tiles >= cus && (p.z == nullptr || wide_tiles <= cus)) launch_wide<FMT, 256, 128>(p, stream);
   else launch_wide<FMT, 128, 128>(p, stream);
