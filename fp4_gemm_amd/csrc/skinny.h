@@ -282,7 +282,9 @@ template <int MB, int FMT, int NW, bool XLDS, bool FUSED, int UB = 0, bool GEN =
 struct Skinny {
   // The fused kernel's 8-wave workgroups take half batches so that two fit
   // on a compute unit (four waves per SIMD), beside a producer workgroup.
-  static constexpr int U = UB > 0 ? UB : ((FUSED && NW == 8 && MB == 1) ? 2 : SkinnyCfg<MB>::U);
+  // (The W8A16 GEMM's activations take twice the registers: half batches.)
+  static constexpr int U0 = UB > 0 ? UB : ((FUSED && NW == 8 && MB == 1) ? 2 : SkinnyCfg<MB>::U);
+  static constexpr int U = (A16 && U0 > 1) ? U0 / 2 : U0;
   static constexpr int T = MB * 16;
   // Activations from other workgroups of a fused grid are read coherently;
   // the W8A16 GEMM reads the caller's bf16 rows, which no workgroup writes.
@@ -352,10 +354,11 @@ struct Skinny {
   __device__ __forceinline__ int slice(int64_t n) const { return GEN ? slice_of(p.ad, n) : 0; }
 
   // ---- loads ----------------------------------------------------------------
-  __device__ __forceinline__ void load_w(SkinnyBatch<MB, U, XV>& b, int j) const {
-    const bool live = j < total;
+  // Weights of step batch `batch` (U steps) of tile `tile` (the workgroup's
+  // tile index: rows (g + tile * G) * 16 ...) into wa / wb.
+  __device__ __forceinline__ void load_w_at(u32x4 (&wa)[U], u32x4 (&wb)[U], int tile, int batch, bool live) const {
     const int64_t K = p.K;
-    const int64_t n0 = live ? n0_of(j) : 0;
+    const int64_t n0 = live ? (int64_t)(g + tile * J.gwgs) * 16 : 0;
     const int64_t rows = live ? (p.N - n0 < 16 ? p.N - n0 : 16) : 0;
     const int64_t wrow = FMT == EPILORA_W_FP8 ? K : K / 2;
     const auto wr = make_rsrc(p.wt.w + n0 * wrow, (uint32_t)(rows * wrow));
@@ -368,62 +371,71 @@ struct Skinny {
     const uint32_t c16 = (uint32_t)(lane & 7) * 16u;
     const uint32_t wbase0 = r0 < rows ? (uint32_t)(r0 * wrow) + c16 : kOutOfRange;
     const uint32_t wbase1 = r0 + 8 < rows ? (uint32_t)((r0 + 8) * wrow) + c16 : kOutOfRange;
-    const int s0 = sb + (live ? j % nb : 0) * U;
+    const int s0 = sb + (live ? batch : 0) * U;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (FMT == EPILORA_W_FP8) {
         const uint32_t k = (uint32_t)(s0 + u) * 128u;
         const bool ok = s0 + u < se && (int64_t)(k + c16) < K;
-        b.wa[u] = bufv_load16<kCached>(wr, ok ? wbase0 + k : kOutOfRange);
-        b.wb[u] = bufv_load16<kCached>(wr, ok ? wbase1 + k : kOutOfRange);
+        wa[u] = bufv_load16<kCached>(wr, ok ? wbase0 + k : kOutOfRange);
+        wb[u] = bufv_load16<kCached>(wr, ok ? wbase1 + k : kOutOfRange);
       } else {
         const uint32_t k = (uint32_t)(s0 + u) * 128u + kofs;
         const bool ok = s0 + u < se && (int64_t)k < K;
-        b.wa[u] = bufv_load16<kCached>(wr, ok ? wbase + k / 2 : kOutOfRange);
-        b.wb[u] = u32x4{buf_load2<kCached>(sr, ok ? sbase + k / 16 : kOutOfRange), 0u, 0u, 0u};
+        wa[u] = bufv_load16<kCached>(wr, ok ? wbase + k / 2 : kOutOfRange);
+        wb[u] = u32x4{buf_load2<kCached>(sr, ok ? sbase + k / 16 : kOutOfRange), 0u, 0u, 0u};
       }
     }
   }
+  __device__ __forceinline__ void load_w(SkinnyBatch<MB, U, XV>& b, int j) const {
+    load_w_at(b.wa, b.wb, j < total ? j / nb : 0, j < total ? j % nb : 0, j < total);
+  }
 
-  __device__ __forceinline__ void load_x(SkinnyBatch<MB, U, XV>& b, int j) const {
+  // Activations of step batch `batch` into xv (unless they sit in LDS).
+  __device__ __forceinline__ void load_x_at(u32x4 (&xv)[U][MB][XV], int batch, bool live) const {
     if (XLDS) return;
-    const int s0 = sb + (j < total ? j % nb : 0) * U;
+    const int s0 = sb + (live ? batch : 0) * U;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const uint32_t k = (uint32_t)(s0 + u) * 128u + kofs;
-      const bool ok = j < total && s0 + u < se && (int64_t)k < p.K;
+      const bool ok = live && s0 + u < se && (int64_t)k < p.K;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const uint32_t off = ok ? xbase[mb] + k * XB : kOutOfRange;
 #pragma unroll
-        for (int v = 0; v < XV; ++v) b.xv[u][mb][v] = bufv_load16<XPOL>(xr, off + 16 * v);
+        for (int v = 0; v < XV; ++v) xv[u][mb][v] = bufv_load16<XPOL>(xr, off + 16 * v);
       }
     }
   }
+  __device__ __forceinline__ void load_x(SkinnyBatch<MB, U, XV>& b, int j) const {
+    load_x_at(b.xv, j < total ? j % nb : 0, j < total);
+  }
 
   // ---- multiply a batch (steps past the range were loaded as zeros) ---------
-  __device__ __forceinline__ void compute(const SkinnyBatch<MB, U, XV>& b, int j, f32x4 (&acc)[MB]) const {
-    const int s0 = sb + (j < total ? j % nb : 0) * U;
+  __device__ __forceinline__ void compute_at(const u32x4 (&wa)[U], const u32x4 (&wb)[U],
+                                             const u32x4 (&xv)[U][MB][XV], int batch, bool live,
+                                             f32x4 (&acc)[MB]) const {
+    const int s0 = sb + (live ? batch : 0) * U;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       i32x8 wf;
       if (FMT == EPILORA_W_FP8) {
         const int r0 = lane >> 3;
         const uint32_t pw = (uint32_t)((lane & 7) ^ (r0 & 7)) * 16u;
-        *reinterpret_cast<u32x4*>(wst + r0 * 128 + pw) = b.wa[u];
-        *reinterpret_cast<u32x4*>(wst + (r0 + 8) * 128 + pw) = b.wb[u];
+        *reinterpret_cast<u32x4*>(wst + r0 * 128 + pw) = wa[u];
+        *reinterpret_cast<u32x4*>(wst + (r0 + 8) * 128 + pw) = wb[u];
         const uint32_t p0 = (uint32_t)((2 * (lane >> 4)) ^ (row & 7)) * 16u;
         const u32x4 q0 = *reinterpret_cast<const u32x4*>(wst + row * 128 + p0);
         const u32x4 q1 = *reinterpret_cast<const u32x4*>(wst + row * 128 + (p0 ^ 16u));
         wf = cat8(q0, q1);
       } else {
-        const uint32_t sc = b.wb[u].x;
+        const uint32_t sc = wb[u].x;
         const uint2 t0 = tbl[sc & 0xFFu], t1 = tbl[(sc >> 8) & 0xFFu];
         uint32_t o[8];
-        fold8(b.wa[u].x, t0.x, t0.y, o[0], o[1]);
-        fold8(b.wa[u].y, t0.x, t0.y, o[2], o[3]);
-        fold8(b.wa[u].z, t1.x, t1.y, o[4], o[5]);
-        fold8(b.wa[u].w, t1.x, t1.y, o[6], o[7]);
+        fold8(wa[u].x, t0.x, t0.y, o[0], o[1]);
+        fold8(wa[u].y, t0.x, t0.y, o[2], o[3]);
+        fold8(wa[u].z, t1.x, t1.y, o[4], o[5]);
+        fold8(wa[u].w, t1.x, t1.y, o[6], o[7]);
         wf = i32x8{(int)o[0], (int)o[1], (int)o[2], (int)o[3], (int)o[4], (int)o[5], (int)o[6], (int)o[7]};
       }
       const uint32_t k = (uint32_t)(s0 + u) * 128u + kofs;
@@ -449,7 +461,7 @@ struct Skinny {
           }
         } else {
 #pragma unroll
-          for (int v = 0; v < XV; ++v) xq4[v] = b.xv[u][mb][v];
+          for (int v = 0; v < XV; ++v) xq4[v] = xv[u][mb][v];
         }
         if (A16) {
 #pragma unroll
@@ -460,6 +472,9 @@ struct Skinny {
         }
       }
     }
+  }
+  __device__ __forceinline__ void compute(const SkinnyBatch<MB, U, XV>& b, int j, f32x4 (&acc)[MB]) const {
+    compute_at(b.wa, b.wb, b.xv, j < total ? j % nb : 0, j < total, acc);
   }
 
   // ---- epilogue pieces --------------------------------------------------------
@@ -714,8 +729,116 @@ struct Skinny {
     }
   }
 
+  // ---- the whole job, two or more token blocks: batch-major ----------------
+  // With 17-64 tokens the activations of a step (up to 8 KB per wave) outweigh
+  // its 2 KB of weights, so reading them again for every 16-row tile made the
+  // caches, not HBM, the limit.  Here each wave takes its K batches in turn
+  // and, for each, loads its activations once into registers (double
+  // buffered across batches) and runs them against every tile of the
+  // workgroup (at most S, which the host guarantees), each tile with its own
+  // accumulators and its own weight registers: the load of a tile's next
+  // batch is issued right after its current batch is multiplied, so the
+  // weights of the other tiles stay in flight meanwhile.  Each wave still
+  // sums its own K range of a tile in step order, so the results are bitwise
+  // those of the tile-major loop; the tiles are reduced across the waves
+  // after the last batch (into the stash when fused, else straight to the
+  // outputs).
+  __device__ __forceinline__ void run_batches() {
+    constexpr int S = StashCfg<MB>::n;
+    constexpr int NT = NW * kWave;
+    const int64_t M = p.M;
+    int* err = p.ctrl != nullptr ? p.ctrl + kCtrlError : nullptr;
+    const int mine = total / nb;
+    const TokenLoad tl = load_token();
+    __builtin_amdgcn_sched_barrier(0);
+    // Every load below is issued unconditionally (a dead one gets an
+    // out-of-range offset and reads zero without touching memory), so the
+    // number of loads in flight at each multiply is known when compiling and
+    // each waits only for its own registers.
+    u32x4 wa[S][U], wb[S][U];
+#pragma unroll
+    for (int t = 0; t < S; ++t) load_w_at(wa[t], wb[t], t, 0, t < mine);
+    __builtin_amdgcn_sched_barrier(0);
+    if (FMT == EPILORA_W_FP4) build_fold_table(tbl);
+    resolve_tokens(tl, g == 0);
+    float pw[S];  // each tile's weight scale for the epilogue
+#pragma unroll
+    for (int t = 0; t < S; ++t) pw[t] = t < mine ? row_wscale(n0_of(t * nb)) : 0.f;
+    bool ok = true;
+    if (FUSED && !A16) {  // the quantized rows come from other workgroups
+      ok = wait_flag(J.qflag, J.qtarget, J.wait_ticks, err, p.ctrl + kCtrlForceTimeout, verdict);
+      const auto sr = make_rsrc(p.sx, (uint32_t)(M * 4));
+      for (int t = threadIdx.x; t < M; t += NT) sxs[t] = __uint_as_float(buf_load4<kCoherent>(sr, 4u * t));
+    } else {
+      for (int t = threadIdx.x; t < M; t += NT) sxs[t] = A16 ? 1.0f : p.sx[t];
+    }
+    __syncthreads();
+
+    f32x4 acc[S][MB];
+#pragma unroll
+    for (int t = 0; t < S; ++t)
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) acc[t][mb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 x0[U][MB][XV], x1[U][MB][XV];
+    load_x_at(x0, 0, true);
+    for (int b = 0; b < nb; b += 2) {
+      load_x_at(x1, b + 1, b + 1 < nb);
+#pragma unroll
+      for (int t = 0; t < S; ++t) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (t < mine) compute_at(wa[t], wb[t], x0, b, true, acc[t]);
+        __builtin_amdgcn_sched_barrier(0);
+        load_w_at(wa[t], wb[t], t, b + 1, t < mine && b + 1 < nb);
+      }
+      if (b + 1 >= nb) break;
+      load_x_at(x0, b + 2, b + 2 < nb);
+#pragma unroll
+      for (int t = 0; t < S; ++t) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (t < mine) compute_at(wa[t], wb[t], x1, b + 1, true, acc[t]);
+        __builtin_amdgcn_sched_barrier(0);
+        load_w_at(wa[t], wb[t], t, b + 2, t < mine && b + 2 < nb);
+      }
+    }
+
+    if (FUSED) {
+#pragma unroll
+      for (int t = 0; t < S; ++t)
+        if (t < mine) reduce_tile(acc[t], stash + t * T * 16);
+      if (ok) finish_stash(ok, pw);
+    } else {
+      uint4 pb[S];
+#pragma unroll
+      for (int t = 0; t < S; ++t)
+        if (t < mine) pb[t] = b_chunk(n0_of(t * nb), threadIdx.x >> 4);
+      if (adapters) {
+        zslice = mine > 0 ? slice(n0_of(0)) : 0;
+        stage_z(zslice);
+      }
+#pragma unroll
+      for (int t = 0; t < S; ++t) {
+        if (t < mine) {
+          reduce_tile(acc[t], red);
+          if (GEN && adapters && p.ad.S > 1) {
+            const int sl = slice(n0_of(t * nb));
+            if (sl != zslice) {
+              stage_z(sl);
+              zslice = sl;
+            }
+          }
+          outputs(n0_of(t * nb), red, true, pb[t], pw[t]);
+        }
+      }
+    }
+    if (!ok && threadIdx.x == 0 && err != nullptr) atomic_or_relaxed(err, EPILORA_DEV_WAIT_TIMEOUT);
+  }
+
   // ---- the whole job --------------------------------------------------------
   __device__ __forceinline__ void run() {
+    if constexpr (MB >= 2 && !XLDS && !A16) {  // (W8A16: too few registers for it)
+      run_batches();
+      return;
+    }
     constexpr int NT = NW * kWave;
     constexpr int RV = NW == 8 ? 4 : 8;
     const int64_t M = p.M, K = p.K;
