@@ -168,14 +168,17 @@ static void launch_decode_nw(DecodeParams& p, bool want_xq, hipStream_t stream) 
   // fused Llama-8B gate_up projection measured 2 us faster per launch than
   // with four-wave workgroups, which the unfused skinny kernel keeps for
   // large N.
+  // The activations sit in LDS only for up to kSelfQuantMaxM tokens, so only
+  // the one-block variants have that form.
   constexpr int xb = A16 ? 2 : 1;
-  if (MB <= 2) {
-    if (skinny_x_in_lds(g.M, g.K, MB, 8, p.s.ad.r, true, FMT, xb)) launch_decode_x<MB, FMT, 8, true, A16>(p, want_xq, stream);
-    else launch_decode_x<MB, FMT, 8, false, A16>(p, want_xq, stream);
-  } else {
-    if (skinny_x_in_lds(g.M, g.K, MB, 4, p.s.ad.r, true, FMT, xb)) launch_decode_x<MB, FMT, 4, true, A16>(p, want_xq, stream);
-    else launch_decode_x<MB, FMT, 4, false, A16>(p, want_xq, stream);
+  constexpr int NW = MB <= 2 ? 8 : 4;
+  if constexpr (MB == 1) {
+    if (skinny_x_in_lds(g.M, g.K, MB, NW, p.s.ad.r, true, FMT, xb)) {
+      launch_decode_x<MB, FMT, NW, true, A16>(p, want_xq, stream);
+      return;
+    }
   }
+  launch_decode_x<MB, FMT, NW, false, A16>(p, want_xq, stream);
 }
 
 template <int FMT, bool A16>

@@ -517,85 +517,152 @@ struct Skinny {
     tok[t] = TokenSlot{a, rk};
   }
 
-  // The r / 16 bf16 values of B[a][n][jl * r / 16 ...] this lane needs for
-  // output o of the tile at n0 (zero past the rank or without an adapter).
-  __device__ __forceinline__ uint4 b_chunk(int64_t n0, int o) const {
+  // ---- the adapter epilogue ---------------------------------------------------
+  // Each output (t, n) of a tile is a dot of B[a_t][n][0 .. rank) with z[t]
+  // taken by a group of 2^sh lanes: lane jl of the group takes the 8-element
+  // chunks jl, jl + 2^sh, ... of the row, at most CPL of them, and the
+  // partial dots meet through DPP moves.  A few lanes per output keep the
+  // arithmetic per output small at low rank (rank 16: one lane, two chunks);
+  // CPL = 1 spreads a row over up to 16 lanes, for the tile-major loop, where
+  // the weight registers are live and a tile has at most 256 outputs.
+  // Without adapters a thread writes whole outputs (sh = 0).  Output o of
+  // the tile is taken by lanes o * 2^sh ... modulo the block size, whose
+  // quotient is a multiple of 16, so a thread meets a single row
+  // n0 + (tid >> sh) % 16.
+  template <int CPL>
+  __device__ __forceinline__ int lane_shift() const {
+    if (!adapters) return 0;
+    const int need = ((p.ad.r >> 3) + CPL - 1) / CPL;
+    return need <= 1 ? 0 : need <= 2 ? 1 : need <= 4 ? 2 : need <= 8 ? 3 : 4;
+  }
+
+  // What the epilogue of a tile requests while the tile streams: the weight
+  // scale of the thread's row (row_ws, any time) and the first B chunk of
+  // its first output (pre_b, once tok[] is resolved; as stored: FP8 codes are
+  // widened when used).
+  struct EpiPre {
+    uint4 b;
+    float ws;
+  };
+  // CPL and group depth inside the tile-major streaming loop and after the
+  // stream (the batch-major loop and the fused stash).
+  static constexpr int kCplLoop = 1, kGLoop = 1;
+  static constexpr int kCplEnd = MB == 1 ? 1 : 4;
+  static constexpr int kGEnd = MB == 1 ? 2 : (GEN ? 2 : 4);
+
+  // The raw 16 bytes (bf16) or 8 bytes (FP8, in .x/.y) of chunk c of
+  // B[ts.a][n], or zeros when the chunk lies past the rank, the row past N or
+  // the token has no adapter.
+  __device__ __forceinline__ uint4 b_raw(const TokenSlot& ts, int64_t n, int c) const {
     uint4 v = zero4();
-    if (!adapters) return v;
-    const int jl = threadIdx.x & 15;
-    const int t = o >> 4;
-    const int64_t n = n0 + (o & 15);
-    if (t >= p.M || n >= p.N) return v;
-    const TokenSlot ts = tok[t];
-    if (ts.a < 0) return v;
-    const int r = p.ad.r;
-    const int ch = r >> 4;
-    const int j0 = jl * ch;
-    if (j0 >= ts.rank) return v;
-    const int64_t off = ((int64_t)ts.a * p.N + n) * r + j0;  // elements
-    if (af8()) {  // FP8 codes, widened to bf16 exactly
-      const uint8_t* src = p.ad.B8() + off;
-      uint32_t lo = 0, hi = 0;
-      if (ch == 8) { const uint2 w = *reinterpret_cast<const uint2*>(src); lo = w.x; hi = w.y; }
-      else if (ch == 4) lo = *reinterpret_cast<const uint32_t*>(src);
-      else if (ch == 2) lo = *reinterpret_cast<const uint16_t*>(src);
-      else lo = *src;
-      v = fp8x8_to_bf16x8(lo, hi);
+    if (ts.a < 0 || n >= p.N || c * 8 >= ts.rank) return v;
+    const int64_t off = ((int64_t)ts.a * p.N + n) * p.ad.r + c * 8;  // elements
+    if (af8()) {
+      const uint2 w = *reinterpret_cast<const uint2*>(p.ad.B8() + off);
+      v.x = w.x;
+      v.y = w.y;
     } else {
-      const uint16_t* src = p.ad.B + off;
-      if (ch == 8) v = *reinterpret_cast<const uint4*>(src);
-      else if (ch == 4) { const uint2 w = *reinterpret_cast<const uint2*>(src); v.x = w.x; v.y = w.y; }
-      else if (ch == 2) v.x = *reinterpret_cast<const uint32_t*>(src);
-      else v.x = *src;
-    }
-    if (j0 + ch > ts.rank) {  // clear the elements past the rank
-      uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        if (e < ch && j0 + e >= ts.rank) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-      v = make_uint4(w[0], w[1], w[2], w[3]);
+      v = *reinterpret_cast<const uint4*>(p.ad.B + off);
     }
     return v;
   }
 
-  // The weight scale of the output row this thread writes in the tile at n0
-  // (the output loop's stride is a multiple of 16, so a thread meets one row).
-  __device__ __forceinline__ float row_wscale(int64_t n0) const {
+  template <int CPL>
+  __device__ __forceinline__ float row_ws(int64_t n0) const {
     if (FMT == EPILORA_W_FP4) return gscale;
-    const int64_t n = n0 + ((threadIdx.x >> 4) & 15);
+    const int64_t n = n0 + ((threadIdx.x >> lane_shift<CPL>()) & 15);
     return n < p.N ? p.wt.sw[n] : 0.f;
+  }
+  template <int CPL>
+  __device__ __forceinline__ uint4 pre_b(int64_t n0) const {
+    if (!adapters) return zero4();
+    const int sh = lane_shift<CPL>();
+    const int o = (int)(threadIdx.x >> sh);
+    if (o >= p.M * 16) return zero4();
+    return b_raw(tok[o >> 4], n0 + (o & 15), threadIdx.x & ((1 << sh) - 1));
   }
 
   // Outputs of the tile at n0 from its reduced accumulators `base` ([T][16]).
-  // With have_pre, `pre` holds this thread's first-pass B slice and `pws` its
-  // row's weight scale, both loaded while the tile was streaming.
-  __device__ __forceinline__ void outputs(int64_t n0, const float* base, bool have_pre, const uint4& pre,
-                                          float pws) const {
-    const int jl = threadIdx.x & 15;
-    const int r = p.ad.r;
-    const int ch = r >> 4;
-    for (int o = threadIdx.x >> 4; o < p.M * 16; o += NW * 4) {
-      const int t = o >> 4;
-      const int64_t n = n0 + (o & 15);
-      float l = 0.f;
-      const bool lora = adapters && tok[t].a >= 0;
-      if (lora) {
-        const uint4 bv = (have_pre && o == (int)(threadIdx.x >> 4)) ? pre : b_chunk(n0, o);
-        const uint32_t w[4] = {bv.x, bv.y, bv.z, bv.w};
-        const float* zt = zs + t * r + jl * ch;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-          if (e < ch) l = fmaf((e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]), zt[e], l);
+  // G groups of outputs per lane have their B chunks requested before any
+  // is used, so their latencies overlap.
+  template <int G, int CPL>
+  __device__ __forceinline__ void outputs(int64_t n0, const float* base, const EpiPre& pre) const {
+    static_assert(CPL == 1 || CPL == 2 || CPL == 4, "chunks per lane");
+    constexpr int NT = NW * kWave;
+    const int total_o = (int)p.M * 16;
+    if (!adapters) {
+      const int64_t n = n0 + (threadIdx.x & 15);
+      if (n >= p.N) return;
+      for (int o = threadIdx.x; o < total_o; o += NT) {
+        const int t = o >> 4;
+        p.y[(int64_t)t * p.ldy + n] = (uint16_t)f32_to_bf16((base[o] * sxs[t]) * pre.ws);
       }
-      l += __shfl_xor(l, 8, 16);
-      l += __shfl_xor(l, 4, 16);
-      l += __shfl_xor(l, 2, 16);
-      l += __shfl_xor(l, 1, 16);
-      if (jl == 0 && n < p.N) {
-        float y = (base[o] * sxs[t]) * (have_pre ? pws : weight_scale<FMT>(p.wt, n));
-        if (lora && af8()) l *= p.ad.sb[(int64_t)tok[t].a * p.N + n];  // FP8 adapters: the row scale
-        if (lora) y = y + p.ad.scale * l;
-        p.y[(int64_t)t * p.ldy + n] = (uint16_t)f32_to_bf16(y);
+      return;
+    }
+    const int sh = lane_shift<CPL>();
+    const int jl = threadIdx.x & ((1 << sh) - 1);
+    const int per = NT >> sh;
+    const int first = (int)(threadIdx.x >> sh);
+    const int64_t n = n0 + (first & 15);
+    const int r = p.ad.r;
+    const int nch = r >> 3;
+    for (int o0 = first; o0 < total_o; o0 += per * G) {
+      uint4 raw[G][CPL];
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        const int o = o0 + gi * per;
+        const TokenSlot ts = o < total_o ? tok[o >> 4] : TokenSlot{-1, 0};
+#pragma unroll
+        for (int q = 0; q < CPL; ++q) {
+          const int c = jl + (q << sh);
+          raw[gi][q] = (o == first && q == 0) ? pre.b : (c < nch ? b_raw(ts, n, c) : zero4());
+        }
+      }
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        const int o = o0 + gi * per;
+        if (o >= total_o) break;
+        const int t = o >> 4;
+        const TokenSlot ts = tok[t];
+        // One partial dot per chunk (its elements in order), then a fixed
+        // tree over the chunk index, lowest bit first: the lane bits through
+        // DPP moves, the rest within the lane.  The tree is the same for any
+        // lanes-per-output, so every path that writes these outputs (tile- or
+        // batch-major, fused or not) gets the same bits.
+        float part[CPL];
+#pragma unroll
+        for (int q = 0; q < CPL; ++q) {
+          const int c = jl + (q << sh);
+          float d = 0.f;
+          if (ts.a >= 0 && c < nch && c * 8 < ts.rank) {
+            const uint4 v = af8() ? fp8x8_to_bf16x8(raw[gi][q].x, raw[gi][q].y) : raw[gi][q];
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            const float4 z0 = *reinterpret_cast<const float4*>(zs + t * r + c * 8);
+            const float4 z1 = *reinterpret_cast<const float4*>(zs + t * r + c * 8 + 4);
+            const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+            const int lim = ts.rank - c * 8;  // elements of the chunk inside the rank
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float b = (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
+              if (e < lim) d = fmaf(b, zv[e], d);
+            }
+          }
+          if (sh >= 1) d += dpp_mov<0xB1>(d);   // quad_perm [1, 0, 3, 2]: chunk bit 0
+          if (sh >= 2) d += dpp_mov<0x4E>(d);   // quad_perm [2, 3, 0, 1]: bit 1
+          if (sh >= 3) d += dpp_mov<0x141>(d);  // row_half_mirror: bit 2 (quads already uniform)
+          if (sh >= 4) d += dpp_mov<0x140>(d);  // row_mirror: bit 3 (half rows already uniform)
+          part[q] = d;
+        }
+        float l;
+        if constexpr (CPL == 1) l = part[0];
+        else if constexpr (CPL == 2) l = part[0] + part[1];
+        else l = (part[0] + part[1]) + (part[2] + part[3]);
+        if (jl == 0 && n < p.N) {
+          float y = (base[o] * sxs[t]) * pre.ws;
+          if (ts.a >= 0 && af8()) l *= p.ad.sb[(int64_t)ts.a * p.N + n];  // FP8 adapters: the row scale
+          if (ts.a >= 0) y = y + p.ad.scale * l;
+          p.y[(int64_t)t * p.ldy + n] = (uint16_t)f32_to_bf16(y);
+        }
       }
     }
   }
@@ -681,7 +748,7 @@ struct Skinny {
   // Tile j / nb is complete in `acc`.  Fused: reduce it into its stash slot.
   // Otherwise z is ready: write its outputs, then request the next tile's
   // first B slice and weight scale.
-  __device__ __forceinline__ void tile_done(int j, f32x4 (&acc)[MB], uint4& pre, float& pws) {
+  __device__ __forceinline__ void tile_done(int j, f32x4 (&acc)[MB], EpiPre& pre) {
     if (FUSED) {
       reduce_tile(acc, stash + (j / nb) * T * 16);
       return;
@@ -694,10 +761,10 @@ struct Skinny {
         zslice = sl;
       }
     }
-    outputs(n0_of(j), red, true, pre, pws);
+    outputs<kGLoop, kCplLoop>(n0_of(j), red, pre);
     if (j + 1 < total) {
-      pre = b_chunk(n0_of(j + 1), threadIdx.x >> 4);
-      pws = row_wscale(n0_of(j + 1));
+      pre.b = pre_b<kCplLoop>(n0_of(j + 1));
+      pre.ws = row_ws<kCplLoop>(n0_of(j + 1));
     }
   }
 
@@ -710,7 +777,7 @@ struct Skinny {
     uint4 pb[S];
 #pragma unroll
     for (int s = 0; s < S; ++s)
-      if (s < mine) pb[s] = b_chunk(n0_of(s * nb), threadIdx.x >> 4);
+      if (s < mine) pb[s] = pre_b<kCplEnd>(n0_of(s * nb));
     // The tiles come in output order: for each slice they span (one unless
     // the projection has several), poll that slice's z into LDS, then write
     // the outputs of the tiles inside it.
@@ -725,7 +792,7 @@ struct Skinny {
 #pragma unroll
       for (int s = 0; s < S; ++s)
         if (s < mine && (sl0 == sl1 || slice(n0_of(s * nb)) == sl))
-          outputs(n0_of(s * nb), stash + s * T * 16, true, pb[s], pw[s]);
+          outputs<kGEnd, kCplEnd>(n0_of(s * nb), stash + s * T * 16, EpiPre{pb[s], pw[s]});
     }
   }
 
@@ -763,7 +830,7 @@ struct Skinny {
     resolve_tokens(tl, g == 0);
     float pw[S];  // each tile's weight scale for the epilogue
 #pragma unroll
-    for (int t = 0; t < S; ++t) pw[t] = t < mine ? row_wscale(n0_of(t * nb)) : 0.f;
+    for (int t = 0; t < S; ++t) pw[t] = t < mine ? row_ws<kCplEnd>(n0_of(t * nb)) : 0.f;
     bool ok = true;
     if (FUSED && !A16) {  // the quantized rows come from other workgroups
       ok = wait_flag(J.qflag, J.qtarget, J.wait_ticks, err, p.ctrl + kCtrlForceTimeout, verdict);
@@ -810,7 +877,7 @@ struct Skinny {
       uint4 pb[S];
 #pragma unroll
       for (int t = 0; t < S; ++t)
-        if (t < mine) pb[t] = b_chunk(n0_of(t * nb), threadIdx.x >> 4);
+        if (t < mine) pb[t] = pre_b<kCplEnd>(n0_of(t * nb));
       if (adapters) {
         zslice = mine > 0 ? slice(n0_of(0)) : 0;
         stage_z(zslice);
@@ -826,7 +893,7 @@ struct Skinny {
               zslice = sl;
             }
           }
-          outputs(n0_of(t * nb), red, true, pb[t], pw[t]);
+          outputs<kGEnd, kCplEnd>(n0_of(t * nb), red, EpiPre{pb[t], pw[t]});
         }
       }
     }
@@ -883,11 +950,11 @@ struct Skinny {
     f32x4 acc[MB];
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[mb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    uint4 pre = FUSED ? zero4() : b_chunk(n0_of(0), threadIdx.x >> 4);
-    float pws = FUSED ? 0.f : row_wscale(n0_of(0));
+    EpiPre pre{zero4(), 0.f};
+    if (!FUSED) pre = EpiPre{pre_b<kCplLoop>(n0_of(0)), row_ws<kCplLoop>(n0_of(0))};
     float pw[StashCfg<MB>::n];  // fused: the weight scale of each tile, needed after the stream
 #pragma unroll
-    for (int s = 0; s < StashCfg<MB>::n; ++s) pw[s] = (FUSED && s < total / nb) ? row_wscale(n0_of(s * nb)) : 0.f;
+    for (int s = 0; s < StashCfg<MB>::n; ++s) pw[s] = (FUSED && s < total / nb) ? row_ws<kCplEnd>(n0_of(s * nb)) : 0.f;
 
     if (FUSED && !XLDS && !A16) {  // the quantized rows come from other workgroups
       ok = wait_flag(J.qflag, J.qtarget, J.wait_ticks, err, p.ctrl + kCtrlForceTimeout, verdict);
@@ -910,14 +977,14 @@ struct Skinny {
       __builtin_amdgcn_sched_barrier(0);
       compute(A, j, acc);
       __builtin_amdgcn_sched_barrier(0);
-      if (endA) tile_done(j, acc, pre, pws);
+      if (endA) tile_done(j, acc, pre);
       __builtin_amdgcn_sched_barrier(0);
       load_w(A, j + 2);
       load_x(A, j + 2);
       __builtin_amdgcn_sched_barrier(0);
       compute(B, j + 1, acc);
       __builtin_amdgcn_sched_barrier(0);
-      if (endB) tile_done(j + 1, acc, pre, pws);
+      if (endB) tile_done(j + 1, acc, pre);
       __builtin_amdgcn_sched_barrier(0);
       load_w(B, j + 3);
       load_x(B, j + 3);
