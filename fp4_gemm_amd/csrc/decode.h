@@ -11,12 +11,12 @@
 //                              quantized-rows flag (nq = 0 when every GEMM
 //                              workgroup quantizes the few rows into its own
 //                              LDS and the caller keeps no copy);
-//   the next tiles*splits*S    compute the shrink (bf16 x, fp32 partials,
-//                              the last split of a tile adds them in a fixed
-//                              order; one set per output slice with its own
-//                              adapter pair) and store z in place, each word as its
-//                              bitwise complement into a region that reads
-//                              zero until then;
+//   the next M*S*(r/RW)        compute the shrink, one unit (token, output
+//                              slice with its own adapter pair, RW rank
+//                              rows) each over the whole of K, and store z
+//                              in place, each word as its bitwise
+//                              complement into a region that reads zero
+//                              until then;
 //   the rest                   own 16-row weight tiles: request their first
 //                              weight batch, obtain the quantized rows,
 //                              stream the weights through the matrix cores
@@ -44,7 +44,7 @@ namespace epilora {
 struct DecodeParams {
   SkinnyJob job;  // job.g.xq / job.g.sx: where the quantized rows go; job.g.z: ws z
   ShrinkParams s;
-  int nq, ns, tiles;
+  int nq, ns;
   int count_q;  // the GEMM workgroups wait for the quantized rows
   int flags;    // a flag is counted or z handed over: the GEMM workgroups reset / clear at the end
   int* done;    // kDoneGroups sub-counters, kDoneStride words apart
@@ -72,15 +72,7 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((XLDS &
     return;
   }
   if (bid < p.nq + p.ns) {  // ---- shrink
-    const int sb = bid - p.nq;
-    const int tile = sb % p.tiles, rest = sb / p.tiles;
-    const int split = rest % p.s.splits, slice = rest / p.s.splits;
-    int s_begin, s_end;
-    shrink_range(p.s, split, s_begin, s_end);
-    float* red = reinterpret_cast<float*>(smem);
-    const uint64_t active =
-        shrink_tile<NW, GEN>(p.s, (int64_t)tile * kShrinkTokens, slice, s_begin, s_end, red, split == 0 && slice == 0);
-    shrink_finish<NW, kShrinkTokens, GEN>(p.s, tile, slice, split, red, active);
+    shrink_unit<GEN>(p.s, bid - p.nq, reinterpret_cast<float*>(smem));
     return;
   }
 
@@ -129,9 +121,7 @@ static void launch_decode_u(DecodeParams& p, bool want_xq, hipStream_t stream) {
   p.job.qtarget = (int)g.M;
   p.count_q = (XLDS || A16) ? 0 : 1;
   p.flags = p.count_q || p.ns > 0;
-  size_t lds = skinny_lds(g.M, g.K, MB, NW, r, true, XLDS, FMT, A16 ? 2 : 1);
-  const size_t shrink_lds = (size_t)kShrinkWaves * 16 * r * sizeof(float);
-  if (shrink_lds > lds) lds = shrink_lds;
+  const size_t lds = skinny_lds(g.M, g.K, MB, NW, r, true, XLDS, FMT, A16 ? 2 : 1);  // > the shrink's kShrinkWaves * 4 floats
   // The quantizing and shrink workgroups are dispatched first and hold their
   // slots only until they finish.
   p.job.gwgs = skinny_groups(g.N, resident_groups(decode_kernel<MB, FMT, NW, XLDS, UB, GEN, A16>, NW * 64, lds),

@@ -39,9 +39,8 @@ hipError_t launch_decode_lora(const uint16_t* x, int64_t ldx, int64_t M, int64_t
   p.done = reinterpret_cast<int*>(wsb + kDoneOffset);
   s.counters = reinterpret_cast<int*>(wsb + lay.shrink.counters);
   s.partials = reinterpret_cast<float*>(wsb + lay.shrink.partials);
-  s.splits = shrink_splits(M, K, ad.r);
-  p.tiles = (int)cdiv(M, kShrinkTokens);
-  p.ns = adapters ? p.tiles * s.splits * ad.S : 0;
+  s.splits = 1;
+  p.ns = adapters ? (int)shrink_units(M, ad.S, ad.r, K) : 0;
   const bool want_xq = xq_out != nullptr || sx_out != nullptr;
   if (x16) decode_dispatch_a16(p, want_xq, stream);
   else if (wt.fmt == EPILORA_W_FP8) decode_dispatch_fp8(p, want_xq, stream);

@@ -6,14 +6,10 @@ namespace epilora {
 
 constexpr int kShrinkThreads = 256;
 
-__global__ __launch_bounds__(kShrinkThreads) void shrink_kernel(ShrinkParams p) {
-  extern __shared__ float red[];  // [4 waves][16 tokens][r]
-  int s_begin, s_end;
-  shrink_range(p, blockIdx.y, s_begin, s_end);
-  const int slice = blockIdx.z;
-  const uint64_t active = shrink_tile<4>(p, (int64_t)blockIdx.x * kShrinkTokens, slice, s_begin, s_end, red,
-                                         blockIdx.y == 0 && slice == 0);
-  shrink_finish<4>(p, blockIdx.x, slice, blockIdx.y, red, active);
+// Decode batches (M <= 64): one workgroup per unit (shrink_unit).
+__global__ __launch_bounds__(kShrinkThreads) void shrink_unit_kernel(ShrinkParams p) {
+  __shared__ float red[kShrinkWaves * 4];
+  shrink_unit<true>(p, (int)blockIdx.x, red);
 }
 
 // ---------------------------------------------------------------------------
@@ -141,9 +137,8 @@ hipError_t launch_shrink(const uint16_t* x, int64_t M, int64_t K, int64_t ldx, c
     hipLaunchKernelGGL(shrink_wide_kernel, grid, dim3(kShrinkThreads), 0, stream, p);
     return hipGetLastError();
   }
-  const dim3 grid((unsigned)cdiv(M, kShrinkTokens), (unsigned)p.splits, (unsigned)ad.S);
-  const size_t lds = (size_t)kShrinkWaves * 16 * ad.r * sizeof(float);
-  hipLaunchKernelGGL(shrink_kernel, grid, dim3(kShrinkThreads), lds, stream, p);
+  const int64_t units = shrink_units(M, ad.S, ad.r, K);
+  hipLaunchKernelGGL(shrink_unit_kernel, dim3((unsigned)units), dim3(kShrinkThreads), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -294,6 +294,145 @@ __device__ __forceinline__ bool shrink_finish(const ShrinkParams& p, int tile, i
   return true;
 }
 
+// ---------------------------------------------------------------------------
+// Decode batches (M <= kShrinkWideM): one workgroup per unit (token t, output
+// slice, block of RW consecutive rank rows) over the whole of K, so no sum
+// crosses workgroups and z is stored as soon as the unit's loads are in.
+// With few tokens, tiles of 16 tokens leave the matrix cores' columns mostly
+// empty anyway (and a tile of distinct tenants would take its adapters one
+// after another); a unit is a matrix-vector product on the vector ALUs.
+// The first kShrinkWaves waves take the 8-element chunks tid, tid + 256, ...
+// of K (further waves of a larger block idle, so the sums round the same way
+// in every kernel that carries this code); each thread requests its chunks
+// of x and of the RW rows of A at once (RW * K <= 16384 elements: one round
+// of loads for K up to 16384) and sums its chunks in K order, one fp32 FMA
+// per element (bf16 products are exact in fp32); the 64 lanes of a wave
+// meet in a fixed tree (DPP moves, then two swaps across rows) and the
+// waves in wave order.  FP8 adapters: the codes are widened exactly and the
+// row scale sa multiplies the finished sum.  z rows of inactive tokens are
+// written as zeros by the separate shrink and not at all by the fused path
+// (zflip != 0), which stores exactly the words its consumers poll.
+// ---------------------------------------------------------------------------
+__host__ __device__ inline int shrink_unit_rows(int64_t K) { return K <= 4096 ? 4 : (K <= 8192 ? 2 : 1); }
+__host__ __device__ inline int64_t shrink_units(int64_t M, int S, int r, int64_t K) {
+  return M * S * (r / shrink_unit_rows(K));
+}
+
+// Sum over the 64 lanes of a wave, the same bits in every lane.
+__device__ __forceinline__ float wave_tree_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));   // lane ^ 1
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));   // lane ^ 2
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));  // half-row mirror
+  v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));  // row mirror
+  v += __shfl_xor(v, 16, kWave);
+  v += __shfl_xor(v, 32, kWave);
+  return v;
+}
+
+template <int RW, bool GEN, typename XT>
+__device__ __forceinline__ void shrink_unit_rows_of(const ShrinkParams& p, int64_t t, int slice, int j0, int a,
+                                                    int rank, float* red, const XT& xt) {
+  constexpr int CG = 8 / RW;                   // chunks of K per thread and round
+  constexpr int NTS = kShrinkWaves * kWave;    // the threads that take chunks
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool working = tid < NTS;
+  const int64_t K = p.K;
+  const int nck = (int)(K >> 3);
+  const int r = p.ad.r, S = GEN ? p.ad.S : 1, zld = GEN ? p.ad.zld : r;
+  const bool a8 = GEN && p.ad.afmt != 0;
+  const bool live = a >= 0 && j0 < rank;  // uniform over the block
+  float acc[RW];
+#pragma unroll
+  for (int q = 0; q < RW; ++q) acc[q] = 0.f;
+  if (live) {
+    const int64_t arow = (((int64_t)a * S + slice) * r + j0) * K;  // elements
+    const uint16_t* xr = p.x + t * p.ldx;
+    for (int c0 = tid; c0 < nck; c0 += NTS * CG) {
+      uint4 xv[CG], av[RW][CG];
+#pragma unroll
+      for (int i = 0; i < CG; ++i) {
+        const int kc = c0 + i * NTS;
+        xv[i] = (working && kc < nck) ? ld16(xr + 8 * (int64_t)kc) : make_uint4(0, 0, 0, 0);
+      }
+#pragma unroll
+      for (int q = 0; q < RW; ++q)
+#pragma unroll
+        for (int i = 0; i < CG; ++i) {
+          const int kc = c0 + i * NTS;
+          const bool ok = working && kc < nck && j0 + q < rank;
+          if (a8) {
+            const uint2 w = ok ? *reinterpret_cast<const uint2*>(p.ad.A8() + arow + q * K + 8 * (int64_t)kc)
+                               : make_uint2(0, 0);
+            av[q][i] = make_uint4(w.x, w.y, 0, 0);
+          } else {
+            av[q][i] = ok ? ld16(p.ad.A + arow + q * K + 8 * (int64_t)kc) : make_uint4(0, 0, 0, 0);
+          }
+        }
+#pragma unroll
+      for (int i = 0; i < CG; ++i) {
+        const int kc = c0 + i * NTS;
+        const uint4 x8 = (working && kc < nck) ? xt(xv[i], 8 * (int64_t)kc, 0) : xv[i];
+        const uint32_t xw[4] = {x8.x, x8.y, x8.z, x8.w};
+#pragma unroll
+        for (int q = 0; q < RW; ++q) {
+          const uint4 v = a8 ? fp8x8_to_bf16x8(av[q][i].x, av[q][i].y) : av[q][i];
+          const uint32_t aw[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float xe = (e & 1) ? bf16_hi(xw[e >> 1]) : bf16_lo(xw[e >> 1]);
+            const float ae = (e & 1) ? bf16_hi(aw[e >> 1]) : bf16_lo(aw[e >> 1]);
+            acc[q] = fmaf(ae, xe, acc[q]);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < RW; ++q) {
+    const float v = wave_tree_sum(acc[q]);
+    if (lane == 0 && wave < kShrinkWaves) red[wave * RW + q] = v;
+  }
+  __syncthreads();
+  if (tid == 0 && (a >= 0 || p.zflip == 0u)) {
+    float zv[RW];
+#pragma unroll
+    for (int q = 0; q < RW; ++q) {
+      float v = red[q];
+#pragma unroll
+      for (int w = 1; w < kShrinkWaves; ++w) v += red[w * RW + q];
+      if (a < 0 || j0 + q >= rank) v = 0.f;
+      else if (a8) v *= p.ad.sa[((int64_t)a * S + slice) * r + j0 + q];
+      zv[q] = v;
+    }
+    const uint32_t f = p.zflip;
+    const auto zr = make_rsrc(p.z + t * zld + slice * r + j0, (uint32_t)(RW * 4));
+    if constexpr (RW == 4)
+      buf_store16<kCoherent>(zr, 0u, make_uint4(__float_as_uint(zv[0]) ^ f, __float_as_uint(zv[1]) ^ f,
+                                                __float_as_uint(zv[2]) ^ f, __float_as_uint(zv[3]) ^ f));
+    else if constexpr (RW == 2)
+      buf_store8<kCoherent>(zr, 0u, make_uint2(__float_as_uint(zv[0]) ^ f, __float_as_uint(zv[1]) ^ f));
+    else
+      buf_store4<kCoherent>(zr, 0u, __float_as_uint(zv[0]) ^ f);
+  }
+}
+
+// Unit `unit` of a decode batch's shrink (units in token, slice, row-block
+// order).  `red`: LDS of kShrinkWaves * 4 floats.  Every thread of the block
+// calls it; it ends with no pending barrier.
+template <bool GEN, typename XT = XIdentity>
+__device__ __forceinline__ void shrink_unit(const ShrinkParams& p, int unit, float* red, const XT& xt = XT()) {
+  const int r = p.ad.r, S = GEN ? p.ad.S : 1;
+  const int RW = shrink_unit_rows(p.K), nrb = r / RW;
+  const int rb = unit % nrb, rest = unit / nrb;
+  const int slice = rest % S;
+  const int64_t t = rest / S;
+  int rank;
+  const int a = resolve_token(t, p.M, p.ad, p.ctrl + kCtrlError, threadIdx.x == 0 && slice == 0 && rb == 0, rank);
+  if (RW == 4) shrink_unit_rows_of<4, GEN>(p, t, slice, rb * 4, a, rank, red, xt);
+  else if (RW == 2) shrink_unit_rows_of<2, GEN>(p, t, slice, rb * 2, a, rank, red, xt);
+  else shrink_unit_rows_of<1, GEN>(p, t, slice, rb, a, rank, red, xt);
+}
+
 // K-step range of split `split`.
 __device__ __forceinline__ void shrink_range(const ShrinkParams& p, int split, int& s_begin, int& s_end) {
   const int steps = (int)cdiv(p.K, kShrinkStep);
