@@ -1,4 +1,5 @@
-// The fused small-batch (decode) path in one persistent launch.
+// The fused small-batch (decode) path in one persistent launch (with more
+// than 32 tokens, a quantizer launch before it).
 //
 // The method launches the down-projection first and the GEMM as its
 // programmatic dependent, which waits for the down-projection only before
@@ -10,7 +11,11 @@
 //   workgroups [0, nq)         quantize one token row each and count up the
 //                              quantized-rows flag (nq = 0 when every GEMM
 //                              workgroup quantizes the few rows into its own
-//                              LDS and the caller keeps no copy);
+//                              LDS and the caller keeps no copy, and with
+//                              more than 32 tokens, whose rows a quantizer
+//                              launch writes beforehand: every GEMM
+//                              workgroup reads all M rows, which then go
+//                              through its XCD's L2 instead of past it);
 //   the next M*S*(r/RW)        compute the shrink, one unit (token, output
 //                              slice with its own adapter pair, RW rank
 //                              rows) each over the whole of K, and store z
@@ -117,9 +122,17 @@ template <int MB, int FMT, int NW, bool XLDS, int UB, bool GEN, bool A16>
 static void launch_decode_u(DecodeParams& p, bool want_xq, hipStream_t stream) {
   const GemmParams& g = p.job.g;
   const int r = p.s.ad.r;
-  p.nq = (A16 || (XLDS && !want_xq)) ? 0 : (int)g.M;
+  // Quantized rows: kept in LDS (each GEMM workgroup quantizes them, and M
+  // workgroups also write xq_out when the caller asks for it), produced by M
+  // workgroups of this grid behind the quantized-rows flag, or (more than 32
+  // tokens) by the quantizer kernel launched just before.
+  constexpr bool before = !XLDS && !A16 && MB >= kQuantBeforeMB;
+  if (before && launch_quant_rows(p.job.x, g.M, g.K, p.job.ldx, const_cast<uint8_t*>(g.xq), g.ldq,
+                                  const_cast<float*>(g.sx), stream) != hipSuccess)
+    return;
+  p.nq = (A16 || before || (XLDS && !want_xq)) ? 0 : (int)g.M;
   p.job.qtarget = (int)g.M;
-  p.count_q = (XLDS || A16) ? 0 : 1;
+  p.count_q = (XLDS || A16 || before) ? 0 : 1;
   p.flags = p.count_q || p.ns > 0;
   const size_t lds = skinny_lds(g.M, g.K, MB, NW, r, true, XLDS, FMT, A16 ? 2 : 1);  // > the shrink's kShrinkWaves * 4 floats
   // The quantizing and shrink workgroups are dispatched first and hold their

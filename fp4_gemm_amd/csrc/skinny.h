@@ -46,6 +46,12 @@ namespace epilora {
 constexpr int kXInLdsMax = 32768;  // bytes of quantized activations kept in LDS
 constexpr int kSelfQuantMaxM = 4;  // the fused kernel quantizes up to this many rows itself
 constexpr uint32_t kLdsBudget = 65536;
+// The fused kernel takes quantized rows that are not kept in LDS from
+// quantizing workgroups of its own grid for up to 32 tokens (read
+// device-coherently), and from a quantizer launch just before it for more
+// (read through the caches): each workgroup reads all M rows, and from 33
+// tokens on those reads, sent past the L2, cost more than the extra launch.
+constexpr int kQuantBeforeMB = 3;
 
 // Tiles of one fused workgroup, held in LDS until z is published.
 template <int MB>
@@ -288,7 +294,9 @@ struct Skinny {
   static constexpr int T = MB * 16;
   // Activations from other workgroups of a fused grid are read coherently;
   // the W8A16 GEMM reads the caller's bf16 rows, which no workgroup writes.
-  static constexpr int XPOL = (FUSED && !A16) ? kCoherent : kCached;
+  // rows quantized inside this grid, announced by the quantized-rows flag
+  static constexpr bool kRowsInGrid = FUSED && !XLDS && !A16 && MB < kQuantBeforeMB;
+  static constexpr int XPOL = kRowsInGrid ? kCoherent : kCached;
   static constexpr int XB = A16 ? 2 : 1;   // bytes per activation element
   static constexpr int XV = A16 ? 4 : 2;   // 16-byte activation vectors per lane and step
   static_assert(!A16 || FMT == EPILORA_W_FP8, "W8A16 takes FP8 weights");
@@ -832,7 +840,7 @@ struct Skinny {
 #pragma unroll
     for (int t = 0; t < S; ++t) pw[t] = t < mine ? row_ws<kCplEnd>(n0_of(t * nb)) : 0.f;
     bool ok = true;
-    if (FUSED && !A16) {  // the quantized rows come from other workgroups
+    if (kRowsInGrid) {  // the quantized rows come from other workgroups
       ok = wait_flag(J.qflag, J.qtarget, J.wait_ticks, err, p.ctrl + kCtrlForceTimeout, verdict);
       const auto sr = make_rsrc(p.sx, (uint32_t)(M * 4));
       for (int t = threadIdx.x; t < M; t += NT) sxs[t] = __uint_as_float(buf_load4<kCoherent>(sr, 4u * t));
@@ -956,14 +964,13 @@ struct Skinny {
 #pragma unroll
     for (int s = 0; s < StashCfg<MB>::n; ++s) pw[s] = (FUSED && s < total / nb) ? row_ws<kCplEnd>(n0_of(s * nb)) : 0.f;
 
-    if (FUSED && !XLDS && !A16) {  // the quantized rows come from other workgroups
+    if (kRowsInGrid) {  // the quantized rows come from other workgroups
       ok = wait_flag(J.qflag, J.qtarget, J.wait_ticks, err, p.ctrl + kCtrlForceTimeout, verdict);
       const auto sr = make_rsrc(p.sx, (uint32_t)(M * 4));
       for (int t = threadIdx.x; t < M; t += NT) sxs[t] = __uint_as_float(buf_load4<kCoherent>(sr, 4u * t));
       __syncthreads();
-    }
-    if (FUSED && !XLDS && A16) {  // the caller's bf16 rows, read directly
-      for (int t = threadIdx.x; t < M; t += NT) sxs[t] = 1.0f;
+    } else if (FUSED && !XLDS) {  // rows quantized by an earlier launch, or the caller's bf16 rows
+      for (int t = threadIdx.x; t < M; t += NT) sxs[t] = A16 ? 1.0f : p.sx[t];
       __syncthreads();
     }
     load_x(A, 0);

@@ -110,7 +110,8 @@ class DeviceGemm:
 
     def shrink(self, ws=None):
         ws = ws if ws is not None else ep.new_workspace(ep.OP_SHRINK, self.M, self.N, self.K, self.r * self.S)
-        z = torch.empty(self.M, self.r * self.S, dtype=torch.float32, device=DEV)
+        # NaN-filled: every word, inactive rows included, must be written
+        z = torch.full((self.M, self.r * self.S), float("nan"), dtype=torch.float32, device=DEV)
         ep.epilora_lora_shrink(self.x, self.A, self.idx, z, ws, ranks=self.ranks, mask=self.mask, **self.akw)
         return z, ws
 

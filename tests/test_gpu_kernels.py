@@ -125,6 +125,8 @@ SHRINK_CASES = [
     (33, 4224, 6, 32, "mixed", False, True),
     (100, 512, 3, 128, "sorted", True, True),
     (16, 14336, 64, 64, "distinct", False, False),
+    (9, 8192, 12, 128, "distinct", False, True),  # two rank rows per unit
+    (3, 29568, 5, 32, "mixed", True, True),       # one row per unit, two rounds of loads
     # prefill batches: 64-token tiles, ragged token and K tails, many splits
     (65, 256, 2, 16, "mixed", False, False),
     (300, 4112, 8, 128, "mixed", True, True),
@@ -308,6 +310,23 @@ def test_decode_workspace_shared_by_different_calls():
         assert ep.epilora_device_error(ws) == 0
 
 
+def test_decode_fresh_rows_each_call():
+    # 17 to 64 tokens: the quantizing workgroups hand the rows to the GEMM
+    # workgroups through the workspace (the same addresses every call), which
+    # read them through the caches after an agent-scope acquire.  Different
+    # activations in turn on one workspace: every call must read its own rows.
+    for M in (48, 64):
+        say(f"decode M={M}: one workspace, different activations in turn")
+        ds = [DeviceGemm(custom_layer(f"f{i}", 1300 + 7 * i + M, M, 4096, 1024, 8, 32,
+                                      list(range(-1, 7)) * (M // 8)).gemms[0]) for i in range(2)]
+        ws = ep.new_workspace(ep.OP_DECODE, M, 1024, 4096, 32)
+        for d in (ds[0], ds[1], ds[0], ds[1]):
+            fused = d.decode(ws=ws, keep_xq=False)
+            sep = d.separate()
+            assert torch.equal(fused["y"], sep["y"])
+            assert ep.epilora_device_error(ws) == 0
+
+
 def test_decode_base_only():
     lay = custom_layer("db", 950, 3, 512, 256, 1, 16, [-1, -1, -1])
     d = DeviceGemm(lay.gemms[0])
@@ -343,8 +362,8 @@ def test_decode_inactive_tiles_leave_no_stale_z():
 @pytest.mark.parametrize("M", [1, 24])
 def test_decode_forced_timeout_then_recovers(M):
     # The failure path of the bounded waits, forced from the host: every wait
-    # gives up at once (M = 1: the wait for z; M = 24: also the wait for the
-    # quantized rows), every kernel still runs to its end, the call raises
+    # for z gives up at once (M = 1: the rows in LDS; M = 24: the rows
+    # quantized by a launch of their own), every kernel still runs to its end, the call raises
     # EPILORA_DEV_WAIT_TIMEOUT, and after epilora_workspace_init the next call
     # on the workspace is bitwise correct again.
     say(f"decode: forced timeout M={M}")
