@@ -137,8 +137,9 @@ static void launch_decode_u(DecodeParams& p, bool want_xq, hipStream_t stream) {
   const size_t lds = skinny_lds(g.M, g.K, MB, NW, r, true, XLDS, FMT, A16 ? 2 : 1);  // > the shrink's kShrinkWaves * 4 floats
   // The quantizing and shrink workgroups are dispatched first and hold their
   // slots only until they finish.
-  p.job.gwgs = skinny_groups(g.N, resident_groups(decode_kernel<MB, FMT, NW, XLDS, UB, GEN, A16>, NW * 64, lds),
-                             StashCfg<MB>::n);
+  const int resident = resident_groups(decode_kernel<MB, FMT, NW, XLDS, UB, GEN, A16>, NW * 64, lds);
+  p.job.gwgs = (MB >= 2 && !XLDS && !A16) ? skinny_batch_groups(g.N, MB, resident)
+                                          : skinny_groups(g.N, resident, StashCfg<MB>::n);
   const unsigned grid = (unsigned)(p.nq + p.ns + p.job.gwgs);
   hipLaunchKernelGGL((decode_kernel<MB, FMT, NW, XLDS, UB, GEN, A16>), dim3(grid), dim3(NW * 64), lds, stream, p);
 }

@@ -24,8 +24,8 @@ static void launch_skinny_g(SkinnyJob& J, hipStream_t stream) {
   const size_t lds = skinny_lds(p.M, p.K, MB, NW, p.ad.r, false, XLDS, FMT, A16 ? 2 : 1);
   // two or more token blocks without the activations in LDS run batch-major
   // over at most stash_tiles(MB) tiles per workgroup
-  const int cap = (MB >= 2 && !XLDS && !A16) ? stash_tiles(MB) : 0;
-  J.gwgs = skinny_groups(p.N, resident_groups(gemm_skinny_kernel<MB, FMT, NW, XLDS, GEN, A16>, NW * 64, lds), cap);
+  const int resident = resident_groups(gemm_skinny_kernel<MB, FMT, NW, XLDS, GEN, A16>, NW * 64, lds);
+  J.gwgs = (MB >= 2 && !XLDS && !A16) ? skinny_batch_groups(p.N, MB, resident) : skinny_groups(p.N, resident);
   hipLaunchKernelGGL((gemm_skinny_kernel<MB, FMT, NW, XLDS, GEN, A16>), dim3(J.gwgs), dim3(NW * 64), lds, stream, J);
 }
 
