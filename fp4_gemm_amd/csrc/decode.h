@@ -34,8 +34,9 @@
 // completed, so no workgroup has to write back or invalidate its L2.  Workgroups are dispatched in index order, so the
 // producers are resident before any consumer spins; every wait is bounded by
 // a wall-clock limit and a timeout raises EPILORA_DEV_WAIT_TIMEOUT instead of
-// hanging.  The last GEMM workgroup to finish puts the flags back to zero and
-// clears z for the next call.  The quantizer, shrink and GEMM arithmetic is the same code
+// hanging.  Each GEMM workgroup counts itself done as soon as z is in its
+// LDS (the atomic's round trip overlaps its epilogues); the last one puts
+// the flags back to zero and clears z for the next call.  The quantizer, shrink and GEMM arithmetic is the same code
 // as in the separate kernels, with the same summation orders, so every output
 // is bitwise equal to the separate quant + shrink + GEMM calls.
 #pragma once
@@ -49,10 +50,9 @@ namespace epilora {
 struct DecodeParams {
   SkinnyJob job;  // job.g.xq / job.g.sx: where the quantized rows go; job.g.z: ws z
   ShrinkParams s;
-  int nq, ns;
+  int nq, ns;  // quantizing and shrink workgroups
+  int units;   // shrink units (shrink_unit), taken by the ns workgroups in turn
   int count_q;  // the GEMM workgroups wait for the quantized rows
-  int flags;    // a flag is counted or z handed over: the GEMM workgroups reset / clear at the end
-  int* done;    // kDoneGroups sub-counters, kDoneStride words apart
 };
 
 // A16: the matched W8A16 GEMM (bf16 activations read as they are, no
@@ -76,42 +76,21 @@ __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu((XLDS &
     }
     return;
   }
-  if (bid < p.nq + p.ns) {  // ---- shrink
-    shrink_unit<GEN>(p.s, bid - p.nq, reinterpret_cast<float*>(smem));
+  if (bid < p.nq + p.ns) {  // ---- shrink: units bid - nq, + ns, ...
+    for (int u = bid - p.nq; u < p.units; u += p.ns) {
+      if (u != bid - p.nq) __syncthreads();  // the previous unit's sums are read
+      shrink_unit<GEN>(p.s, u, reinterpret_cast<float*>(smem));
+    }
     return;
   }
 
   // ---- GEMM workgroup (persistent over its tiles)
-  {
-    Skinny<MB, FMT, NW, XLDS, true, UB, GEN, A16> sk(p.job, smem, bid - p.nq - p.ns);
-    sk.run();
-  }
-  if (!p.flags) return;
-  // Every flag and z read of this workgroup is behind it: count it done.
-  // The last of each group counts the group, and the last group puts the
-  // flags back to zero and clears z; each counter is reset by the one that
-  // completed it.
-  int* last = reinterpret_cast<int*>(smem);
-  __syncthreads();
-  if (threadIdx.x == 0) *last = 0;
-  if (threadIdx.x == 0) {
-    const int gi = bid - p.nq - p.ns;
-    const int ng = (int)gridDim.x - p.nq - p.ns;
-    const int groups = ng < kDoneGroups ? ng : kDoneGroups;
-    const int grp = gi % groups;
-    const int members = ng / groups + (grp < ng % groups ? 1 : 0);
-    int* sub = p.done + grp * kDoneStride;
-    if (atomic_add_relaxed(sub, 1) == members - 1) {
-      store_relaxed(sub, 0);
-      if (atomic_add_relaxed(ctrl + kCtrlGemmDone, 1) == groups - 1) {
-        store_relaxed(ctrl + kCtrlQuantDone, 0);
-        store_relaxed(ctrl + kCtrlGemmDone, 0);
-        *last = 1;
-      }
-    }
-  }
-  __syncthreads();
-  if (*last != 0 && p.ns > 0) {
+  Skinny<MB, FMT, NW, XLDS, true, UB, GEN, A16> sk(p.job, smem, bid - p.nq - p.ns);
+  sk.run();
+  if (!p.job.flags) return;
+  // Count the workgroup done (if the epilogue has not already) and, in the
+  // last one, clear z.
+  if (sk.done_finish() && p.ns > 0) {
     const int n = (int)(g.M * p.s.ad.zld);
     const auto zr = make_rsrc(g.z, (uint32_t)(n * 4));
     for (int e = 4 * threadIdx.x; e < n; e += 4 * NW * 64) buf_store16<kCoherent>(zr, 4u * e, make_uint4(0u, 0u, 0u, 0u));
@@ -133,7 +112,7 @@ static void launch_decode_u(DecodeParams& p, bool want_xq, hipStream_t stream) {
   p.nq = (A16 || before || (XLDS && !want_xq)) ? 0 : (int)g.M;
   p.job.qtarget = (int)g.M;
   p.count_q = (XLDS || A16 || before) ? 0 : 1;
-  p.flags = p.count_q || p.ns > 0;
+  p.job.flags = p.count_q || p.ns > 0;
   const size_t lds = skinny_lds(g.M, g.K, MB, NW, r, true, XLDS, FMT, A16 ? 2 : 1);  // > the shrink's kShrinkWaves * 4 floats
   // The quantizing and shrink workgroups are dispatched first and hold their
   // slots only until they finish.

@@ -4,6 +4,13 @@
 
 namespace epilora {
 
+// Shrink workgroups of the fused grid at most (each takes units in turn).
+// They are dispatched before the GEMM workgroups; a thousand of them (64
+// tokens, K = 29568: one rank row per unit) held the GEMM workgroups back by
+// 8 us and crowded them onto fewer compute units, while 64 or fewer left the
+// 2048 units of the 8B-shaped down projection at 32 tokens too long in turn.
+constexpr int kDecodeShrinkWgs = 256;
+
 hipError_t launch_decode_lora(const uint16_t* x, int64_t ldx, int64_t M, int64_t N, int64_t K,
                               const WeightArgs& wt, const AdapterArgs& ad, uint16_t* y, int64_t ldy,
                               uint8_t* xq_out, float* sx_out, int64_t ldq_out, void* ws, bool x16,
@@ -36,11 +43,12 @@ hipError_t launch_decode_lora(const uint16_t* x, int64_t ldx, int64_t M, int64_t
   s.z = reinterpret_cast<float*>(wsb + kZOffset);
   s.zflip = ~0u;
   s.ctrl = ctrl;
-  p.done = reinterpret_cast<int*>(wsb + kDoneOffset);
+  J.done = reinterpret_cast<int*>(wsb + kDoneOffset);
   s.counters = reinterpret_cast<int*>(wsb + lay.shrink.counters);
   s.partials = reinterpret_cast<float*>(wsb + lay.shrink.partials);
   s.splits = 1;
-  p.ns = adapters ? (int)shrink_units(M, ad.S, ad.r, K) : 0;
+  p.units = adapters ? (int)shrink_units(M, ad.S, ad.r, K) : 0;
+  p.ns = p.units < kDecodeShrinkWgs ? p.units : kDecodeShrinkWgs;
   const bool want_xq = xq_out != nullptr || sx_out != nullptr;
   if (x16) decode_dispatch_a16(p, want_xq, stream);
   else if (wt.fmt == EPILORA_W_FP8) decode_dispatch_fp8(p, want_xq, stream);

@@ -330,8 +330,8 @@ __device__ __forceinline__ float wave_tree_sum(float v) {
 }
 
 template <int RW, bool GEN, typename XT>
-__device__ __forceinline__ void shrink_unit_rows_of(const ShrinkParams& p, int64_t t, int slice, int j0, int a,
-                                                    int rank, float* red, const XT& xt) {
+__device__ __forceinline__ void shrink_unit_rows_of(const ShrinkParams& p, int64_t t, int slice, int j0, float* red,
+                                                    bool report, const XT& xt) {
   constexpr int CG = 8 / RW;                   // chunks of K per thread and round
   constexpr int NTS = kShrinkWaves * kWave;    // the threads that take chunks
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -340,26 +340,49 @@ __device__ __forceinline__ void shrink_unit_rows_of(const ShrinkParams& p, int64
   const int nck = (int)(K >> 3);
   const int r = p.ad.r, S = GEN ? p.ad.S : 1, zld = GEN ? p.ad.zld : r;
   const bool a8 = GEN && p.ad.afmt != 0;
-  const bool live = a >= 0 && j0 < rank;  // uniform over the block
+  const uint16_t* xr = p.x + t * p.ldx;
+  // The token's slot and mask byte and the first round of activations are
+  // requested together (none depends on another); the adapter's rows and
+  // its rank then go out together too.  Rows past the rank are read (they
+  // lie inside the slot) and dropped at the end, so no load waits for the
+  // rank: two round trips to memory before the sums instead of four.
+  const int a_raw = p.ad.idx[t];
+  const int mk = p.ad.mask != nullptr ? (int)p.ad.mask[t] : 1;
+  uint4 xv[CG];
+#pragma unroll
+  for (int i = 0; i < CG; ++i) {
+    const int kc = tid + i * NTS;
+    xv[i] = (working && kc < nck) ? ld16(xr + 8 * (int64_t)kc) : make_uint4(0, 0, 0, 0);
+  }
+  if (a_raw < -1 || a_raw >= p.ad.L) {
+    if (report && p.ctrl != nullptr) atomic_or_relaxed(p.ctrl + kCtrlError, EPILORA_DEV_BAD_INDEX);
+  }
+  const int a = (a_raw >= 0 && a_raw < p.ad.L && mk != 0) ? a_raw : -1;  // uniform over the block
+  int rank = 0;
+  if (a >= 0) {
+    rank = p.ad.ranks != nullptr ? p.ad.ranks[a] : r;
+    rank = rank < r ? rank : r;
+  }
   float acc[RW];
 #pragma unroll
   for (int q = 0; q < RW; ++q) acc[q] = 0.f;
-  if (live) {
+  if (a >= 0) {
     const int64_t arow = (((int64_t)a * S + slice) * r + j0) * K;  // elements
-    const uint16_t* xr = p.x + t * p.ldx;
     for (int c0 = tid; c0 < nck; c0 += NTS * CG) {
-      uint4 xv[CG], av[RW][CG];
+      if (c0 != tid) {
 #pragma unroll
-      for (int i = 0; i < CG; ++i) {
-        const int kc = c0 + i * NTS;
-        xv[i] = (working && kc < nck) ? ld16(xr + 8 * (int64_t)kc) : make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < CG; ++i) {
+          const int kc = c0 + i * NTS;
+          xv[i] = (working && kc < nck) ? ld16(xr + 8 * (int64_t)kc) : make_uint4(0, 0, 0, 0);
+        }
       }
+      uint4 av[RW][CG];
 #pragma unroll
       for (int q = 0; q < RW; ++q)
 #pragma unroll
         for (int i = 0; i < CG; ++i) {
           const int kc = c0 + i * NTS;
-          const bool ok = working && kc < nck && j0 + q < rank;
+          const bool ok = working && kc < nck;
           if (a8) {
             const uint2 w = ok ? *reinterpret_cast<const uint2*>(p.ad.A8() + arow + q * K + 8 * (int64_t)kc)
                                : make_uint2(0, 0);
@@ -387,20 +410,21 @@ __device__ __forceinline__ void shrink_unit_rows_of(const ShrinkParams& p, int64
       }
     }
   }
+  const bool active = a >= 0 && rank > 0;
 #pragma unroll
   for (int q = 0; q < RW; ++q) {
     const float v = wave_tree_sum(acc[q]);
     if (lane == 0 && wave < kShrinkWaves) red[wave * RW + q] = v;
   }
   __syncthreads();
-  if (tid == 0 && (a >= 0 || p.zflip == 0u)) {
+  if (tid == 0 && (active || p.zflip == 0u)) {
     float zv[RW];
 #pragma unroll
     for (int q = 0; q < RW; ++q) {
       float v = red[q];
 #pragma unroll
       for (int w = 1; w < kShrinkWaves; ++w) v += red[w * RW + q];
-      if (a < 0 || j0 + q >= rank) v = 0.f;
+      if (!active || j0 + q >= rank) v = 0.f;
       else if (a8) v *= p.ad.sa[((int64_t)a * S + slice) * r + j0 + q];
       zv[q] = v;
     }
@@ -418,7 +442,9 @@ __device__ __forceinline__ void shrink_unit_rows_of(const ShrinkParams& p, int64
 
 // Unit `unit` of a decode batch's shrink (units in token, slice, row-block
 // order).  `red`: LDS of kShrinkWaves * 4 floats.  Every thread of the block
-// calls it; it ends with no pending barrier.
+// calls it; it ends with no pending barrier.  A token is active as in
+// resolve_token (slot in [0, L), mask byte nonzero, rank > 0); an index
+// outside [-1, L) is reported once per token.
 template <bool GEN, typename XT = XIdentity>
 __device__ __forceinline__ void shrink_unit(const ShrinkParams& p, int unit, float* red, const XT& xt = XT()) {
   const int r = p.ad.r, S = GEN ? p.ad.S : 1;
@@ -426,11 +452,10 @@ __device__ __forceinline__ void shrink_unit(const ShrinkParams& p, int unit, flo
   const int rb = unit % nrb, rest = unit / nrb;
   const int slice = rest % S;
   const int64_t t = rest / S;
-  int rank;
-  const int a = resolve_token(t, p.M, p.ad, p.ctrl + kCtrlError, threadIdx.x == 0 && slice == 0 && rb == 0, rank);
-  if (RW == 4) shrink_unit_rows_of<4, GEN>(p, t, slice, rb * 4, a, rank, red, xt);
-  else if (RW == 2) shrink_unit_rows_of<2, GEN>(p, t, slice, rb * 2, a, rank, red, xt);
-  else shrink_unit_rows_of<1, GEN>(p, t, slice, rb, a, rank, red, xt);
+  const bool report = threadIdx.x == 0 && slice == 0 && rb == 0;
+  if (RW == 4) shrink_unit_rows_of<4, GEN>(p, t, slice, rb * 4, red, report, xt);
+  else if (RW == 2) shrink_unit_rows_of<2, GEN>(p, t, slice, rb * 2, red, report, xt);
+  else shrink_unit_rows_of<1, GEN>(p, t, slice, rb, red, report, xt);
 }
 
 // K-step range of split `split`.

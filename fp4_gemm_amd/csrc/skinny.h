@@ -101,6 +101,8 @@ struct SkinnyJob {
   int* qflag;           // fused, activations not in LDS: rows quantized
   int qtarget;
   int64_t wait_ticks;
+  int* done;            // fused with flags: the done sub-counters (kDoneGroups, kDoneStride words apart)
+  int flags;            // fused: a flag is counted or z handed over (the workgroups count themselves done)
 };
 
 // XV 16-byte vectors of activations per lane and step: 2 (32 FP8 codes) or
@@ -317,6 +319,7 @@ struct Skinny {
   bool adapters;
   int zslice;    // unfused: the slice whose z is staged in LDS
   float gscale;  // 4-bit weights: gs * 8
+  int done_old;  // fused, thread 0: what the done sub-counter returned (-1: not counted yet)
 
   __device__ __forceinline__ Skinny(const SkinnyJob& j, char* lds, int gidx) : J(j), p(j.g), g(gidx) {
     const int64_t M = p.M, K = p.K;
@@ -346,6 +349,7 @@ struct Skinny {
       if (threadIdx.x == 0 && p.ctrl != nullptr) atomic_or_relaxed(p.ctrl + kCtrlError, EPILORA_DEV_INTERNAL);
     }
     total = mine * nb;
+    done_old = -1;
     adapters = p.z != nullptr;
     gscale = FMT == EPILORA_W_FP4 ? weight_scale<FMT>(p.wt, 0) : 0.f;
     xr = A16 ? make_rsrc(p.x16, (uint32_t)(((M - 1) * p.ldx16 + K) * 2)) : make_rsrc(p.xq, (uint32_t)((M - 1) * p.ldq + K));
@@ -776,6 +780,42 @@ struct Skinny {
     }
   }
 
+  // ---- fused: counting the workgroups done ----------------------------------
+  // Once a workgroup has every z word it needs in LDS (and long after it
+  // passed the quantized-rows flag) it reads neither again, so it counts
+  // itself done right then: the returning atomic is in flight while the
+  // epilogues run and is waited for only in done_finish.  The last of each
+  // of kDoneGroups groups counts the group; the last group puts the flag back
+  // to zero and tells its workgroup to clear z; each counter is reset by the
+  // one that completed it.
+  __device__ __forceinline__ void done_issue() {
+    if (!FUSED || !J.flags || threadIdx.x != 0 || done_old >= 0) return;
+    const int groups = J.gwgs < kDoneGroups ? J.gwgs : kDoneGroups;
+    done_old = atomic_add_relaxed(J.done + (g % groups) * kDoneStride, 1);
+  }
+  // Every thread calls it (with flags); true in the one workgroup that is
+  // to clear z.  Ends with a barrier.
+  __device__ __forceinline__ bool done_finish() {
+    done_issue();
+    if (threadIdx.x == 0) {
+      const int groups = J.gwgs < kDoneGroups ? J.gwgs : kDoneGroups;
+      const int grp = g % groups;
+      const int members = J.gwgs / groups + (grp < J.gwgs % groups ? 1 : 0);
+      int last = 0;
+      if (done_old == members - 1) {
+        store_relaxed(J.done + grp * kDoneStride, 0);
+        if (atomic_add_relaxed(p.ctrl + kCtrlGemmDone, 1) == groups - 1) {
+          store_relaxed(p.ctrl + kCtrlQuantDone, 0);
+          store_relaxed(p.ctrl + kCtrlGemmDone, 0);
+          last = 1;
+        }
+      }
+      *verdict = last;
+    }
+    __syncthreads();
+    return *verdict != 0;
+  }
+
   // Fused: every tile of the workgroup is in the stash.  Request the first B
   // slice of each, poll z into LDS, write the outputs (pw: each tile's weight
   // scale, requested at the start).
@@ -796,6 +836,7 @@ struct Skinny {
         if (sl > sl0) __syncthreads();  // the previous slice's z is no longer read
         ok = poll_z(sl);
         if (!ok) return;
+        if (sl == sl1) done_issue();  // every z word this workgroup needs is in LDS
       }
 #pragma unroll
       for (int s = 0; s < S; ++s)
