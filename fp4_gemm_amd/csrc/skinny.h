@@ -323,7 +323,8 @@ struct Skinny {
 
   __device__ __forceinline__ Skinny(const SkinnyJob& j, char* lds, int gidx) : J(j), p(j.g), g(gidx) {
     const int64_t M = p.M, K = p.K;
-    L = sk_layout(MB, NW, p.ad.r, XLDS ? (uint32_t)(M * K * XB) : 0u, FUSED ? StashCfg<MB>::n : 0, FMT);
+    L = sk_layout(MB, NW, p.ad.r, XLDS ? (uint32_t)(M * K * XB) : 0u,
+                  (FUSED || (MB >= 2 && !XLDS && !A16)) ? StashCfg<MB>::n : 0, FMT);
     part = reinterpret_cast<float*>(lds + L.part);
     red = reinterpret_cast<float*>(lds + L.red);
     tbl = reinterpret_cast<uint2*>(lds + L.tbl);
@@ -679,6 +680,109 @@ struct Skinny {
     }
   }
 
+  // Outputs of all `mine` tiles of a batch-major workgroup (sums in the
+  // stash, [S][T][16]; pw[s]: this thread's row weight scale of tile s, as
+  // row_ws<CPL>), z of one slice in LDS.  The same arithmetic as outputs(),
+  // with the outputs of all the tiles in one list, so that G outputs per lane
+  // have their B chunks in flight together whichever tile they belong to.
+  template <int G, int CPL>
+  __device__ __forceinline__ void outputs_all(int mine, const float (&pw)[StashCfg<MB>::n]) const {
+    constexpr int S = StashCfg<MB>::n;
+    constexpr int NT = NW * kWave;
+    const int total_o = (int)p.M * 16;
+    if (!adapters) {
+#pragma unroll
+      for (int s = 0; s < S; ++s) {
+        const int64_t n = n0_of(s * nb) + (threadIdx.x & 15);
+        if (s >= mine || n >= p.N) continue;
+        const float* base = stash + s * T * 16;
+        for (int o = threadIdx.x; o < total_o; o += NT) {
+          const int t = o >> 4;
+          p.y[(int64_t)t * p.ldy + n] = (uint16_t)f32_to_bf16((base[o] * sxs[t]) * pw[s]);
+        }
+      }
+      return;
+    }
+    const int sh = lane_shift<CPL>();
+    const int jl = threadIdx.x & ((1 << sh) - 1);
+    const int per = NT >> sh;
+    const int first = (int)(threadIdx.x >> sh);
+    const int r = p.ad.r;
+    const int nch = r >> 3;
+    const int ipt = first < total_o ? (total_o - 1 - first) / per + 1 : 0;  // outputs per tile
+    const int items = mine * ipt;
+    for (int f0 = 0; f0 < items; f0 += G) {
+      uint4 raw[G][CPL];
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        const int f = f0 + gi;
+        const int s = f < items ? f / ipt : 0;
+        const int o = first + (f - s * ipt) * per;
+        const int64_t n = n0_of(s * nb) + (first & 15);
+        const TokenSlot ts = f < items ? tok[o >> 4] : TokenSlot{-1, 0};
+#pragma unroll
+        for (int q = 0; q < CPL; ++q) {
+          const int c = jl + (q << sh);
+          raw[gi][q] = c < nch ? b_raw(ts, n, c) : zero4();
+        }
+      }
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        const int f = f0 + gi;
+        if (f >= items) break;
+        const int s = f / ipt;
+        const int o = first + (f - s * ipt) * per;
+        const int t = o >> 4;
+        const int64_t n = n0_of(s * nb) + (first & 15);
+        float ws = pw[0];
+#pragma unroll
+        for (int s2 = 1; s2 < S; ++s2)
+          if (s == s2) ws = pw[s2];
+        const TokenSlot ts = tok[t];
+        float part[CPL];
+#pragma unroll
+        for (int q = 0; q < CPL; ++q) {
+          const int c = jl + (q << sh);
+          float d = 0.f;
+          if (ts.a >= 0 && c < nch && c * 8 < ts.rank) {
+            const uint4 v = af8() ? fp8x8_to_bf16x8(raw[gi][q].x, raw[gi][q].y) : raw[gi][q];
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+            const float4 z0 = *reinterpret_cast<const float4*>(zs + t * r + c * 8);
+            const float4 z1 = *reinterpret_cast<const float4*>(zs + t * r + c * 8 + 4);
+            const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+            const int lim = ts.rank - c * 8;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+              const float b = (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
+              if (e < lim) d = fmaf(b, zv[e], d);
+            }
+          }
+          if (sh >= 1) d += dpp_mov<0xB1>(d);
+          if (sh >= 2) d += dpp_mov<0x4E>(d);
+          if (sh >= 3) d += dpp_mov<0x141>(d);
+          if (sh >= 4) d += dpp_mov<0x140>(d);
+          part[q] = d;
+        }
+        float l;
+        if constexpr (CPL == 1) l = part[0];
+        else if constexpr (CPL == 2) l = part[0] + part[1];
+        else l = (part[0] + part[1]) + (part[2] + part[3]);
+        if (jl == 0 && n < p.N) {
+          float y = (stash[s * T * 16 + o] * sxs[t]) * ws;
+          if (ts.a >= 0 && af8()) l *= p.ad.sb[(int64_t)ts.a * p.N + n];
+          if (ts.a >= 0) y = y + p.ad.scale * l;
+          p.y[(int64_t)t * p.ldy + n] = (uint16_t)f32_to_bf16(y);
+        }
+      }
+    }
+  }
+  // The list above with its depth by rank: up to rank 16 two chunks per
+  // output (one lane each) and eight outputs per lane, else four and four.
+  __device__ __forceinline__ void outputs_batch(int mine, const float (&pw)[StashCfg<MB>::n]) const {
+    if (adapters && p.ad.r <= 16) outputs_all<8, 2>(mine, pw);
+    else outputs_all<4, 4>(mine, pw);
+  }
+
   // Fused: z is published in place.  Every word of the z region reads zero
   // until its producer stores it (as its bitwise complement), so the
   // workgroup polls the words of its active tokens until none is missing,
@@ -822,6 +926,17 @@ struct Skinny {
   __device__ __forceinline__ void finish_stash(bool& ok, const float (&pw)[StashCfg<MB>::n]) {
     constexpr int S = StashCfg<MB>::n;
     const int mine = total / nb;
+    if constexpr (MB >= 2) {  // batch-major: all tiles in one list when they share a slice
+      if (mine == 0 || slice(n0_of(0)) == slice(n0_of((mine - 1) * nb))) {
+        if (adapters) {
+          ok = poll_z(mine > 0 ? slice(n0_of(0)) : 0);
+          if (!ok) return;
+          done_issue();  // every z word this workgroup needs is in LDS
+        }
+        outputs_batch(mine, pw);
+        return;
+      }
+    }
     uint4 pb[S];
 #pragma unroll
     for (int s = 0; s < S; ++s)
@@ -922,6 +1037,13 @@ struct Skinny {
       for (int t = 0; t < S; ++t)
         if (t < mine) reduce_tile(acc[t], stash + t * T * 16);
       if (ok) finish_stash(ok, pw);
+    } else if (mine == 0 || slice(n0_of(0)) == slice(n0_of((mine - 1) * nb))) {
+      // all tiles in one slice: reduce them all, then one list of outputs
+#pragma unroll
+      for (int t = 0; t < S; ++t)
+        if (t < mine) reduce_tile(acc[t], stash + t * T * 16);
+      if (adapters) stage_z(mine > 0 ? slice(n0_of(0)) : 0);
+      outputs_batch(mine, pw);
     } else {
       uint4 pb[S];
 #pragma unroll
@@ -1080,7 +1202,9 @@ inline bool skinny_x_in_lds(int64_t M, int64_t K, int MB, int NW, int r, bool fu
   return sk_layout(MB, NW, r, (uint32_t)(M * K * xb), nstash, fmt).total <= kLdsBudget;
 }
 inline uint32_t skinny_lds(int64_t M, int64_t K, int MB, int NW, int r, bool fused, bool xlds, int fmt, int xb = 1) {
-  const int nstash = fused ? stash_tiles(MB) : 0;
+  // fused grids and batch-major ones (several token blocks, FP8 codes read
+  // from memory) keep the sums of all their tiles
+  const int nstash = (fused || (MB >= 2 && !xlds && xb == 1)) ? stash_tiles(MB) : 0;
   return sk_layout(MB, NW, r, xlds ? (uint32_t)(M * K * xb) : 0u, nstash, fmt).total;
 }
 
