@@ -153,7 +153,7 @@ __global__ __launch_bounds__(kNormThreads) void norm_unit_kernel(NormParams p) {
   int64_t t = unit;
   bool first = true;
   if (shrink) {
-    const int S = s.ad.S, nrb = s.ad.r / shrink_unit_rows(s.K);
+    const int S = s.ad.S, nrb = s.ad.r / shrink_unit_rows(s.M, S, s.ad.r, s.K);
     t = unit / nrb / S;
     first = unit % (nrb * S) == 0;
   }

@@ -304,8 +304,8 @@ __device__ __forceinline__ bool shrink_finish(const ShrinkParams& p, int tile, i
 // The first kShrinkWaves waves take the 8-element chunks tid, tid + 256, ...
 // of K (further waves of a larger block idle, so the sums round the same way
 // in every kernel that carries this code); each thread requests its chunks
-// of x and of the RW rows of A at once (RW * K <= 16384 elements: one round
-// of loads for K up to 16384) and sums its chunks in K order, one fp32 FMA
+// of x and of the RW rows of A at once, 8 / RW chunks of each per round
+// (one round when RW * K <= 16384), and sums its chunks in K order, one fp32 FMA
 // per element (bf16 products are exact in fp32); the 64 lanes of a wave
 // meet in a fixed tree (DPP moves, then two swaps across rows) and the
 // waves in wave order.  FP8 adapters: the codes are widened exactly and the
@@ -313,9 +313,16 @@ __device__ __forceinline__ bool shrink_finish(const ShrinkParams& p, int tile, i
 // written as zeros by the separate shrink and not at all by the fused path
 // (zflip != 0), which stores exactly the words its consumers poll.
 // ---------------------------------------------------------------------------
-__host__ __device__ inline int shrink_unit_rows(int64_t K) { return K <= 4096 ? 4 : (K <= 8192 ? 2 : 1); }
+// Rows per unit: as many as one round of loads covers (RW * K <= 16384),
+// more when that would make over 256 units (each unit reads its token's
+// activations again; with one row per unit that doubles the shrink's reads).
+__host__ __device__ inline int shrink_unit_rows(int64_t M, int S, int r, int64_t K) {
+  int rw = K <= 4096 ? 4 : (K <= 8192 ? 2 : 1);
+  while (rw < 4 && M * S * (r / rw) > 256) rw *= 2;
+  return rw;
+}
 __host__ __device__ inline int64_t shrink_units(int64_t M, int S, int r, int64_t K) {
-  return M * S * (r / shrink_unit_rows(K));
+  return M * S * (r / shrink_unit_rows(M, S, r, K));
 }
 
 // Sum over the 64 lanes of a wave, the same bits in every lane.
@@ -448,7 +455,7 @@ __device__ __forceinline__ void shrink_unit_rows_of(const ShrinkParams& p, int64
 template <bool GEN, typename XT = XIdentity>
 __device__ __forceinline__ void shrink_unit(const ShrinkParams& p, int unit, float* red, const XT& xt = XT()) {
   const int r = p.ad.r, S = GEN ? p.ad.S : 1;
-  const int RW = shrink_unit_rows(p.K), nrb = r / RW;
+  const int RW = shrink_unit_rows(p.M, S, r, p.K), nrb = r / RW;
   const int rb = unit % nrb, rest = unit / nrb;
   const int slice = rest % S;
   const int64_t t = rest / S;
