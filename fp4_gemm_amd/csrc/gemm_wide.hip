@@ -518,14 +518,19 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(BM
   }
 
   // ---- store: each wave's bf16 quarter through LDS as 16-byte row chunks --
-  uint16_t* sy = reinterpret_cast<uint16_t*>(wave < 2 ? buf0 : buf1) + (wave & 1) * (WM * WN);
+  // Rows of the quarter are WN + 8 elements apart: the four rows one store
+  // instruction writes then fall on different banks (at WN = 64 elements,
+  // 128 bytes, two of them shared every bank).
+  constexpr int SW = WN + 8;
+  static_assert(2 * WM * SW * 2 <= kBuf, "store staging");
+  uint16_t* sy = reinterpret_cast<uint16_t*>(wave < 2 ? buf0 : buf1) + (wave & 1) * (WM * SW);
 #pragma unroll
   for (int tb = 0; tb < TM; ++tb)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int row = tb * 16 + 4 * (lane >> 4) + v;
 #pragma unroll
-      for (int nb = 0; nb < TN; ++nb) sy[row * WN + nb * 16 + (lane & 15)] = (uint16_t)f32_to_bf16(acc[tb][nb][v]);
+      for (int nb = 0; nb < TN; ++nb) sy[row * SW + nb * 16 + (lane & 15)] = (uint16_t)f32_to_bf16(acc[tb][nb][v]);
     }
   __syncthreads();
   const bool vec = (((uintptr_t)p.y | (uintptr_t)(p.ldy * 2)) & 15) == 0;
@@ -534,7 +539,7 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(BM
     const int row = e / CPR, c = e % CPR;
     const int64_t t = tw0 + row, n = nw0 + c * 8;
     if (t >= p.M || n >= p.N) continue;
-    const uint4 v = *reinterpret_cast<const uint4*>(sy + row * WN + c * 8);
+    const uint4 v = *reinterpret_cast<const uint4*>(sy + row * SW + c * 8);
     uint16_t* dst = p.y + t * p.ldy + n;
     if (vec && n + 8 <= p.N) {
       *reinterpret_cast<uint4*>(dst) = v;
