@@ -155,6 +155,16 @@ static void launch_decode_nw(DecodeParams& p, bool want_xq, hipStream_t stream) 
   // the one-block variants have that form.
   constexpr int xb = A16 ? 2 : 1;
   constexpr int NW = MB <= 2 ? 8 : 4;
+  // Two token blocks over more than four tiles per compute unit: eight-wave
+  // workgroups of four tiles (one per compute unit) would take two rounds,
+  // four-wave ones (two per compute unit) take one (the 8B-shaped gate_up
+  // projection at 32 tokens: 80 -> 73 us).
+  if constexpr (MB == 2 && !A16) {
+    if (cdiv(g.N, 16) > 4 * device_cus()) {
+      launch_decode_x<MB, FMT, 4, false, A16>(p, want_xq, stream);
+      return;
+    }
+  }
   if constexpr (MB == 1) {
     if (skinny_x_in_lds(g.M, g.K, MB, NW, p.s.ad.r, true, FMT, xb)) {
       launch_decode_x<MB, FMT, NW, true, A16>(p, want_xq, stream);
