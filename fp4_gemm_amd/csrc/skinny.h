@@ -320,6 +320,14 @@ struct Skinny {
   int zslice;    // unfused: the slice whose z is staged in LDS
   float gscale;  // 4-bit weights: gs * 8
   int done_old;  // fused, thread 0: what the done sub-counter returned (-1: not counted yet)
+  // Fused one-block grids with one adapter slice: the outputs of all the
+  // workgroup's tiles form one list (outputs_flat); the B chunks and weight
+  // scales of this thread's first kFlatPre outputs are requested before the
+  // stream and held through it.
+  static constexpr bool kFlat = FUSED && MB == 1 && !GEN;
+  static constexpr int kFlatPre = 2;
+  uint4 fpre_b[kFlatPre];
+  float fpre_ws[kFlatPre];
 
   __device__ __forceinline__ Skinny(const SkinnyJob& j, char* lds, int gidx) : J(j), p(j.g), g(gidx) {
     const int64_t M = p.M, K = p.K;
@@ -783,6 +791,96 @@ struct Skinny {
     else outputs_all<4, 4>(mine, pw);
   }
 
+  // ---- fused one-block grids: the outputs of all tiles in one list -----------
+  // Item g of the list (g < mine * M * 16) is output o = g % (M * 16) of the
+  // workgroup's tile s = g / (M * 16); each takes 2^sh lanes as in outputs()
+  // (CPL = 1), and lane group `first` takes items first, first + per, ...
+  // The tiles' outputs then run side by side instead of one tile after
+  // another, and a thread's first items need nothing but the prefetch.
+  __device__ __forceinline__ float wscale_at(int64_t n) const {
+    if (FMT == EPILORA_W_FP4) return gscale;
+    return n < p.N ? p.wt.sw[n] : 0.f;
+  }
+  // The requests for items first + k * per, k < P, into b / ws.
+  template <int P>
+  __device__ __forceinline__ void flat_request(int k0, int mine, uint4 (&b)[P], float (&ws)[P]) const {
+    const int sh = lane_shift<1>();
+    const int jl = threadIdx.x & ((1 << sh) - 1);
+    const int per = (NW * kWave) >> sh, first = (int)(threadIdx.x >> sh);
+    const int total_o = (int)p.M * 16, items = mine * total_o;
+    const int nch = p.ad.r >> 3;
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+      const int g = first + (k0 + k) * per;
+      int s = 0, o = 0;
+      if (g < items) {
+        s = g / total_o;
+        o = g - s * total_o;
+      }
+      const int64_t n = n0_of(s * nb) + (o & 15);
+      const TokenSlot ts = (adapters && g < items) ? tok[o >> 4] : TokenSlot{-1, 0};
+      b[k] = jl < nch ? b_raw(ts, n, jl) : zero4();
+      ws[k] = g < items ? wscale_at(n) : 0.f;
+    }
+  }
+  __device__ __forceinline__ void flat_prefetch() {
+    flat_request<kFlatPre>(0, total / nb, fpre_b, fpre_ws);
+  }
+  template <int P>
+  __device__ __forceinline__ void flat_group(int k0, int mine, const uint4 (&b)[P], const float (&ws)[P]) const {
+    const int sh = lane_shift<1>();
+    const int jl = threadIdx.x & ((1 << sh) - 1);
+    const int per = (NW * kWave) >> sh, first = (int)(threadIdx.x >> sh);
+    const int total_o = (int)p.M * 16, items = mine * total_o;
+    const int r = p.ad.r, nch = r >> 3;
+#pragma unroll
+    for (int k = 0; k < P; ++k) {
+      const int g = first + (k0 + k) * per;
+      if (g >= items) break;
+      const int s = g / total_o, o = g - s * total_o, t = o >> 4;
+      const int64_t n = n0_of(s * nb) + (o & 15);
+      const TokenSlot ts = tok[t];
+      float d = 0.f;
+      if (ts.a >= 0 && jl < nch && jl * 8 < ts.rank) {
+        const uint4 v = af8() ? fp8x8_to_bf16x8(b[k].x, b[k].y) : b[k];
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        const float4 z0 = *reinterpret_cast<const float4*>(zs + t * r + jl * 8);
+        const float4 z1 = *reinterpret_cast<const float4*>(zs + t * r + jl * 8 + 4);
+        const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
+        const int lim = ts.rank - jl * 8;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float bb = (e & 1) ? bf16_hi(w[e >> 1]) : bf16_lo(w[e >> 1]);
+          if (e < lim) d = fmaf(bb, zv[e], d);
+        }
+      }
+      if (sh >= 1) d += dpp_mov<0xB1>(d);
+      if (sh >= 2) d += dpp_mov<0x4E>(d);
+      if (sh >= 3) d += dpp_mov<0x141>(d);
+      if (sh >= 4) d += dpp_mov<0x140>(d);
+      if (jl == 0 && n < p.N) {
+        float y = (stash[s * T * 16 + o] * sxs[t]) * ws[k];
+        if (ts.a >= 0 && af8()) d *= p.ad.sb[(int64_t)ts.a * p.N + n];
+        if (ts.a >= 0) y = y + p.ad.scale * d;
+        p.y[(int64_t)t * p.ldy + n] = (uint16_t)f32_to_bf16(y);
+      }
+    }
+  }
+  // Every output of the workgroup's `mine` tiles (sums in the stash, z of
+  // the one slice in LDS).  The same arithmetic as outputs<G, 1>.
+  __device__ __forceinline__ void outputs_flat(int mine) const {
+    const int sh = lane_shift<1>();
+    const int per = (NW * kWave) >> sh, first = (int)(threadIdx.x >> sh);
+    const int items = mine * (int)p.M * 16;
+    flat_group<kFlatPre>(0, mine, fpre_b, fpre_ws);
+    for (int k0 = kFlatPre; first + k0 * per < items; k0 += kFlatPre) {
+      uint4 b[kFlatPre];
+      float ws[kFlatPre];
+      flat_request<kFlatPre>(k0, mine, b, ws);
+      flat_group<kFlatPre>(k0, mine, b, ws);
+    }
+  }
+
   // Fused: z is published in place.  Every word of the z region reads zero
   // until its producer stores it (as its bitwise complement), so the
   // workgroup polls the words of its active tokens until none is missing,
@@ -926,6 +1024,15 @@ struct Skinny {
   __device__ __forceinline__ void finish_stash(bool& ok, const float (&pw)[StashCfg<MB>::n]) {
     constexpr int S = StashCfg<MB>::n;
     const int mine = total / nb;
+    if constexpr (kFlat) {  // one slice (no general adapters)
+      if (adapters) {
+        ok = poll_z(0);
+        if (!ok) return;
+        done_issue();  // every z word this workgroup needs is in LDS
+      }
+      outputs_flat(mine);
+      return;
+    }
     if constexpr (MB >= 2) {  // batch-major: all tiles in one list when they share a slice
       if (mine == 0 || slice(n0_of(0)) == slice(n0_of((mine - 1) * nb))) {
         if (adapters) {
@@ -1125,7 +1232,9 @@ struct Skinny {
     if (!FUSED) pre = EpiPre{pre_b<kCplLoop>(n0_of(0)), row_ws<kCplLoop>(n0_of(0))};
     float pw[StashCfg<MB>::n];  // fused: the weight scale of each tile, needed after the stream
 #pragma unroll
-    for (int s = 0; s < StashCfg<MB>::n; ++s) pw[s] = (FUSED && s < total / nb) ? row_ws<kCplEnd>(n0_of(s * nb)) : 0.f;
+    for (int s = 0; s < StashCfg<MB>::n; ++s)
+      pw[s] = (FUSED && !kFlat && s < total / nb) ? row_ws<kCplEnd>(n0_of(s * nb)) : 0.f;
+    if constexpr (kFlat) flat_prefetch();
 
     if (kRowsInGrid) {  // the quantized rows come from other workgroups
       ok = wait_flag(J.qflag, J.qtarget, J.wait_ticks, err, p.ctrl + kCtrlForceTimeout, verdict);
