@@ -323,8 +323,9 @@ struct Skinny {
   // Fused one-block grids with one adapter slice: the outputs of all the
   // workgroup's tiles form one list (outputs_flat); the B chunks and weight
   // scales of this thread's first kFlatPre outputs are requested before the
-  // stream and held through it.
-  static constexpr bool kFlat = FUSED && MB == 1 && !GEN;
+  // stream and held through it.  (Several slices: per-slice z, tile by tile.)
+  static constexpr bool kFlat = FUSED && MB == 1;  // (with the general adapters: one slice only)
+  __device__ __forceinline__ bool flat() const { return kFlat && (!GEN || p.ad.S <= 1); }
   static constexpr int kFlatPre = 2;
   uint4 fpre_b[kFlatPre];
   float fpre_ws[kFlatPre];
@@ -1024,7 +1025,7 @@ struct Skinny {
   __device__ __forceinline__ void finish_stash(bool& ok, const float (&pw)[StashCfg<MB>::n]) {
     constexpr int S = StashCfg<MB>::n;
     const int mine = total / nb;
-    if constexpr (kFlat) {  // one slice (no general adapters)
+    if (flat()) {
       if (adapters) {
         ok = poll_z(0);
         if (!ok) return;
@@ -1233,8 +1234,8 @@ struct Skinny {
     float pw[StashCfg<MB>::n];  // fused: the weight scale of each tile, needed after the stream
 #pragma unroll
     for (int s = 0; s < StashCfg<MB>::n; ++s)
-      pw[s] = (FUSED && !kFlat && s < total / nb) ? row_ws<kCplEnd>(n0_of(s * nb)) : 0.f;
-    if constexpr (kFlat) flat_prefetch();
+      pw[s] = (FUSED && !flat() && s < total / nb) ? row_ws<kCplEnd>(n0_of(s * nb)) : 0.f;
+    if (flat()) flat_prefetch();
 
     if (kRowsInGrid) {  // the quantized rows come from other workgroups
       ok = wait_flag(J.qflag, J.qtarget, J.wait_ticks, err, p.ctrl + kCtrlForceTimeout, verdict);
