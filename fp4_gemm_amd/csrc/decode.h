@@ -113,7 +113,18 @@ static void launch_decode_u(DecodeParams& p, bool want_xq, hipStream_t stream) {
   p.job.qtarget = (int)g.M;
   p.count_q = (XLDS || A16 || before) ? 0 : 1;
   p.job.flags = p.count_q || p.ns > 0;
-  const size_t lds = skinny_lds(g.M, g.K, MB, NW, r, true, XLDS, FMT, A16 ? 2 : 1);  // > the shrink's kShrinkWaves * 4 floats
+  // One-block grids over several output slices keep the z of every slice in
+  // LDS at once (the outputs of all tiles then run as one list) when that
+  // fits the budget.  The LDS exceeds the shrink's kShrinkWaves * 4 floats.
+  p.job.zplanes = 1;
+  size_t lds = skinny_lds(g.M, g.K, MB, NW, r, true, XLDS, FMT, A16 ? 2 : 1);
+  if (MB == 1 && GEN && p.s.ad.S > 1) {
+    const size_t wide = skinny_lds(g.M, g.K, MB, NW, r, true, XLDS, FMT, A16 ? 2 : 1, p.s.ad.S);
+    if (wide <= kLdsBudget) {
+      p.job.zplanes = p.s.ad.S;
+      lds = wide;
+    }
+  }
   // The quantizing and shrink workgroups are dispatched first and hold their
   // slots only until they finish.
   const int resident = resident_groups(decode_kernel<MB, FMT, NW, XLDS, UB, GEN, A16>, NW * 64, lds);

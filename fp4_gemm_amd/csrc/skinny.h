@@ -75,7 +75,9 @@ struct SkLayout {
 
 constexpr uint32_t kWaveStage = 2048;  // LDS per wave for one FP8 weight step (16 rows x 128 bytes)
 
-__host__ __device__ inline SkLayout sk_layout(int MB, int NW, int r, uint32_t xbytes, int nstash, int fmt) {
+// zplanes: z of that many output slices side by side ([zplanes][T][r]).
+__host__ __device__ inline SkLayout sk_layout(int MB, int NW, int r, uint32_t xbytes, int nstash, int fmt,
+                                              int zplanes = 1) {
   const uint32_t T = MB * 16;
   SkLayout L;
   L.part = 0;                                            // float [NW][T][16]
@@ -84,7 +86,7 @@ __host__ __device__ inline SkLayout sk_layout(int MB, int NW, int r, uint32_t xb
   L.tok = align16(L.tbl + 256 * 8);                      // TokenSlot [T]
   L.sx = align16(L.tok + T * 8);                         // float [T]
   L.zs = align16(L.sx + T * 4);                          // float [T][r]
-  L.xs = align16(L.zs + T * r * 4);                      // uint8 [M][K]
+  L.xs = align16(L.zs + T * r * 4 * (zplanes > 1 ? zplanes : 1));  // uint8 [M][K]
   L.stash = align16(L.xs + xbytes);                      // float [nstash][T][16]
   L.wst = align16(L.stash + nstash * T * 16 * 4);        // uint8 [NW][kWaveStage] (FP8 weights)
   L.total = align16(L.wst + (fmt == EPILORA_W_FP8 ? NW * kWaveStage : 0u) + 16);  // + one flag word
@@ -101,6 +103,7 @@ struct SkinnyJob {
   int* qflag;           // fused, activations not in LDS: rows quantized
   int qtarget;
   int64_t wait_ticks;
+  int zplanes;          // fused: output slices whose z fit in LDS at once (sk_layout)
   int* done;            // fused with flags: the done sub-counters (kDoneGroups, kDoneStride words apart)
   int flags;            // fused: a flag is counted or z handed over (the workgroups count themselves done)
 };
@@ -323,9 +326,10 @@ struct Skinny {
   // Fused one-block grids with one adapter slice: the outputs of all the
   // workgroup's tiles form one list (outputs_flat); the B chunks and weight
   // scales of this thread's first kFlatPre outputs are requested before the
-  // stream and held through it.  (Several slices: per-slice z, tile by tile.)
+  // stream and held through it.  With several output slices the z of every
+  // slice the tiles span sits in LDS at once (J.zplanes planes), when it fits.
   static constexpr bool kFlat = FUSED && MB == 1;  // (with the general adapters: one slice only)
-  __device__ __forceinline__ bool flat() const { return kFlat && (!GEN || p.ad.S <= 1); }
+  __device__ __forceinline__ bool flat() const { return kFlat && (!GEN || p.ad.S <= 1 || J.zplanes >= p.ad.S); }
   static constexpr int kFlatPre = 2;
   uint4 fpre_b[kFlatPre];
   float fpre_ws[kFlatPre];
@@ -333,7 +337,7 @@ struct Skinny {
   __device__ __forceinline__ Skinny(const SkinnyJob& j, char* lds, int gidx) : J(j), p(j.g), g(gidx) {
     const int64_t M = p.M, K = p.K;
     L = sk_layout(MB, NW, p.ad.r, XLDS ? (uint32_t)(M * K * XB) : 0u,
-                  (FUSED || (MB >= 2 && !XLDS && !A16)) ? StashCfg<MB>::n : 0, FMT);
+                  (FUSED || (MB >= 2 && !XLDS && !A16)) ? StashCfg<MB>::n : 0, FMT, FUSED ? J.zplanes : 1);
     part = reinterpret_cast<float*>(lds + L.part);
     red = reinterpret_cast<float*>(lds + L.red);
     tbl = reinterpret_cast<uint2*>(lds + L.tbl);
@@ -828,7 +832,8 @@ struct Skinny {
     flat_request<kFlatPre>(0, total / nb, fpre_b, fpre_ws);
   }
   template <int P>
-  __device__ __forceinline__ void flat_group(int k0, int mine, const uint4 (&b)[P], const float (&ws)[P]) const {
+  __device__ __forceinline__ void flat_group(int k0, int mine, int sl0, const uint4 (&b)[P],
+                                             const float (&ws)[P]) const {
     const int sh = lane_shift<1>();
     const int jl = threadIdx.x & ((1 << sh) - 1);
     const int per = (NW * kWave) >> sh, first = (int)(threadIdx.x >> sh);
@@ -845,8 +850,9 @@ struct Skinny {
       if (ts.a >= 0 && jl < nch && jl * 8 < ts.rank) {
         const uint4 v = af8() ? fp8x8_to_bf16x8(b[k].x, b[k].y) : b[k];
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        const float4 z0 = *reinterpret_cast<const float4*>(zs + t * r + jl * 8);
-        const float4 z1 = *reinterpret_cast<const float4*>(zs + t * r + jl * 8 + 4);
+        const float* zt = zs + (slice(n) - sl0) * (int)p.M * r + t * r + jl * 8;  // z of the tile's slice
+        const float4 z0 = *reinterpret_cast<const float4*>(zt);
+        const float4 z1 = *reinterpret_cast<const float4*>(zt + 4);
         const float zv[8] = {z0.x, z0.y, z0.z, z0.w, z1.x, z1.y, z1.z, z1.w};
         const int lim = ts.rank - jl * 8;
 #pragma unroll
@@ -869,16 +875,16 @@ struct Skinny {
   }
   // Every output of the workgroup's `mine` tiles (sums in the stash, z of
   // the one slice in LDS).  The same arithmetic as outputs<G, 1>.
-  __device__ __forceinline__ void outputs_flat(int mine) const {
+  __device__ __forceinline__ void outputs_flat(int mine, int sl0) const {
     const int sh = lane_shift<1>();
     const int per = (NW * kWave) >> sh, first = (int)(threadIdx.x >> sh);
     const int items = mine * (int)p.M * 16;
-    flat_group<kFlatPre>(0, mine, fpre_b, fpre_ws);
+    flat_group<kFlatPre>(0, mine, sl0, fpre_b, fpre_ws);
     for (int k0 = kFlatPre; first + k0 * per < items; k0 += kFlatPre) {
       uint4 b[kFlatPre];
       float ws[kFlatPre];
       flat_request<kFlatPre>(k0, mine, b, ws);
-      flat_group<kFlatPre>(k0, mine, b, ws);
+      flat_group<kFlatPre>(k0, mine, sl0, b, ws);
     }
   }
 
@@ -889,7 +895,8 @@ struct Skinny {
   // wall-clock limit.  Returns false on a timeout (or when the host has set
   // the workspace's force-timeout word, read with the first poll).  Ends with
   // a barrier.
-  __device__ __forceinline__ bool poll_z(int slice) const {
+  __device__ __forceinline__ bool poll_z(int slice, float* dst = nullptr) const {
+    float* zd = dst != nullptr ? dst : zs;
     const int r = p.ad.r;
     const int n = (int)p.M * r;
     const auto zr = make_rsrc(p.z + slice * r, (uint32_t)(((p.M - 1) * zld() + r) * 4));
@@ -900,11 +907,11 @@ struct Skinny {
       int missing = 0;
       for (int e = threadIdx.x; e < n; e += NW * kWave) {
         if (tok[e / r].a < 0) {
-          zs[e] = 0.f;
+          zd[e] = 0.f;
         } else {
           const uint32_t w = buf_load4<kCoherent>(zr, 4u * ((e / r) * zld() + e % r));
           if (w == 0u) missing = 1;
-          else zs[e] = __uint_as_float(~w);
+          else zd[e] = __uint_as_float(~w);
         }
       }
       if (threadIdx.x == 0) *verdict = 0;
@@ -1026,12 +1033,18 @@ struct Skinny {
     constexpr int S = StashCfg<MB>::n;
     const int mine = total / nb;
     if (flat()) {
+      // the tiles come in output order: the slices they span, sl0 .. sl1,
+      // each polled into its own plane
+      const int sl0 = mine > 0 ? slice(n0_of(0)) : 0;
+      const int sl1 = mine > 0 ? slice(n0_of((mine - 1) * nb)) : 0;
       if (adapters) {
-        ok = poll_z(0);
-        if (!ok) return;
+        for (int sl = sl0; sl <= sl1; ++sl) {
+          ok = poll_z(sl, zs + (sl - sl0) * (int)p.M * p.ad.r);
+          if (!ok) return;
+        }
         done_issue();  // every z word this workgroup needs is in LDS
       }
-      outputs_flat(mine);
+      outputs_flat(mine, sl0);
       return;
     }
     if constexpr (MB >= 2) {  // batch-major: all tiles in one list when they share a slice
@@ -1311,11 +1324,12 @@ inline bool skinny_x_in_lds(int64_t M, int64_t K, int MB, int NW, int r, bool fu
   const int nstash = fused ? stash_tiles(MB) : 0;
   return sk_layout(MB, NW, r, (uint32_t)(M * K * xb), nstash, fmt).total <= kLdsBudget;
 }
-inline uint32_t skinny_lds(int64_t M, int64_t K, int MB, int NW, int r, bool fused, bool xlds, int fmt, int xb = 1) {
+inline uint32_t skinny_lds(int64_t M, int64_t K, int MB, int NW, int r, bool fused, bool xlds, int fmt, int xb = 1,
+                           int zplanes = 1) {
   // fused grids and batch-major ones (several token blocks, FP8 codes read
   // from memory) keep the sums of all their tiles
   const int nstash = (fused || (MB >= 2 && !xlds && xb == 1)) ? stash_tiles(MB) : 0;
-  return sk_layout(MB, NW, r, xlds ? (uint32_t)(M * K * xb) : 0u, nstash, fmt).total;
+  return sk_layout(MB, NW, r, xlds ? (uint32_t)(M * K * xb) : 0u, nstash, fmt, zplanes).total;
 }
 
 }  // namespace epilora
