@@ -642,6 +642,51 @@ def traffic_probe(args):
                       "algorithmic_bytes_per_launch": p.bytes()}), flush=True)
 
 
+def counter_probe(args):
+    """Dispatches for the counter runs behind the profiles (run under
+    rocprofv3 --pmc): "gate_up", a 256 MiB device copy (its read requests
+    calibrate the L2 counters) then four eager fused gate_up launches at each
+    of the 8B layer at M = 1, the 8B multi-tenant layer at M = 32 and the 72B
+    PreFT layer at M = 64; "prefill", the 2048-token FP8 GEMMs with 32
+    tenant segments (gate_up and down), three eager launches each of the
+    base-only GEMM, the GEMM with its adapter epilogue and the shrink."""
+    torch.cuda.set_device(0)
+    ep.lib()
+    if args.counter_probe == "gate_up":
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=DEV).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+        torch.cuda.empty_cache()
+        for cfg, M in ((2, None), (3, None), (4, 64)):
+            layer = config(cfg, M=M) if M else config(cfg)
+            p = Proj(layer.gemm("gate_up"), copies=1)
+            torch.cuda.synchronize()
+            for _ in range(4):
+                p.fused(0)
+            torch.cuda.synchronize()
+            print(json.dumps({"probe": "gate_up", "config": cfg, "M": layer.M, "launches": 4,
+                              "algorithmic_bytes_per_launch": p.bytes()}), flush=True)
+            del p
+            torch.cuda.empty_cache()
+    else:
+        layer = config(5, segments=32, wfmt="fp8")
+        for g in layer.gemms:
+            p = Proj(g, "fp8", copies=1)
+            p.quant(0)
+            p.shrink(0)
+            torch.cuda.synchronize()
+            for fn in ("gemm_base", "gemm_lora", "shrink"):
+                for _ in range(3):
+                    getattr(p, fn)(0)
+                torch.cuda.synchronize()
+            print(json.dumps({"probe": "prefill", "gemm": g.name, "launches": 3, "flops": p.flops()}), flush=True)
+            del p
+            torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -653,6 +698,8 @@ def main():
     ap.add_argument("--no-mt", action="store_true", help="skip the 32-token multi-tenant decode layer")
     ap.add_argument("--traffic-probe", action="store_true",
                     help="only the dispatches the HBM-counter runs measure (see traffic_probe)")
+    ap.add_argument("--counter-probe", choices=("gate_up", "prefill"),
+                    help="only the dispatches of a counter run (see counter_probe)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this layer shards by tensor parallelism, which is "
@@ -660,6 +707,9 @@ def main():
         sys.exit(2)
     if args.traffic_probe:
         traffic_probe(args)
+        return
+    if args.counter_probe:
+        counter_probe(args)
         return
     torch.cuda.set_device(0)
     ep.lib()

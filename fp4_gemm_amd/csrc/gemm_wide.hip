@@ -78,11 +78,20 @@ __global__ __launch_bounds__(kWideThreads) __attribute__((amdgpu_waves_per_eu(BM
   const int wm = wave & 1, wn = wave >> 1;
 
   // ---- tile of this workgroup: a contiguous run of tiles per XCD ----------
+  // The run is taken in groups of kGroupN output columns: inside a group the
+  // column index moves fastest, so the tiles an XCD holds at once share both
+  // their activation and their weight blocks in its L2.  (Token blocks
+  // moving fastest put every activation block of the problem in flight on
+  // each XCD at once, more than its L2 holds; the 2048-token gate_up GEMM
+  // with adapters ran 7% slower that way.)
+  constexpr int kGroupN = 16;
   const int nt = tiles_m * tiles_n;
   const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
   const int per = nt >> 3, rem = nt & 7;
   const int tile = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + local;
-  const int64_t m0 = (int64_t)(tile % tiles_m) * BM, n0 = (int64_t)(tile / tiles_m) * BN;
+  const int grp = tile / (kGroupN * tiles_m), in_grp = tile % (kGroupN * tiles_m);
+  const int cols = tiles_n - grp * kGroupN < kGroupN ? tiles_n - grp * kGroupN : kGroupN;  // of this group
+  const int64_t m0 = (int64_t)(in_grp / cols) * BM, n0 = (int64_t)(grp * kGroupN + in_grp % cols) * BN;
   const int64_t K = p.K;
   if (FMT == EPILORA_W_FP4) build_fold_table(tbl);
 
