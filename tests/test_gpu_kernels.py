@@ -186,9 +186,11 @@ GEMM_CASES = [
     (1100, 256, 13100, 6, 64, "sorted", True, True, "fp8"),
     (700, 384, 12000, 5, 32, "mixed", False, False, "fp4"),
     (1030, 160, 13100, 4, 16, "mixed", True, False, "fp4"),
-    # enough 256 x 256 tiles that the base-only call takes that kernel
+    # enough 256 x 256 tiles for that kernel, base-only and with its adapter
+    # epilogue (bf16 adapters, one slice): ragged edges, masks, own ranks
     (2048, 256, 16384, 8, 64, "sorted", False, False, "fp8"),
     (2100, 160, 16000, 4, 32, "mixed", True, False, "fp4"),
+    (2050, 192, 16400, 7, 128, "mixed", True, True, "fp8"),
 ]
 
 
