@@ -21,7 +21,8 @@ __global__ __launch_bounds__(kShrinkThreads) void shrink_unit_kernel(ShrinkParam
 // multiplied), and each wave with member tokens multiplies them by its
 // tokens' x (other tokens zero) on bf16 MFMA.  Each (token, rank) sum is
 // owned by one wave, so the partials need no cross-wave reduction; the
-// splits are combined as in the 16-token kernel.
+// splits are combined by the last one of the tile in a fixed order
+// (shrink_finish), as the normalization kernel's 16-token shrink does.
 // ---------------------------------------------------------------------------
 constexpr int kWideRows = 128;  // rank rows staged (r <= 128)
 

@@ -1,4 +1,7 @@
-// The shrink's workgroup-level pieces, shared by the shrink kernel and the
+// The shrink's workgroup-level pieces: the 16-token tile with split-K
+// partials and their fixed-order combine (the normalization kernel's shrink
+// over more than 64 tokens; the combine also serves the prefill shrink), and
+// the unit shrink of decode batches, shared by the shrink kernel and the
 // fused decode path.
 #pragma once
 
@@ -10,7 +13,7 @@ namespace epilora {
 constexpr int kMaxJB = 8;  // r <= 128 -> at most 8 blocks of 16 rank rows
 // The shrink's work is laid out over this many waves whatever the block size
 // (further waves of a larger block idle), so its sums round the same way in
-// the shrink kernel and in the fused decode kernel.
+// every kernel that carries it.
 constexpr int kShrinkWaves = 4;
 
 // ---------------------------------------------------------------------------
@@ -147,8 +150,7 @@ __device__ __forceinline__ uint64_t shrink_tile(const ShrinkParams& p, int64_t t
 }
 
 // The fixed-order sum of the split partials ([splits][M][r] fp32) of the
-// tile of `rows` tokens at t0, shared by the shrink's last split and by the
-// fused decode path's GEMM workgroups, so that both round identically.  The
+// tile of `rows` tokens at t0, taken by the tile's last split.  The
 // quads (4 floats) of the tile times chunks of consecutive splits are spread
 // over the threads; each chunk is summed in split order, then the chunk sums
 // in chunk order (the chunking depends on the tile shape only, not on the

@@ -25,14 +25,19 @@
 //
 // A tile's epilogue sums the NW partial accumulators in wave order through
 // LDS, applies the scales, and adds the adapter term of each active token:
-// an fp32 dot over the rank, 16 lanes per output (lane j takes a contiguous
-// r / 16 slice of the rank) reduced by shuffles; the first pass of B slices
-// for a tile is requested during the previous tile.  In the fused decode
-// kernel z is produced by other workgroups of the same grid, so the
-// streaming loop only reduces each finished tile into an LDS stash (room for
-// kStashTiles tiles; the host never gives a workgroup more); once the last
-// tile is in, the workgroup requests the B slices of all its tiles, waits
-// once for z and runs the epilogues.  Keeping the wait, the hand-off and the
+// an fp32 dot over the rank, each output taken by 2^sh lanes that hold CPL
+// 8-rank chunks each, summed over the chunks in one fixed tree (by chunk
+// index: DPP moves across the lanes' bits first, then the lane's own chunks),
+// so that every layout of lanes rounds the same way.  With two or more token
+// blocks and the activations not in LDS the loop runs batch-major instead
+// (run_batches): each wave loads its activations of a K batch once and runs
+// them against every tile of the workgroup.  In the fused decode kernel z is
+// produced by other workgroups of the same grid, so the streaming loop only
+// reduces each finished tile into an LDS stash (StashCfg<MB>::n tiles; the
+// host never gives a workgroup more); once the last tile is in, the
+// workgroup polls z into LDS, counts itself done and runs the epilogues of
+// all its tiles as one list (their first B chunks requested before the
+// stream at one token block).  Keeping the wait, the hand-off and the
 // epilogues out of the loop keeps the loop's code small: a loop that also
 // carried them streamed measurably slower even when they never ran.
 #pragma once
