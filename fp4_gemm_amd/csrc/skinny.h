@@ -302,11 +302,17 @@ struct Skinny {
   static constexpr int U0 = UB > 0 ? UB : ((FUSED && NW == 8 && MB == 1) ? 2 : SkinnyCfg<MB>::U);
   static constexpr int U = (A16 && U0 > 1) ? U0 / 2 : U0;
   static constexpr int T = MB * 16;
-  // Activations from other workgroups of a fused grid are read coherently;
-  // the W8A16 GEMM reads the caller's bf16 rows, which no workgroup writes.
-  // rows quantized inside this grid, announced by the quantized-rows flag
+  // Rows quantized inside this grid, announced by the quantized-rows flag.
+  // They are read through the caches all the same: a launch starts with no
+  // stale L2 lines for memory written before it, no workgroup touches the
+  // rows before the flag, and their producers write them through to the
+  // point of coherence before they count the flag up, so a workgroup's first
+  // read of a line misses to the rows of this call, and every later read of
+  // it on that XCD hits.  (Reading them device-coherently sent every weight
+  // batch's activations past the L2: the 72B-shaped layer at 8 tokens took
+  // 229 us instead of 214.)  Only the tiny scale vector is read coherently.
   static constexpr bool kRowsInGrid = FUSED && !XLDS && !A16 && MB < kQuantBeforeMB;
-  static constexpr int XPOL = kRowsInGrid ? kCoherent : kCached;
+  static constexpr int XPOL = kCached;
   static constexpr int XB = A16 ? 2 : 1;   // bytes per activation element
   static constexpr int XV = A16 ? 4 : 2;   // 16-byte activation vectors per lane and step
   static_assert(!A16 || FMT == EPILORA_W_FP8, "W8A16 takes FP8 weights");

@@ -313,11 +313,13 @@ def test_decode_workspace_shared_by_different_calls():
 
 
 def test_decode_fresh_rows_each_call():
-    # 17 to 64 tokens: the quantizing workgroups hand the rows to the GEMM
-    # workgroups through the workspace (the same addresses every call), which
-    # read them through the caches after an agent-scope acquire.  Different
-    # activations in turn on one workspace: every call must read its own rows.
-    for M in (48, 64):
+    # More than 4 tokens: the quantized rows reach the GEMM workgroups through
+    # the workspace (the same addresses every call), written by quantizing
+    # workgroups of the same grid behind a flag (8, 24 tokens) or by the
+    # quantizer launched just before (48, 64), and read through the caches.
+    # Different activations in turn on one workspace: every call must read
+    # its own rows.
+    for M in (8, 24, 48, 64):
         say(f"decode M={M}: one workspace, different activations in turn")
         ds = [DeviceGemm(custom_layer(f"f{i}", 1300 + 7 * i + M, M, 4096, 1024, 8, 32,
                                       list(range(-1, 7)) * (M // 8)).gemms[0]) for i in range(2)]
