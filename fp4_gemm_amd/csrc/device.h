@@ -136,25 +136,12 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
-// Sum over each aligned group of 16 lanes, every lane of the group getting
-// the same bits: swap neighbours, swap pairs (quad permutes), then add the
-// mirror image within each half row and within the row (DPP moves, no LDS).
+// A lane's value moved by one DPP control (0xB1 swaps neighbours, 0x4E
+// swaps pairs, 0x141 mirrors each half row, 0x140 each row of 16 lanes), no
+// LDS; the epilogues' fixed reduction trees are built from these.
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float v) {
   return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float sum16(float v) {
-  v += dpp_mov<0xB1>(v);   // quad_perm [1, 0, 3, 2]
-  v += dpp_mov<0x4E>(v);   // quad_perm [2, 3, 0, 1]
-  v += dpp_mov<0x141>(v);  // row_half_mirror
-  v += dpp_mov<0x140>(v);  // row_mirror
-  return v;
-}
-
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
 }
 
 // ---------------------------------------------------------------------------
@@ -264,15 +251,6 @@ __device__ __forceinline__ void lds_barrier() {
 // Agent-scope counters and flags (visible across the chip's XCDs)
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ int atomic_add_acq_rel(int* p, int v) {
-  return __hip_atomic_fetch_add(p, v, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void atomic_add_release(int* p, int v) {
-  __hip_atomic_fetch_add(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ int load_acquire(int* p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-}
 __device__ __forceinline__ void store_relaxed(int* p, int v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }

@@ -45,11 +45,6 @@ constexpr int kBuf = (kBM + kBN) * kStep;  // one step's operands, 64 KB
 __device__ __forceinline__ f32x16 mfma_fp8_32(const i32x8& a, const i32x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
-// C[32][32] += A[32][16] * B[16][32], bf16 operands (8 per lane: row or
-// column l % 32, K elements [8 (l / 32), +8)); C as above.
-__device__ __forceinline__ f32x16 mfma_bf16_32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
 
 // 128-byte operand rows; 16-byte chunk c of row r sits at slot c ^ ((r / 2) % 8).
 __device__ __forceinline__ int swz(int row, int chunk) { return row * 128 + ((chunk ^ ((row >> 1) & 7)) << 4); }

@@ -45,24 +45,6 @@ struct RawW {
   uint32_t s;   // 4-bit: the two block scales
 };
 
-template <int FMT>
-__device__ __forceinline__ RawW load_w_raw(const WeightArgs& wt, int64_t n, int64_t K, int64_t k, bool ok) {
-  RawW r;
-  r.a = zero4();
-  r.b = zero4();
-  r.s = 0;
-  if (!ok) return r;
-  if (FMT == EPILORA_W_FP8) {
-    const uint4* p = reinterpret_cast<const uint4*>(wt.w + n * K + k);
-    r.a = p[0];
-    r.b = p[1];
-  } else {
-    r.a = *reinterpret_cast<const uint4*>(wt.w + n * (K / 2) + k / 2);
-    r.s = *reinterpret_cast<const uint16_t*>(wt.bs + n * (K / 16) + k / 16);
-  }
-  return r;
-}
-
 // 32 FP8 bytes in element order (the 4-bit codes go through the fold table).
 template <int FMT>
 __device__ __forceinline__ i32x8 w_frag(const RawW& r, const uint2* tbl) {
